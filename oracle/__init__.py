@@ -1,0 +1,154 @@
+"""ORACLE -- test infrastructure only.
+
+Python access to the plain fp64 CPU statement of one rank's share of an
+Ulysses attention layer (``oracle.c``).  Only the tests, the smoke check and
+the benchmark's CPU-baseline leg may import this package; the product path
+(``ulysses_sp_attention_amd``) never does, and the two share no code.
+
+Every function takes and returns numpy arrays:
+
+* permutations work on raw storage (any dtype) and are bit copies;
+* attention takes float64 arrays [N, bs, heads, hd] holding the exact input
+  values and returns float64 results.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build_lib() -> str:
+    """Compile ``liboracle.so`` with gcc (always recompiles)."""
+    tmp = _LIB_PATH + ".tmp"
+    cmd = ["gcc", "-O2", "-fPIC", "-shared", "-fopenmp", "-std=c11", "-Wall", _SRC, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        build_lib()
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i64, ci, dbl = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_double
+    lib.oracle_num_threads.argtypes = []
+    lib.oracle_num_threads.restype = ci
+    lib.oracle_seq_to_head.argtypes = [vp, ci, ci, i64, ci, ci, ci, ci, vp]
+    lib.oracle_seq_to_head.restype = ci
+    lib.oracle_head_to_seq.argtypes = [vp, ci, ci, i64, ci, ci, ci, ci, vp]
+    lib.oracle_head_to_seq.restype = ci
+    lib.oracle_attn_fwd.argtypes = [vp, vp, vp, i64, ci, ci, ci, ci, dbl, ci, vp, ci, vp, i64, vp, vp]
+    lib.oracle_attn_fwd.restype = ci
+    lib.oracle_attn_bwd.argtypes = [vp, vp, vp, vp, i64, ci, ci, ci, ci, dbl, ci, vp, ci,
+                                    vp, i64, vp, i64, vp, vp, vp]
+    lib.oracle_attn_bwd.restype = ci
+    _lib = lib
+    return lib
+
+
+def num_threads() -> int:
+    return int(_load().oracle_num_threads())
+
+
+def _ptr_array(arrays):
+    arr = (ctypes.c_void_p * len(arrays))()
+    for i, a in enumerate(arrays):
+        arr[i] = a.ctypes.data
+    return arr
+
+
+def _local_heads(heads: int, P: int) -> int:
+    return heads // P if heads >= P else 1
+
+
+def seq_to_head(chunks, rank: int) -> np.ndarray:
+    """P seq-sharded chunks [n, bs, heads, hd] -> rank's [P*n, bs, heads_l, hd]."""
+    P = len(chunks)
+    n, bs, heads, hd = chunks[0].shape
+    for c in chunks:
+        if c.shape != chunks[0].shape or c.dtype != chunks[0].dtype or not c.flags.c_contiguous:
+            raise ValueError("chunks must be contiguous and alike")
+    out = np.empty((P * n, bs, _local_heads(heads, P), hd), dtype=chunks[0].dtype)
+    rc = _load().oracle_seq_to_head(_ptr_array(chunks), P, rank, n, bs, heads, hd,
+                                    chunks[0].itemsize, out.ctypes.data)
+    if rc:
+        raise ValueError("oracle_seq_to_head: bad arguments")
+    return out
+
+
+def head_to_seq(x: np.ndarray, chunks, rank: int) -> None:
+    """Rank's [P*n, bs, heads_l, hd] -> its head slots of the P chunks (in place)."""
+    P = len(chunks)
+    n, bs, heads, hd = chunks[0].shape
+    if x.shape != (P * n, bs, heads // P, hd) or not x.flags.c_contiguous:
+        raise ValueError("bad head-sharded input shape")
+    rc = _load().oracle_head_to_seq(x.ctypes.data, P, rank, n, bs, heads, hd, x.itemsize,
+                                    _ptr_array(chunks))
+    if rc:
+        raise ValueError("oracle_head_to_seq: bad arguments")
+
+
+def _f64(a):
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _cu64(cu):
+    return None if cu is None else np.ascontiguousarray(cu, dtype=np.int64)
+
+
+def attn_fwd(q, k, v, scale: float, causal: bool = True, cu_seqlens=None, rows=None):
+    """Returns (O, LSE): O [nsel, bs, hq, hd], LSE [bs, hq, nsel] (nsel = N or len(rows))."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    N, bs, hq, hd = q.shape
+    hkv = k.shape[2]
+    cu = _cu64(cu_seqlens)
+    rows_a = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    nsel = N if rows_a is None else len(rows_a)
+    o = np.empty((nsel, bs, hq, hd))
+    lse = np.empty((bs, hq, nsel))
+    rc = _load().oracle_attn_fwd(
+        q.ctypes.data, k.ctypes.data, v.ctypes.data, N, bs, hq, hkv, hd, float(scale), int(causal),
+        None if cu is None else cu.ctypes.data, 0 if cu is None else len(cu) - 1,
+        None if rows_a is None else rows_a.ctypes.data, nsel, o.ctypes.data, lse.ctypes.data)
+    if rc:
+        raise ValueError("oracle_attn_fwd: bad arguments")
+    return o, lse
+
+
+def attn_bwd(q, k, v, dout, scale: float, causal: bool = True, cu_seqlens=None,
+             dq_rows=None, dkv_cols=None):
+    """Returns (dQ, dK, dV), compact over the selected rows / columns."""
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    N, bs, hq, hd = q.shape
+    hkv = k.shape[2]
+    cu = _cu64(cu_seqlens)
+    qr = None if dq_rows is None else np.ascontiguousarray(dq_rows, dtype=np.int64)
+    kc = None if dkv_cols is None else np.ascontiguousarray(dkv_cols, dtype=np.int64)
+    nq = N if qr is None else len(qr)
+    nk = N if kc is None else len(kc)
+    dq = np.empty((nq, bs, hq, hd))
+    dk = np.empty((nk, bs, hkv, hd))
+    dv = np.empty((nk, bs, hkv, hd))
+    # a zero-length selection still needs a valid (non-NULL) pointer
+    dummy = np.zeros(1, np.int64)
+    qr_p = None if qr is None else (qr if nq else dummy).ctypes.data
+    kc_p = None if kc is None else (kc if nk else dummy).ctypes.data
+    rc = _load().oracle_attn_bwd(
+        q.ctypes.data, k.ctypes.data, v.ctypes.data, dout.ctypes.data, N, bs, hq, hkv, hd,
+        float(scale), int(causal), None if cu is None else cu.ctypes.data,
+        0 if cu is None else len(cu) - 1, qr_p, nq, kc_p, nk,
+        dq.ctypes.data, dk.ctypes.data, dv.ctypes.data)
+    if rc:
+        raise ValueError("oracle_attn_bwd: bad arguments")
+    return dq, dk, dv

@@ -1,0 +1,358 @@
+/*
+ * ORACLE -- test infrastructure only.
+ *
+ * A plain, slow CPU statement of what one rank's share of an Ulysses
+ * sequence-parallel attention layer computes.  Only the tests, the smoke
+ * check and the benchmark's CPU-baseline leg may load it; the product path
+ * never does.  It shares no code with the HIP library.
+ *
+ * Sources (the pages' titles and sections):
+ *  - "Ulysses Sequence Parallelism: Training with Million-Token Contexts"
+ *    (Hugging Face blog, Chinese translation), section "The challenge of
+ *    long-sequence training" -> how Ulysses works: sequence sharding, an
+ *    all-to-all that leaves every GPU with all positions for a subset of the
+ *    heads, local attention per head, and an inverse all-to-all.
+ *  - "DeepSpeed Ulysses SP and ALST integration guide for HF Transformers"
+ *    (zwxr.cn), sections on the attention adapter (tensor layout
+ *    [sl, bs, hc, hs]; causality from position ids instead of a 4D mask;
+ *    GQA/MQA head rules; packed samples reset position ids).
+ *  - Transformers "DeepSpeed ALST/Ulysses" guide walkthrough
+ *    (demingchina.com), the two-GPU layout diagram.
+ *  - "DeepSpeed Ulysses: system optimizations for training extremely long
+ *    sequence Transformer models" (DeepSpeed blog, Chinese), the design
+ *    section (per-head attention after the first all-to-all).
+ *
+ * Readings where the pages are silent (also listed in the design doc):
+ *  - attention is standard scaled dot-product softmax attention per head
+ *    (the formula on the DeepSpeed blog is an image that did not survive);
+ *  - query head h uses key/value head floor(h / (hq / hkv));
+ *  - causal mask is j <= i (queries and keys share positions);
+ *  - with documents (cu_seqlens) a query attends only inside its own
+ *    document; without causality it attends to its whole document;
+ *  - LSE is the natural-log log-sum-exp of the scaled scores;
+ *  - the backward pass is the gradient of O with respect to Q, K and V.
+ *
+ * Arithmetic: every float sum and product is carried out in double from the
+ * exact input values; exp and log are the C library's double functions.
+ * Loops over independent output rows may run on several threads
+ * (OpenMP); every output element is computed by one thread in a fixed
+ * order, so results do not depend on the thread count.
+ *
+ * Parity pins for every function are in tests/test_oracle_pins.py.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/* ------------------------------------------------------------------------
+ * Layout exchange, one rank's view.
+ *
+ * Seq-sharded: chunk c (held by rank c before the exchange) is
+ * [n, bs, heads, hd] and holds tokens [c*n, (c+1)*n) with all heads.
+ * Head-sharded: rank r holds [P*n, bs, heads_l, hd], all tokens for its
+ * head slice.  heads_l = heads / P; when heads < P (and P % heads == 0) the
+ * head is replicated: heads_l = 1 and rank r takes head floor(r*heads/P).
+ * ---------------------------------------------------------------------- */
+
+static int local_heads(int heads, int P) { return heads >= P ? heads / P : 1; }
+
+static int source_head(int heads, int P, int rank, int h) {
+  if (heads >= P) return rank * (heads / P) + h;
+  return (int)(((long)rank * heads) / P);
+}
+
+/* out[c*n + s, b, h, :] = chunk_c[s, b, source_head(h), :] */
+int oracle_seq_to_head(const void* const* chunks, int P, int rank, int64_t n, int bs,
+                       int heads, int hd, int esize, void* out) {
+  if (P <= 0 || rank < 0 || rank >= P || n < 0 || bs <= 0 || heads <= 0 || hd <= 0) return -1;
+  if (heads >= P ? heads % P : P % heads) return -1;
+  const int hl = local_heads(heads, P);
+  const size_t row = (size_t)hd * esize;
+  for (int c = 0; c < P; ++c) {
+    const char* src = (const char*)chunks[c];
+    for (int64_t s = 0; s < n; ++s)
+      for (int b = 0; b < bs; ++b)
+        for (int h = 0; h < hl; ++h) {
+          const int64_t t = (int64_t)c * n + s;
+          const size_t o_off = ((((size_t)t * bs + b) * hl) + h) * row;
+          const size_t i_off = ((((size_t)s * bs + b) * heads) + source_head(heads, P, rank, h)) * row;
+          memcpy((char*)out + o_off, src + i_off, row);
+        }
+  }
+  return 0;
+}
+
+/* chunk_c[s, b, rank*hl + h, :] = in[c*n + s, b, h, :]; other head slots of
+ * the chunks are not written (they belong to the other ranks). */
+int oracle_head_to_seq(const void* in, int P, int rank, int64_t n, int bs, int heads,
+                       int hd, int esize, void* const* chunks) {
+  if (P <= 0 || rank < 0 || rank >= P || n < 0 || bs <= 0 || heads <= 0 || hd <= 0) return -1;
+  if (heads % P) return -1;
+  const int hl = heads / P;
+  const size_t row = (size_t)hd * esize;
+  for (int c = 0; c < P; ++c) {
+    char* dst = (char*)chunks[c];
+    for (int64_t s = 0; s < n; ++s)
+      for (int b = 0; b < bs; ++b)
+        for (int h = 0; h < hl; ++h) {
+          const int64_t t = (int64_t)c * n + s;
+          const size_t i_off = ((((size_t)t * bs + b) * hl) + h) * row;
+          const size_t o_off = ((((size_t)s * bs + b) * heads) + rank * hl + h) * row;
+          memcpy(dst + o_off, (const char*)in + i_off, row);
+        }
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------
+ * Attention.
+ *
+ * Tensors are [N, bs, heads, hd] (row-major, the pages' [sl, bs, hc, hs]).
+ * cu is NULL (one document) or cu[0]=0 < cu[1] < ... < cu[ndocs]=N.
+ * ---------------------------------------------------------------------- */
+
+typedef struct {
+  const double *q, *k, *v;
+  int64_t N;
+  int bs, hq, hkv, hd;
+  double scale;
+  int causal;
+  const int64_t* cu;
+  int ndocs;
+} attn_t;
+
+static double qv(const attn_t* a, const double* x, int heads, int64_t t, int b, int h, int e) {
+  return x[(((size_t)t * a->bs + b) * heads + h) * a->hd + e];
+}
+
+/* Document index of position i. */
+static int doc_of(const attn_t* a, int64_t i) {
+  if (!a->cu) return 0;
+  int d = 0;
+  while (d + 1 < a->ndocs && a->cu[d + 1] <= i) ++d;
+  return d;
+}
+
+static int64_t doc_start(const attn_t* a, int64_t i) { return a->cu ? a->cu[doc_of(a, i)] : 0; }
+static int64_t doc_end(const attn_t* a, int64_t i) { return a->cu ? a->cu[doc_of(a, i) + 1] : a->N; }
+
+/* Keys j that query i may attend to: [lo, hi). */
+static void key_range(const attn_t* a, int64_t i, int64_t* lo, int64_t* hi) {
+  *lo = doc_start(a, i);
+  *hi = a->causal ? i + 1 : doc_end(a, i);
+}
+
+/* Queries i that attend to key j: [lo, hi). */
+static void query_range(const attn_t* a, int64_t j, int64_t* lo, int64_t* hi) {
+  *lo = a->causal ? j : doc_start(a, j);
+  *hi = doc_end(a, j);
+}
+
+static int kv_head(const attn_t* a, int h) { return h / (a->hq / a->hkv); }
+
+/* s_ij = scale * <q_i, k_j> */
+static double score(const attn_t* a, int64_t i, int64_t j, int b, int h) {
+  const int kh = kv_head(a, h);
+  double acc = 0.0;
+  for (int e = 0; e < a->hd; ++e)
+    acc += qv(a, a->q, a->hq, i, b, h, e) * qv(a, a->k, a->hkv, j, b, kh, e);
+  return a->scale * acc;
+}
+
+/* Row statistics of query (i, b, h): LSE_i = m_i + ln sum_j exp(s_ij - m_i)
+ * and, if o != NULL, O_i = sum_j exp(s_ij - LSE_i) v_j.  s is scratch of
+ * length >= number of keys. */
+static double row_forward(const attn_t* a, int64_t i, int b, int h, double* s, double* o) {
+  int64_t lo, hi;
+  key_range(a, i, &lo, &hi);
+  double m = -INFINITY;
+  for (int64_t j = lo; j < hi; ++j) {
+    s[j - lo] = score(a, i, j, b, h);
+    if (s[j - lo] > m) m = s[j - lo];
+  }
+  double l = 0.0;
+  for (int64_t j = lo; j < hi; ++j) l += exp(s[j - lo] - m);
+  const double lse = m + log(l);
+  if (o) {
+    const int kh = kv_head(a, h);
+    for (int e = 0; e < a->hd; ++e) o[e] = 0.0;
+    for (int64_t j = lo; j < hi; ++j) {
+      const double p = exp(s[j - lo] - lse);
+      for (int e = 0; e < a->hd; ++e) o[e] += p * qv(a, a->v, a->hkv, j, b, kh, e);
+    }
+  }
+  return lse;
+}
+
+static int check_docs(const int64_t* cu, int ndocs, int64_t N) {
+  if (!cu) return 0;
+  if (ndocs < 1 || cu[0] != 0 || cu[ndocs] != N) return -1;
+  for (int d = 0; d < ndocs; ++d)
+    if (cu[d + 1] <= cu[d]) return -1;
+  return 0;
+}
+
+/*
+ * Forward.  rows: NULL for all N positions, else nrows positions.  Outputs
+ * are compact over the selected positions: o[t, b, h, :] for t < nrows and
+ * lse[b, h, t].  Returns 0, or -1 on malformed arguments.
+ */
+int oracle_attn_fwd(const double* q, const double* k, const double* v, int64_t N, int bs,
+                    int hq, int hkv, int hd, double scale, int causal, const int64_t* cu,
+                    int ndocs, const int64_t* rows, int64_t nrows, double* o, double* lse) {
+  if (N <= 0 || bs <= 0 || hq <= 0 || hkv <= 0 || hd <= 0 || hq % hkv) return -1;
+  if (check_docs(cu, ndocs, N)) return -1;
+  const attn_t a = {q, k, v, N, bs, hq, hkv, hd, scale, causal, cu, ndocs};
+  const int64_t nsel = rows ? nrows : N;
+  for (int64_t t = 0; t < nsel; ++t)
+    if (rows && (rows[t] < 0 || rows[t] >= N)) return -1;
+  const int64_t total = nsel * bs * hq;
+#pragma omp parallel
+  {
+    double* s = (double*)malloc(sizeof(double) * (size_t)N);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t w = 0; w < total; ++w) {
+      const int64_t t = w / (bs * hq);
+      const int b = (int)((w / hq) % bs);
+      const int h = (int)(w % hq);
+      const int64_t i = rows ? rows[t] : t;
+      double* orow = o + (((size_t)t * bs + b) * hq + h) * hd;
+      lse[((size_t)b * hq + h) * nsel + t] = row_forward(&a, i, b, h, s, orow);
+    }
+    free(s);
+  }
+  return 0;
+}
+
+/*
+ * Backward of O with respect to Q, K, V for upstream gradient dO:
+ *   D_i    = sum_e dO_ie O_ie
+ *   P_ij   = exp(s_ij - LSE_i)
+ *   dP_ij  = <dO_i, v_j>
+ *   dS_ij  = P_ij (dP_ij - D_i)
+ *   dQ_i   = scale * sum_j dS_ij k_j
+ *   dK_j   = scale * sum_{h in group} sum_i dS_ij q_i
+ *   dV_j   = sum_{h in group} sum_i P_ij dO_i
+ * where j ranges over the keys query i attends to, and i over the queries
+ * that attend to key j.  LSE_i and O_i are this file's own forward values.
+ *
+ * dq_rows: NULL for all positions, else the positions whose dQ is wanted
+ * (dq is compact [t, bs, hq, hd]).  dkv_cols likewise for dK/dV
+ * (compact [t, bs, hkv, hd]).  Pass n = 0 with a non-NULL pointer to skip.
+ */
+int oracle_attn_bwd(const double* q, const double* k, const double* v, const double* dout,
+                    int64_t N, int bs, int hq, int hkv, int hd, double scale, int causal,
+                    const int64_t* cu, int ndocs, const int64_t* dq_rows, int64_t n_dq,
+                    const int64_t* dkv_cols, int64_t n_dkv, double* dq, double* dk, double* dv) {
+  if (N <= 0 || bs <= 0 || hq <= 0 || hkv <= 0 || hd <= 0 || hq % hkv) return -1;
+  if (check_docs(cu, ndocs, N)) return -1;
+  const attn_t a = {q, k, v, N, bs, hq, hkv, hd, scale, causal, cu, ndocs};
+  const int64_t nq = dq_rows ? n_dq : N;
+  const int64_t nk = dkv_cols ? n_dkv : N;
+  for (int64_t t = 0; t < nq; ++t)
+    if (dq_rows && (dq_rows[t] < 0 || dq_rows[t] >= N)) return -1;
+  for (int64_t t = 0; t < nk; ++t)
+    if (dkv_cols && (dkv_cols[t] < 0 || dkv_cols[t] >= N)) return -1;
+  const int g = hq / hkv;
+
+  /* Which query rows need LSE and D: the dQ rows, and every query that
+   * attends to a requested key. */
+  char* need = (char*)calloc((size_t)N, 1);
+  for (int64_t t = 0; t < nq; ++t) need[dq_rows ? dq_rows[t] : t] = 1;
+  for (int64_t t = 0; t < nk; ++t) {
+    int64_t lo, hi;
+    query_range(&a, dkv_cols ? dkv_cols[t] : t, &lo, &hi);
+    for (int64_t i = lo; i < hi; ++i) need[i] = 1;
+  }
+  double* LSE = (double*)malloc(sizeof(double) * (size_t)N * bs * hq);
+  double* D = (double*)malloc(sizeof(double) * (size_t)N * bs * hq);
+  const int64_t total = N * bs * hq;
+#pragma omp parallel
+  {
+    double* s = (double*)malloc(sizeof(double) * (size_t)N);
+    double* o = (double*)malloc(sizeof(double) * (size_t)hd);
+#pragma omp for schedule(dynamic, 16)
+    for (int64_t w = 0; w < total; ++w) {
+      const int64_t i = w / (bs * hq);
+      if (!need[i]) continue;
+      const int b = (int)((w / hq) % bs);
+      const int h = (int)(w % hq);
+      const size_t idx = ((size_t)b * hq + h) * N + i;
+      LSE[idx] = row_forward(&a, i, b, h, s, o);
+      double d = 0.0;
+      for (int e = 0; e < hd; ++e) d += qv(&a, dout, hq, i, b, h, e) * o[e];
+      D[idx] = d;
+    }
+    free(s);
+    free(o);
+  }
+
+  /* dQ rows. */
+  const int64_t totq = nq * bs * hq;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t w = 0; w < totq; ++w) {
+    const int64_t t = w / (bs * hq);
+    const int b = (int)((w / hq) % bs);
+    const int h = (int)(w % hq);
+    const int64_t i = dq_rows ? dq_rows[t] : t;
+    const int kh = kv_head(&a, h);
+    const size_t idx = ((size_t)b * hq + h) * N + i;
+    double* out = dq + (((size_t)t * bs + b) * hq + h) * hd;
+    for (int e = 0; e < hd; ++e) out[e] = 0.0;
+    int64_t lo, hi;
+    key_range(&a, i, &lo, &hi);
+    for (int64_t j = lo; j < hi; ++j) {
+      const double p = exp(score(&a, i, j, b, h) - LSE[idx]);
+      double dp = 0.0;
+      for (int e = 0; e < hd; ++e) dp += qv(&a, dout, hq, i, b, h, e) * qv(&a, v, hkv, j, b, kh, e);
+      const double ds = p * (dp - D[idx]);
+      for (int e = 0; e < hd; ++e) out[e] += ds * qv(&a, k, hkv, j, b, kh, e);
+    }
+    for (int e = 0; e < hd; ++e) out[e] *= scale;
+  }
+
+  /* dK, dV columns. */
+  const int64_t totk = nk * bs * hkv;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t w = 0; w < totk; ++w) {
+    const int64_t t = w / (bs * hkv);
+    const int b = (int)((w / hkv) % bs);
+    const int kh = (int)(w % hkv);
+    const int64_t j = dkv_cols ? dkv_cols[t] : t;
+    double* okk = dk + (((size_t)t * bs + b) * hkv + kh) * hd;
+    double* ovv = dv + (((size_t)t * bs + b) * hkv + kh) * hd;
+    for (int e = 0; e < hd; ++e) okk[e] = ovv[e] = 0.0;
+    int64_t lo, hi;
+    query_range(&a, j, &lo, &hi);
+    for (int h = kh * g; h < (kh + 1) * g; ++h)
+      for (int64_t i = lo; i < hi; ++i) {
+        const size_t idx = ((size_t)b * hq + h) * N + i;
+        const double p = exp(score(&a, i, j, b, h) - LSE[idx]);
+        double dp = 0.0;
+        for (int e = 0; e < hd; ++e) dp += qv(&a, dout, hq, i, b, h, e) * qv(&a, v, hkv, j, b, kh, e);
+        const double ds = p * (dp - D[idx]);
+        for (int e = 0; e < hd; ++e) {
+          okk[e] += ds * qv(&a, q, hq, i, b, h, e);
+          ovv[e] += p * qv(&a, dout, hq, i, b, h, e);
+        }
+      }
+    for (int e = 0; e < hd; ++e) okk[e] *= scale;
+  }
+  free(need);
+  free(LSE);
+  free(D);
+  return 0;
+}

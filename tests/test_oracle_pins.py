@@ -1,0 +1,384 @@
+"""Pins of the oracle to facts outside itself (CPU only).
+
+Each test checks the oracle against something the pages or mathematics fix:
+the pages' two-GPU layout diagram, library routines that compute the same
+definition by another route (numpy slicing, torch's fp64 scaled-dot-product
+attention, torch autograd), closed forms, invariants and finite differences.
+A plausible slip in the oracle (a dropped term, a wrong sign or index, a
+transposed operand, an off-by-one mask) fails at least one of them.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+RNG = np.random.default_rng(20261202)
+
+
+def rand(*shape):
+    return RNG.standard_normal(shape)
+
+
+def doc_ids(cu, N):
+    return np.searchsorted(np.asarray(cu), np.arange(N), side="right") - 1
+
+
+def allowed_mask(N, causal, cu):
+    """Boolean [N, N] mask (query, key) built from positions and document ids."""
+    i = np.arange(N)[:, None]
+    j = np.arange(N)[None, :]
+    m = np.ones((N, N), dtype=bool)
+    if causal:
+        m &= j <= i
+    if cu is not None:
+        d = doc_ids(cu, N)
+        m &= d[:, None] == d[None, :]
+    return m
+
+
+def sdpa_reference(q, k, v, scale, causal, cu):
+    """torch's fp64 scaled_dot_product_attention; layout [N, bs, H, hd]."""
+    tq = torch.from_numpy(q).permute(1, 2, 0, 3)
+    tk = torch.from_numpy(k).permute(1, 2, 0, 3)
+    tv = torch.from_numpy(v).permute(1, 2, 0, 3)
+    mask = torch.from_numpy(allowed_mask(q.shape[0], causal, cu))
+    out = torch.nn.functional.scaled_dot_product_attention(
+        tq, tk, tv, attn_mask=mask, scale=scale, enable_gqa=q.shape[2] != k.shape[2])
+    return out.permute(2, 0, 1, 3).numpy()
+
+
+def explicit_attention_torch(q, k, v, scale, causal, cu):
+    """Scores -> masked softmax -> weighted values, by torch tensor ops (fp64);
+    returns (O, LSE, autograd-ready leaf tensors)."""
+    N, bs, hq, hd = q.shape
+    g = hq // k.shape[2]
+    tq = torch.tensor(q, requires_grad=True)
+    tk = torch.tensor(k, requires_grad=True)
+    tv = torch.tensor(v, requires_grad=True)
+    kr = tk.repeat_interleave(g, dim=2)
+    vr = tv.repeat_interleave(g, dim=2)
+    s = torch.einsum("ibhe,jbhe->bhij", tq, kr) * scale
+    mask = torch.from_numpy(allowed_mask(N, causal, cu))
+    s = s.masked_fill(~mask, float("-inf"))
+    lse = torch.logsumexp(s, dim=-1)                       # [bs, hq, N]
+    p = torch.softmax(s, dim=-1)
+    o = torch.einsum("bhij,jbhe->ibhe", p, vr)
+    return o, lse, (tq, tk, tv)
+
+
+# --------------------------------------------------------------------------
+# Layout exchange
+# --------------------------------------------------------------------------
+
+def test_layout_matches_two_gpu_diagram():
+    fx = json.load(open(os.path.join(GOLDEN, "layout_2gpu_diagram.json")))
+    chunks = [np.asarray(fx["seq_sharded"][f"gpu{c}"], dtype=np.int32)[:, None, :, None]
+              for c in range(fx["P"])]
+    for r in range(fx["P"]):
+        got = oracle.seq_to_head(chunks, r)
+        want = np.asarray(fx["head_sharded"][f"gpu{r}"], dtype=np.int32)[:, None, :, None]
+        np.testing.assert_array_equal(got, want)
+    back = [np.full_like(c, -1) for c in chunks]
+    for r in range(fx["P"]):
+        x = np.asarray(fx["head_sharded"][f"gpu{r}"], dtype=np.int32)[:, None, :, None].copy()
+        oracle.head_to_seq(x, back, r)
+    for c in range(fx["P"]):
+        np.testing.assert_array_equal(back[c], chunks[c])
+
+
+@pytest.mark.parametrize("P,heads,bs,n,hd,dtype", [
+    (2, 4, 1, 8, 16, np.float32), (4, 8, 2, 5, 8, np.uint16), (8, 32, 1, 3, 4, np.uint16),
+    (8, 8, 1, 4, 128, np.uint16), (1, 3, 2, 6, 4, np.float64)])
+def test_seq_to_head_is_concat_then_head_slice(P, heads, bs, n, hd, dtype):
+    hl = heads // P
+    chunks = [RNG.integers(0, 60000, size=(n, bs, heads, hd)).astype(dtype) for _ in range(P)]
+    full = np.concatenate(chunks, axis=0)
+    for r in range(P):
+        got = oracle.seq_to_head(chunks, r)
+        np.testing.assert_array_equal(got, full[:, :, r * hl:(r + 1) * hl, :])
+        assert got.tobytes() == np.ascontiguousarray(full[:, :, r * hl:(r + 1) * hl, :]).tobytes()
+
+
+@pytest.mark.parametrize("P,heads", [(8, 2), (4, 1), (8, 4), (2, 1)])
+def test_seq_to_head_replicates_kv_when_heads_below_P(P, heads):
+    chunks = [RNG.integers(0, 1000, size=(3, 1, heads, 4)).astype(np.int16) for _ in range(P)]
+    full = np.concatenate(chunks, axis=0)
+    for r in range(P):
+        got = oracle.seq_to_head(chunks, r)
+        src = (r * heads) // P
+        np.testing.assert_array_equal(got, full[:, :, src:src + 1, :])
+
+
+@pytest.mark.parametrize("P,heads", [(8, 12), (3, 4), (8, 3)])
+def test_seq_to_head_rejects_indivisible_heads(P, heads):
+    chunks = [np.zeros((2, 1, heads, 4), np.float32) for _ in range(P)]
+    with pytest.raises(ValueError):
+        oracle.seq_to_head(chunks, 0)
+
+
+@pytest.mark.parametrize("P,heads,bs", [(2, 4, 1), (4, 8, 2), (8, 32, 1)])
+def test_round_trip_over_all_ranks_is_identity_and_touches_only_own_slots(P, heads, bs):
+    n, hd = 5, 8
+    hl = heads // P
+    chunks = [RNG.integers(0, 65535, size=(n, bs, heads, hd)).astype(np.uint16) for _ in range(P)]
+    canary = np.uint16(0xDEAD)
+    back = [np.full_like(c, canary) for c in chunks]
+    for r in range(P):
+        oracle.head_to_seq(oracle.seq_to_head(chunks, r), back, r)
+        for c in range(P):
+            owned = back[c][:, :, : (r + 1) * hl, :]
+            np.testing.assert_array_equal(owned, chunks[c][:, :, : (r + 1) * hl, :])
+            assert np.all(back[c][:, :, (r + 1) * hl:, :] == canary)
+    for c in range(P):
+        assert back[c].tobytes() == chunks[c].tobytes()
+
+
+def test_single_rank_exchange_is_identity():
+    x = RNG.integers(0, 65535, size=(7, 2, 3, 4)).astype(np.uint16)
+    np.testing.assert_array_equal(oracle.seq_to_head([x], 0), x)
+
+
+# --------------------------------------------------------------------------
+# Attention forward
+# --------------------------------------------------------------------------
+
+FWD_CASES = [
+    # N, bs, hq, hkv, hd, scale, causal, cu
+    (1, 1, 2, 2, 8, 0.35, True, None),
+    (7, 1, 2, 2, 8, 0.35, True, None),
+    (33, 2, 4, 1, 16, 0.25, True, None),
+    (40, 1, 4, 2, 8, 1.0, True, None),
+    (64, 1, 2, 1, 16, 0.125, True, [0, 1, 20, 21, 64]),
+    (30, 2, 2, 2, 8, 0.5, False, None),
+    (30, 1, 4, 2, 8, 0.5, False, [0, 11, 12, 30]),
+]
+
+
+@pytest.mark.parametrize("N,bs,hq,hkv,hd,scale,causal,cu", FWD_CASES)
+def test_fwd_matches_torch_sdpa_and_logsumexp(N, bs, hq, hkv, hd, scale, causal, cu):
+    q, k, v = rand(N, bs, hq, hd), rand(N, bs, hkv, hd), rand(N, bs, hkv, hd)
+    o, lse = oracle.attn_fwd(q, k, v, scale, causal, cu)
+    np.testing.assert_allclose(o, sdpa_reference(q, k, v, scale, causal, cu), rtol=1e-11, atol=1e-12)
+    _, lse_t, _ = explicit_attention_torch(q, k, v, scale, causal, cu)
+    np.testing.assert_allclose(lse, lse_t.detach().numpy(), rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("cu", [None, [0, 5, 6, 17, 40]])
+def test_fwd_zero_q_gives_prefix_mean_and_log_count(cu):
+    N, hd = 40, 8
+    q = np.zeros((N, 1, 2, hd))
+    k, v = rand(N, 1, 1, hd), rand(N, 1, 1, hd)
+    o, lse = oracle.attn_fwd(q, k, v, 0.7, True, cu)
+    starts = np.zeros(N, dtype=int) if cu is None else np.asarray(cu)[doc_ids(cu, N)]
+    for i in range(N):
+        mean = v[starts[i]:i + 1, 0, 0, :].mean(axis=0)
+        for h in range(2):
+            np.testing.assert_allclose(o[i, 0, h], mean, rtol=1e-12, atol=1e-13)
+            assert abs(lse[0, h, i] - np.log(i - starts[i] + 1)) < 1e-12
+
+
+def test_fwd_constant_v_returns_v():
+    N, hd = 50, 16
+    q, k = rand(N, 2, 4, hd), rand(N, 2, 2, hd)
+    row = rand(hd)
+    v = np.broadcast_to(row, (N, 2, 2, hd)).copy()
+    o, _ = oracle.attn_fwd(q, k, v, 0.3, True, [0, 13, 50])
+    np.testing.assert_allclose(o, np.broadcast_to(row, o.shape), rtol=1e-12, atol=1e-12)
+
+
+def test_fwd_single_token_returns_its_value_and_score():
+    q, k, v = rand(1, 1, 3, 8), rand(1, 1, 3, 8), rand(1, 1, 3, 8)
+    o, lse = oracle.attn_fwd(q, k, v, 0.9, True)
+    np.testing.assert_allclose(o, v, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(lse[0, :, 0], 0.9 * np.sum(q[0, 0] * k[0, 0], axis=-1), rtol=1e-14)
+
+
+def test_fwd_gqa_equals_mha_with_repeated_kv():
+    N, hd, g = 37, 8, 4
+    q, k, v = rand(N, 1, 8, hd), rand(N, 1, 2, hd), rand(N, 1, 2, hd)
+    o1, l1 = oracle.attn_fwd(q, k, v, 0.4, True)
+    o2, l2 = oracle.attn_fwd(q, np.repeat(k, g, axis=2), np.repeat(v, g, axis=2), 0.4, True)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+
+
+def test_fwd_documents_are_independent_attentions():
+    cu = [0, 9, 10, 31, 48]
+    N, hd = 48, 8
+    q, k, v = rand(N, 1, 2, hd), rand(N, 1, 1, hd), rand(N, 1, 1, hd)
+    o, lse = oracle.attn_fwd(q, k, v, 0.5, True, cu)
+    for a, b in zip(cu[:-1], cu[1:]):
+        od, ld = oracle.attn_fwd(q[a:b], k[a:b], v[a:b], 0.5, True)
+        np.testing.assert_allclose(o[a:b], od, rtol=1e-13, atol=1e-14)
+        np.testing.assert_allclose(lse[:, :, a:b], ld, rtol=1e-13, atol=1e-14)
+
+
+def test_fwd_sampled_rows_equal_full_rows():
+    N, hd = 45, 8
+    cu = [0, 20, 45]
+    q, k, v = rand(N, 2, 2, hd), rand(N, 2, 1, hd), rand(N, 2, 1, hd)
+    o, lse = oracle.attn_fwd(q, k, v, 0.5, True, cu)
+    rows = [44, 0, 19, 20, 7]
+    os_, ls = oracle.attn_fwd(q, k, v, 0.5, True, cu, rows=rows)
+    np.testing.assert_array_equal(os_, o[rows])
+    np.testing.assert_array_equal(ls, lse[:, :, rows])
+
+
+@pytest.mark.parametrize("P,hq,hkv", [(2, 4, 4), (4, 8, 4), (4, 8, 2)])
+def test_head_sharded_share_equals_full_mha_restricted_to_rank_heads(P, hq, hkv):
+    """Heads are independent, so running every rank's share (exchange,
+    local attention on hq/P heads, inverse exchange) rebuilds full
+    multi-head attention."""
+    N, hd, n = 24, 8, 24 // P
+    q, k, v = rand(N, 1, hq, hd), rand(N, 1, hkv, hd), rand(N, 1, hkv, hd)
+    o_full, _ = oracle.attn_fwd(q, k, v, 0.6, True)
+    qc = [np.ascontiguousarray(q[c * n:(c + 1) * n]) for c in range(P)]
+    kc = [np.ascontiguousarray(k[c * n:(c + 1) * n]) for c in range(P)]
+    vc = [np.ascontiguousarray(v[c * n:(c + 1) * n]) for c in range(P)]
+    oc = [np.full((n, 1, hq, hd), np.nan) for _ in range(P)]
+    for r in range(P):
+        ql, kl, vl = oracle.seq_to_head(qc, r), oracle.seq_to_head(kc, r), oracle.seq_to_head(vc, r)
+        ol, _ = oracle.attn_fwd(ql, kl, vl, 0.6, True)
+        oracle.head_to_seq(np.ascontiguousarray(ol), oc, r)
+    np.testing.assert_allclose(np.concatenate(oc, axis=0), o_full, rtol=1e-13, atol=1e-14)
+
+
+def test_fwd_rejects_bad_documents():
+    q = rand(8, 1, 1, 4)
+    for cu in ([0, 4, 7], [1, 8], [0, 4, 4, 8]):
+        with pytest.raises(ValueError):
+            oracle.attn_fwd(q, q, q, 1.0, True, cu)
+
+
+# --------------------------------------------------------------------------
+# Attention backward
+# --------------------------------------------------------------------------
+
+BWD_CASES = [
+    (9, 1, 2, 2, 8, 0.4, True, None),
+    (33, 2, 4, 1, 8, 0.25, True, None),
+    (40, 1, 4, 2, 16, 1.3, True, [0, 1, 17, 18, 40]),
+    (21, 1, 2, 1, 8, 0.5, False, [0, 8, 21]),
+]
+
+
+@pytest.mark.parametrize("N,bs,hq,hkv,hd,scale,causal,cu", BWD_CASES)
+def test_bwd_matches_torch_autograd(N, bs, hq, hkv, hd, scale, causal, cu):
+    q, k, v = rand(N, bs, hq, hd), rand(N, bs, hkv, hd), rand(N, bs, hkv, hd)
+    do = rand(N, bs, hq, hd)
+    dq, dk, dv = oracle.attn_bwd(q, k, v, do, scale, causal, cu)
+    o, _, (tq, tk, tv) = explicit_attention_torch(q, k, v, scale, causal, cu)
+    o.backward(torch.from_numpy(do))
+    np.testing.assert_allclose(dq, tq.grad.numpy(), rtol=1e-10, atol=1e-11)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), rtol=1e-10, atol=1e-11)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), rtol=1e-10, atol=1e-11)
+
+
+def test_bwd_matches_central_finite_differences():
+    N, hd = 12, 4
+    cu = [0, 5, 12]
+    q, k, v = rand(N, 1, 2, hd), rand(N, 1, 1, hd), rand(N, 1, 1, hd)
+    do = rand(N, 1, 2, hd)
+    dq, dk, dv = oracle.attn_bwd(q, k, v, do, 0.8, True, cu)
+
+    def loss(q_, k_, v_):
+        o, _ = oracle.attn_fwd(q_, k_, v_, 0.8, True, cu)
+        return float(np.sum(o * do))
+
+    eps = 1e-5
+    for name, x, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        for idx in [(0, 0, 0, 1), (4, 0, 0, 3), (5, 0, 0, 0), (11, 0, x.shape[2] - 1, 2)]:
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            args_p = {"q": (xp, k, v), "k": (q, xp, v), "v": (q, k, xp)}[name]
+            args_m = {"q": (xm, k, v), "k": (q, xm, v), "v": (q, k, xm)}[name]
+            fd = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+            assert abs(fd - grad[idx]) < 1e-8 * max(1.0, abs(fd)), (name, idx, fd, grad[idx])
+
+
+def test_bwd_constant_v_has_zero_dq_dk_and_constant_k_has_zero_dq():
+    N, hd = 30, 8
+    q, k = rand(N, 1, 2, hd), rand(N, 1, 1, hd)
+    row = rand(hd)
+    vconst = np.broadcast_to(row, (N, 1, 1, hd)).copy()
+    do = rand(N, 1, 2, hd)
+    dq, dk, _ = oracle.attn_bwd(q, k, vconst, do, 0.5, True, [0, 10, 30])
+    assert np.max(np.abs(dq)) < 1e-12 and np.max(np.abs(dk)) < 1e-12
+    kconst = np.broadcast_to(rand(hd), (N, 1, 1, hd)).copy()
+    dq, _, _ = oracle.attn_bwd(q, kconst, rand(N, 1, 1, hd), do, 0.5, True)
+    assert np.max(np.abs(dq)) < 1e-12
+
+
+def test_bwd_column_sums_per_document():
+    """Softmax is shift-invariant: sum_j dK_j = 0 in each document; and
+    sum_j dV_j equals the group's summed dO over the document."""
+    N, hd, cu = 36, 8, [0, 7, 8, 36]
+    q, k, v = rand(N, 1, 4, hd), rand(N, 1, 2, hd), rand(N, 1, 2, hd)
+    do = rand(N, 1, 4, hd)
+    _, dk, dv = oracle.attn_bwd(q, k, v, do, 0.7, True, cu)
+    for a, b in zip(cu[:-1], cu[1:]):
+        np.testing.assert_allclose(dk[a:b].sum(axis=0), 0.0, atol=1e-12)
+        for kh in range(2):
+            want = do[a:b, :, 2 * kh:2 * kh + 2].sum(axis=(0, 2))
+            np.testing.assert_allclose(dv[a:b, :, kh].sum(axis=0), want, rtol=1e-12, atol=1e-12)
+
+
+def test_bwd_zero_q_dv_closed_form():
+    N, hd, cu = 25, 4, [0, 10, 25]
+    q = np.zeros((N, 1, 2, hd))
+    k, v, do = rand(N, 1, 1, hd), rand(N, 1, 1, hd), rand(N, 1, 2, hd)
+    _, _, dv = oracle.attn_bwd(q, k, v, do, 1.0, True, cu)
+    starts = np.asarray(cu)[doc_ids(cu, N)]
+    ends = np.asarray(cu)[doc_ids(cu, N) + 1]
+    for j in range(N):
+        want = sum(do[i, 0, h] / (i - starts[i] + 1) for h in range(2) for i in range(j, ends[j]))
+        np.testing.assert_allclose(dv[j, 0, 0], want, rtol=1e-12, atol=1e-12)
+
+
+def test_bwd_sampled_rows_and_columns_equal_full():
+    N, hd, cu = 30, 8, [0, 12, 30]
+    q, k, v, do = rand(N, 2, 2, hd), rand(N, 2, 1, hd), rand(N, 2, 1, hd), rand(N, 2, 2, hd)
+    dq, dk, dv = oracle.attn_bwd(q, k, v, do, 0.5, True, cu)
+    rows, cols = [29, 3, 12], [0, 11, 12, 29]
+    sq, sk, sv = oracle.attn_bwd(q, k, v, do, 0.5, True, cu, dq_rows=rows, dkv_cols=cols)
+    np.testing.assert_array_equal(sq, dq[rows])
+    np.testing.assert_array_equal(sk, dk[cols])
+    np.testing.assert_array_equal(sv, dv[cols])
+    eq, ek, ev = oracle.attn_bwd(q, k, v, do, 0.5, True, cu, dq_rows=[], dkv_cols=cols)
+    assert eq.shape[0] == 0
+    np.testing.assert_array_equal(ek, dk[cols])
+
+
+# --------------------------------------------------------------------------
+# Inputs shared by both sides
+# --------------------------------------------------------------------------
+
+def test_splitmix64_matches_published_outputs():
+    fx = json.load(open(os.path.join(GOLDEN, "splitmix64_1234567.json")))
+    got = synth.splitmix64_sequence(fx["state"], len(fx["outputs"]))
+    assert [int(x) for x in got] == [int(s) for s in fx["outputs"]]
+
+
+def test_generated_normals_have_unit_moments_and_are_sliceable():
+    x = synth.normal(7, 1, (400000,))
+    assert abs(x.mean()) < 0.01 and abs(x.std() - 1.0) < 0.01
+    part = synth.normal(7, 1, (1000,), offset=1234)
+    np.testing.assert_array_equal(part, x[1234:2234])
+    b = synth.normal(7, 1, (1000,), dtype="bf16", offset=1234)
+    f = synth.normal(7, 1, (1000,), dtype="f32", offset=1234)
+    np.testing.assert_array_equal(synth.bf16_to_f64(b), torch.from_numpy(f).to(torch.bfloat16).double().numpy())
+
+
+def test_document_lengths_follow_the_recipe():
+    for seed in (1005, 1, 2):
+        lengths = synth.doc_lengths(seed, 65536)
+        assert sum(lengths) == 65536
+        assert all(512 <= L <= 16384 for L in lengths[:-1])
+        assert 1 <= lengths[-1] <= 16384
