@@ -48,10 +48,10 @@ def _load():
     lib.oracle_seq_to_head.restype = ci
     lib.oracle_head_to_seq.argtypes = [vp, ci, ci, i64, ci, ci, ci, ci, vp]
     lib.oracle_head_to_seq.restype = ci
-    lib.oracle_attn_fwd.argtypes = [vp, vp, vp, i64, ci, ci, ci, ci, dbl, ci, vp, ci, vp, i64, vp, vp]
+    lib.oracle_attn_fwd.argtypes = [vp, vp, vp, i64, ci, ci, ci, ci, dbl, ci, vp, ci, vp, i64, vp, vp, vp]
     lib.oracle_attn_fwd.restype = ci
     lib.oracle_attn_bwd.argtypes = [vp, vp, vp, vp, i64, ci, ci, ci, ci, dbl, ci, vp, ci,
-                                    vp, i64, vp, i64, vp, vp, vp]
+                                    vp, i64, vp, i64, vp, vp, vp, vp, vp, vp]
     lib.oracle_attn_bwd.restype = ci
     _lib = lib
     return lib
@@ -107,8 +107,10 @@ def _cu64(cu):
     return None if cu is None else np.ascontiguousarray(cu, dtype=np.int64)
 
 
-def attn_fwd(q, k, v, scale: float, causal: bool = True, cu_seqlens=None, rows=None):
-    """Returns (O, LSE): O [nsel, bs, hq, hd], LSE [bs, hq, nsel] (nsel = N or len(rows))."""
+def attn_fwd(q, k, v, scale: float, causal: bool = True, cu_seqlens=None, rows=None,
+             magnitude: bool = False):
+    """Returns (O, LSE): O [nsel, bs, hq, hd], LSE [bs, hq, nsel] (nsel = N or len(rows)).
+    With magnitude=True returns (O, LSE, M) where M = sum_j P_ij |v_j| (O's layout)."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     N, bs, hq, hd = q.shape
     hkv = k.shape[2]
@@ -117,18 +119,22 @@ def attn_fwd(q, k, v, scale: float, causal: bool = True, cu_seqlens=None, rows=N
     nsel = N if rows_a is None else len(rows_a)
     o = np.empty((nsel, bs, hq, hd))
     lse = np.empty((bs, hq, nsel))
+    mag = np.empty_like(o) if magnitude else None
     rc = _load().oracle_attn_fwd(
         q.ctypes.data, k.ctypes.data, v.ctypes.data, N, bs, hq, hkv, hd, float(scale), int(causal),
         None if cu is None else cu.ctypes.data, 0 if cu is None else len(cu) - 1,
-        None if rows_a is None else rows_a.ctypes.data, nsel, o.ctypes.data, lse.ctypes.data)
+        None if rows_a is None else rows_a.ctypes.data, nsel, o.ctypes.data, lse.ctypes.data,
+        None if mag is None else mag.ctypes.data)
     if rc:
         raise ValueError("oracle_attn_fwd: bad arguments")
-    return o, lse
+    return (o, lse, mag) if magnitude else (o, lse)
 
 
 def attn_bwd(q, k, v, dout, scale: float, causal: bool = True, cu_seqlens=None,
-             dq_rows=None, dkv_cols=None):
-    """Returns (dQ, dK, dV), compact over the selected rows / columns."""
+             dq_rows=None, dkv_cols=None, magnitude: bool = False):
+    """Returns (dQ, dK, dV), compact over the selected rows / columns.  With
+    magnitude=True returns (dQ, dK, dV, (M_dQ, M_dK, M_dV)): each output sum
+    re-evaluated with every term replaced by its absolute value."""
     q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
     N, bs, hq, hd = q.shape
     hkv = k.shape[2]
@@ -140,6 +146,7 @@ def attn_bwd(q, k, v, dout, scale: float, causal: bool = True, cu_seqlens=None,
     dq = np.empty((nq, bs, hq, hd))
     dk = np.empty((nk, bs, hkv, hd))
     dv = np.empty((nk, bs, hkv, hd))
+    mags = (np.empty_like(dq), np.empty_like(dk), np.empty_like(dv)) if magnitude else (None,) * 3
     # a zero-length selection still needs a valid (non-NULL) pointer
     dummy = np.zeros(1, np.int64)
     qr_p = None if qr is None else (qr if nq else dummy).ctypes.data
@@ -148,7 +155,8 @@ def attn_bwd(q, k, v, dout, scale: float, causal: bool = True, cu_seqlens=None,
         q.ctypes.data, k.ctypes.data, v.ctypes.data, dout.ctypes.data, N, bs, hq, hkv, hd,
         float(scale), int(causal), None if cu is None else cu.ctypes.data,
         0 if cu is None else len(cu) - 1, qr_p, nq, kc_p, nk,
-        dq.ctypes.data, dk.ctypes.data, dv.ctypes.data)
+        dq.ctypes.data, dk.ctypes.data, dv.ctypes.data,
+        *[None if m is None else m.ctypes.data for m in mags])
     if rc:
         raise ValueError("oracle_attn_bwd: bad arguments")
-    return dq, dk, dv
+    return (dq, dk, dv, mags) if magnitude else (dq, dk, dv)

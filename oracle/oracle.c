@@ -175,7 +175,8 @@ static double score(const attn_t* a, int64_t i, int64_t j, int b, int h) {
 /* Row statistics of query (i, b, h): LSE_i = m_i + ln sum_j exp(s_ij - m_i)
  * and, if o != NULL, O_i = sum_j exp(s_ij - LSE_i) v_j.  s is scratch of
  * length >= number of keys. */
-static double row_forward(const attn_t* a, int64_t i, int b, int h, double* s, double* o) {
+static double row_forward(const attn_t* a, int64_t i, int b, int h, double* s, double* o,
+                          double* o_mag) {
   int64_t lo, hi;
   key_range(a, i, &lo, &hi);
   double m = -INFINITY;
@@ -189,9 +190,14 @@ static double row_forward(const attn_t* a, int64_t i, int b, int h, double* s, d
   if (o) {
     const int kh = kv_head(a, h);
     for (int e = 0; e < a->hd; ++e) o[e] = 0.0;
+    if (o_mag)
+      for (int e = 0; e < a->hd; ++e) o_mag[e] = 0.0;
     for (int64_t j = lo; j < hi; ++j) {
       const double p = exp(s[j - lo] - lse);
-      for (int e = 0; e < a->hd; ++e) o[e] += p * qv(a, a->v, a->hkv, j, b, kh, e);
+      for (int e = 0; e < a->hd; ++e) {
+        o[e] += p * qv(a, a->v, a->hkv, j, b, kh, e);
+        if (o_mag) o_mag[e] += p * fabs(qv(a, a->v, a->hkv, j, b, kh, e));
+      }
     }
   }
   return lse;
@@ -208,11 +214,15 @@ static int check_docs(const int64_t* cu, int ndocs, int64_t N) {
 /*
  * Forward.  rows: NULL for all N positions, else nrows positions.  Outputs
  * are compact over the selected positions: o[t, b, h, :] for t < nrows and
- * lse[b, h, t].  Returns 0, or -1 on malformed arguments.
+ * lse[b, h, t].  o_mag (optional, same layout as o) receives the magnitude
+ * of each output sum, sum_j P_ij |v_j|: the scale of the rounding error a
+ * finite-precision evaluation of that sum can make.  Returns 0, or -1 on
+ * malformed arguments.
  */
 int oracle_attn_fwd(const double* q, const double* k, const double* v, int64_t N, int bs,
                     int hq, int hkv, int hd, double scale, int causal, const int64_t* cu,
-                    int ndocs, const int64_t* rows, int64_t nrows, double* o, double* lse) {
+                    int ndocs, const int64_t* rows, int64_t nrows, double* o, double* lse,
+                    double* o_mag) {
   if (N <= 0 || bs <= 0 || hq <= 0 || hkv <= 0 || hd <= 0 || hq % hkv) return -1;
   if (check_docs(cu, ndocs, N)) return -1;
   const attn_t a = {q, k, v, N, bs, hq, hkv, hd, scale, causal, cu, ndocs};
@@ -229,8 +239,9 @@ int oracle_attn_fwd(const double* q, const double* k, const double* v, int64_t N
       const int b = (int)((w / hq) % bs);
       const int h = (int)(w % hq);
       const int64_t i = rows ? rows[t] : t;
-      double* orow = o + (((size_t)t * bs + b) * hq + h) * hd;
-      lse[((size_t)b * hq + h) * nsel + t] = row_forward(&a, i, b, h, s, orow);
+      const size_t off = (((size_t)t * bs + b) * hq + h) * hd;
+      lse[((size_t)b * hq + h) * nsel + t] =
+          row_forward(&a, i, b, h, s, o + off, o_mag ? o_mag + off : NULL);
     }
     free(s);
   }
@@ -252,11 +263,16 @@ int oracle_attn_fwd(const double* q, const double* k, const double* v, int64_t N
  * dq_rows: NULL for all positions, else the positions whose dQ is wanted
  * (dq is compact [t, bs, hq, hd]).  dkv_cols likewise for dK/dV
  * (compact [t, bs, hkv, hd]).  Pass n = 0 with a non-NULL pointer to skip.
+ * dq_mag, dk_mag, dv_mag (optional, NULL to skip; layouts as dq, dk, dv)
+ * receive the magnitude of each output sum -- the same sum with every term
+ * replaced by its absolute value:
+ *   scale sum_j |dS_ij| |k_j|,  scale sum_h sum_i |dS_ij| |q_i|,  sum_h sum_i P_ij |dO_i|.
  */
 int oracle_attn_bwd(const double* q, const double* k, const double* v, const double* dout,
                     int64_t N, int bs, int hq, int hkv, int hd, double scale, int causal,
                     const int64_t* cu, int ndocs, const int64_t* dq_rows, int64_t n_dq,
-                    const int64_t* dkv_cols, int64_t n_dkv, double* dq, double* dk, double* dv) {
+                    const int64_t* dkv_cols, int64_t n_dkv, double* dq, double* dk, double* dv,
+                    double* dq_mag, double* dk_mag, double* dv_mag) {
   if (N <= 0 || bs <= 0 || hq <= 0 || hkv <= 0 || hd <= 0 || hq % hkv) return -1;
   if (check_docs(cu, ndocs, N)) return -1;
   const attn_t a = {q, k, v, N, bs, hq, hkv, hd, scale, causal, cu, ndocs};
@@ -291,7 +307,7 @@ int oracle_attn_bwd(const double* q, const double* k, const double* v, const dou
       const int b = (int)((w / hq) % bs);
       const int h = (int)(w % hq);
       const size_t idx = ((size_t)b * hq + h) * N + i;
-      LSE[idx] = row_forward(&a, i, b, h, s, o);
+      LSE[idx] = row_forward(&a, i, b, h, s, o, NULL);
       double d = 0.0;
       for (int e = 0; e < hd; ++e) d += qv(&a, dout, hq, i, b, h, e) * o[e];
       D[idx] = d;
@@ -311,7 +327,10 @@ int oracle_attn_bwd(const double* q, const double* k, const double* v, const dou
     const int kh = kv_head(&a, h);
     const size_t idx = ((size_t)b * hq + h) * N + i;
     double* out = dq + (((size_t)t * bs + b) * hq + h) * hd;
+    double* mag = dq_mag ? dq_mag + (((size_t)t * bs + b) * hq + h) * hd : NULL;
     for (int e = 0; e < hd; ++e) out[e] = 0.0;
+    if (mag)
+      for (int e = 0; e < hd; ++e) mag[e] = 0.0;
     int64_t lo, hi;
     key_range(&a, i, &lo, &hi);
     for (int64_t j = lo; j < hi; ++j) {
@@ -319,9 +338,14 @@ int oracle_attn_bwd(const double* q, const double* k, const double* v, const dou
       double dp = 0.0;
       for (int e = 0; e < hd; ++e) dp += qv(&a, dout, hq, i, b, h, e) * qv(&a, v, hkv, j, b, kh, e);
       const double ds = p * (dp - D[idx]);
-      for (int e = 0; e < hd; ++e) out[e] += ds * qv(&a, k, hkv, j, b, kh, e);
+      for (int e = 0; e < hd; ++e) {
+        out[e] += ds * qv(&a, k, hkv, j, b, kh, e);
+        if (mag) mag[e] += fabs(ds) * fabs(qv(&a, k, hkv, j, b, kh, e));
+      }
     }
     for (int e = 0; e < hd; ++e) out[e] *= scale;
+    if (mag)
+      for (int e = 0; e < hd; ++e) mag[e] *= scale;
   }
 
   /* dK, dV columns. */
@@ -332,9 +356,16 @@ int oracle_attn_bwd(const double* q, const double* k, const double* v, const dou
     const int b = (int)((w / hkv) % bs);
     const int kh = (int)(w % hkv);
     const int64_t j = dkv_cols ? dkv_cols[t] : t;
-    double* okk = dk + (((size_t)t * bs + b) * hkv + kh) * hd;
-    double* ovv = dv + (((size_t)t * bs + b) * hkv + kh) * hd;
+    const size_t off = (((size_t)t * bs + b) * hkv + kh) * hd;
+    double* okk = dk + off;
+    double* ovv = dv + off;
+    double* mk = dk_mag ? dk_mag + off : NULL;
+    double* mv = dv_mag ? dv_mag + off : NULL;
     for (int e = 0; e < hd; ++e) okk[e] = ovv[e] = 0.0;
+    if (mk)
+      for (int e = 0; e < hd; ++e) mk[e] = 0.0;
+    if (mv)
+      for (int e = 0; e < hd; ++e) mv[e] = 0.0;
     int64_t lo, hi;
     query_range(&a, j, &lo, &hi);
     for (int h = kh * g; h < (kh + 1) * g; ++h)
@@ -347,9 +378,13 @@ int oracle_attn_bwd(const double* q, const double* k, const double* v, const dou
         for (int e = 0; e < hd; ++e) {
           okk[e] += ds * qv(&a, q, hq, i, b, h, e);
           ovv[e] += p * qv(&a, dout, hq, i, b, h, e);
+          if (mk) mk[e] += fabs(ds) * fabs(qv(&a, q, hq, i, b, h, e));
+          if (mv) mv[e] += p * fabs(qv(&a, dout, hq, i, b, h, e));
         }
       }
     for (int e = 0; e < hd; ++e) okk[e] *= scale;
+    if (mk)
+      for (int e = 0; e < hd; ++e) mk[e] *= scale;
   }
   free(need);
   free(LSE);

@@ -382,3 +382,47 @@ def test_document_lengths_follow_the_recipe():
         assert sum(lengths) == 65536
         assert all(512 <= L <= 16384 for L in lengths[:-1])
         assert 1 <= lengths[-1] <= 16384
+
+
+# --------------------------------------------------------------------------
+# Magnitudes (sum of |terms|) used to size rounding-error tolerances
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("causal,cu", [(True, None), (True, [0, 9, 10, 30]), (False, [0, 12, 30])])
+def test_magnitudes_match_torch_absolute_sums(causal, cu):
+    """M = the output sum with every term replaced by its absolute value;
+    dS_ij comes from torch autograd on the scores, P from torch.softmax."""
+    N, hd, hq, hkv, scale = 30, 8, 4, 2, 0.6
+    g = hq // hkv
+    q, k, v, do = rand(N, 1, hq, hd), rand(N, 1, hkv, hd), rand(N, 1, hkv, hd), rand(N, 1, hq, hd)
+    _, _, mo = oracle.attn_fwd(q, k, v, scale, causal, cu, magnitude=True)
+    _, _, _, (mdq, mdk, mdv) = oracle.attn_bwd(q, k, v, do, scale, causal, cu, magnitude=True)
+    mask = torch.from_numpy(allowed_mask(N, causal, cu))
+    kr = torch.from_numpy(np.repeat(k[:, 0], g, axis=1))   # [N, hq, hd]
+    vr = torch.from_numpy(np.repeat(v[:, 0], g, axis=1))
+    tq, tdo = torch.from_numpy(q[:, 0]), torch.from_numpy(do[:, 0])
+    s = (torch.einsum("ihe,jhe->hij", tq, kr) * scale).detach().requires_grad_(True)
+    p = torch.softmax(s.masked_fill(~mask, float("-inf")), dim=-1)
+    o = torch.einsum("hij,jhe->ihe", p, vr)
+    o.backward(tdo)
+    ds = s.grad.abs()                                        # [hq, N, N]
+    pa = p.detach()
+    want_mo = torch.einsum("hij,jhe->ihe", pa, vr.abs())
+    want_mdq = scale * torch.einsum("hij,jhe->ihe", ds, kr.abs())
+    want_mdk = scale * torch.einsum("hij,ihe->jhe", ds, tq.abs()).reshape(N, hkv, g, hd).sum(2)
+    want_mdv = torch.einsum("hij,ihe->jhe", pa, tdo.abs()).reshape(N, hkv, g, hd).sum(2)
+    np.testing.assert_allclose(mo[:, 0], want_mo.numpy(), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(mdq[:, 0], want_mdq.numpy(), rtol=1e-10, atol=1e-11)
+    np.testing.assert_allclose(mdk[:, 0], want_mdk.numpy(), rtol=1e-10, atol=1e-11)
+    np.testing.assert_allclose(mdv[:, 0], want_mdv.numpy(), rtol=1e-11, atol=1e-12)
+
+
+def test_magnitudes_bound_the_values_and_equal_them_for_same_sign_terms():
+    N, hd = 25, 8
+    q, k = rand(N, 1, 2, hd), rand(N, 1, 1, hd)
+    v_pos, do_pos = np.abs(rand(N, 1, 1, hd)), np.abs(rand(N, 1, 2, hd))
+    o, _, mo = oracle.attn_fwd(q, k, v_pos, 0.5, True, magnitude=True)
+    np.testing.assert_allclose(mo, o, rtol=1e-13)            # all terms positive
+    dq, dk, dv, (mdq, mdk, mdv) = oracle.attn_bwd(q, k, v_pos, do_pos, 0.5, True, magnitude=True)
+    np.testing.assert_allclose(mdv, dv, rtol=1e-13)
+    assert np.all(mdq >= np.abs(dq) - 1e-12) and np.all(mdk >= np.abs(dk) - 1e-12)
