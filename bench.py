@@ -1,0 +1,255 @@
+#!/usr/bin/env python3
+"""Throughput of one rank's share of an Ulysses attention layer on one GPU.
+
+One step is the whole rank-share path over one batch of synthetic input,
+inputs already resident in HBM:
+
+  forward : seq_to_head(Q), seq_to_head(K), seq_to_head(V)   (8 chunks each)
+            attention forward (O, LSE)
+            head_to_seq(O)
+  backward: seq_to_head(dO)
+            attention backward (dQ, dK, dV)
+            head_to_seq(dQ), head_to_seq(dK), head_to_seq(dV)
+
+Workload: the Llama-8B-shaped rank share at P=8 and N=131072 (32 query /
+8 key-value heads globally, so 4 query heads and 1 key/value head per rank,
+head size 128, bf16, causal).  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2516.6   # MI355X dense bf16 matrix-core peak
+HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E peak
+WORKLOAD = "llama8b-share-128k"
+
+
+def parse_args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=768,
+                    help="query rows of the oracle's timed sample")
+    return ap.parse_args()
+
+
+def git_sha():
+    try:
+        return subprocess.run(["git", "rev-parse", "--short", "HEAD"], cwd=ROOT, capture_output=True,
+                              text=True, timeout=10).stdout.strip() or None
+    except Exception:
+        return None
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's share of the path; --gpus {args.gpus} is not supported "
+              "(this build runs on a single GPU, with no collectives between GPUs)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import synth
+    import ulysses_sp_attention_amd as uly
+
+    if not os.path.exists(uly.LIB_PATH):
+        from ulysses_sp_attention_amd import _build
+        _build.build_lib()
+    uly.load_library()
+    torch.cuda.set_device(0)
+
+    w = synth.WORKLOADS[WORKLOAD]
+    N, P, n, r = w.seqlen, w.P, w.n_local, w.rank
+    hl, kl, hd = w.hq_local, w.hkv_local, w.head_dim
+
+    def dev_seq(stream, heads, scale=1.0):
+        host = w.seq_tensor(stream, heads, scale=scale)
+        t = torch.from_numpy(host.view(np.int16)).view(torch.bfloat16).cuda()
+        del host
+        return t
+
+    t0 = time.time()
+    q_full = dev_seq(synth.STREAM_Q, w.hq, w.q_prescale)
+    k_full = dev_seq(synth.STREAM_K, w.hkv)
+    v_full = dev_seq(synth.STREAM_V, w.hkv)
+    do_full = dev_seq(synth.STREAM_DO, w.hq)
+    gen_s = time.time() - t0
+
+    def chunks(t):
+        return [t[c * n:(c + 1) * n] for c in range(P)]
+
+    bf = torch.bfloat16
+    cq, ck, cv, cdo = chunks(q_full), chunks(k_full), chunks(v_full), chunks(do_full)
+    o_full = torch.zeros_like(q_full)
+    dq_full, dk_full, dv_full = torch.zeros_like(q_full), torch.zeros_like(k_full), torch.zeros_like(v_full)
+    co, cdq, cdk, cdv = chunks(o_full), chunks(dq_full), chunks(dk_full), chunks(dv_full)
+    q = torch.empty((N, 1, hl, hd), dtype=bf, device="cuda")
+    k = torch.empty((N, 1, kl, hd), dtype=bf, device="cuda")
+    v = torch.empty_like(k)
+    o = torch.empty_like(q)
+    do = torch.empty_like(q)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(k)
+    lse = torch.empty((1, hl, N), dtype=torch.float32, device="cuda")
+    ws = torch.empty(uly.ulysses_attn_bwd_workspace_size(N, 1, hl, kl, hd, uly.BF16),
+                     dtype=torch.uint8, device="cuda")
+    scale = w.softmax_scale
+
+    stream = torch.cuda.current_stream()
+    names = ["pack_qkv", "attn_fwd", "unpack_o", "pack_do", "attn_bwd", "unpack_dqkv"]
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record(stream)
+        mark(0)
+        uly.ulysses_seq_to_head(cq, r, q)
+        uly.ulysses_seq_to_head(ck, r, k)
+        uly.ulysses_seq_to_head(cv, r, v)
+        mark(1)
+        uly.ulysses_attn_fwd(q, k, v, o, lse, scale, True)
+        mark(2)
+        uly.ulysses_head_to_seq(o, r, co)
+        mark(3)
+        uly.ulysses_seq_to_head(cdo, r, do)
+        mark(4)
+        uly.ulysses_attn_bwd(q, k, v, o, lse, do, dq, dk, dv, ws, scale, True)
+        mark(5)
+        uly.ulysses_head_to_seq(dq, r, cdq)
+        uly.ulysses_head_to_seq(dk, r, cdk)
+        uly.ulysses_head_to_seq(dv, r, cdv)
+        mark(6)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for s in range(args.steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_step = wall * 1e3 / args.steps
+
+    seg_ms = {nm: [] for nm in names}
+    for ev in events:
+        for i, nm in enumerate(names):
+            seg_ms[nm].append(ev[i].elapsed_time(ev[i + 1]))
+    avg = {nm: float(np.mean(v_)) for nm, v_ in seg_ms.items()}
+
+    # Algorithmic work (causal pairs per query head; recompute not counted).
+    pairs = w.causal_pairs()
+    fwd_flop = 4.0 * hd * hl * pairs
+    bwd_flop = 10.0 * hd * hl * pairs
+    e = 2
+    pack_qkv_bytes = 2.0 * N * (hl + 2 * kl) * hd * e   # read + write
+    unpack_o_bytes = 2.0 * N * hl * hd * e
+    pack_do_bytes = 2.0 * N * hl * hd * e
+    unpack_dqkv_bytes = pack_qkv_bytes
+
+    def tflops(flop, ms):
+        return flop / (ms * 1e-3) / 1e12
+
+    def gbps(b, ms):
+        return b / (ms * 1e-3) / 1e9
+
+    fwd_tf = tflops(fwd_flop, avg["attn_fwd"])
+    bwd_tf = tflops(bwd_flop, avg["attn_bwd"])
+    value = tflops(fwd_flop + bwd_flop, ms_step)
+    breakdown = {
+        "attn_fwd": {"ms": avg["attn_fwd"], "TFLOP/s": fwd_tf, "frac_of_mfma_peak": fwd_tf / MFMA_BF16_PEAK_TFLOPS},
+        "attn_bwd": {"ms": avg["attn_bwd"], "TFLOP/s": bwd_tf, "frac_of_mfma_peak": bwd_tf / MFMA_BF16_PEAK_TFLOPS},
+        "pack_qkv": {"ms": avg["pack_qkv"], "GB/s": gbps(pack_qkv_bytes, avg["pack_qkv"])},
+        "unpack_o": {"ms": avg["unpack_o"], "GB/s": gbps(unpack_o_bytes, avg["unpack_o"])},
+        "pack_do": {"ms": avg["pack_do"], "GB/s": gbps(pack_do_bytes, avg["pack_do"])},
+        "unpack_dqkv": {"ms": avg["unpack_dqkv"], "GB/s": gbps(unpack_dqkv_bytes, avg["unpack_dqkv"])},
+    }
+    pack_ms = avg["pack_qkv"] + avg["unpack_o"] + avg["pack_do"] + avg["unpack_dqkv"]
+    pack_bytes = pack_qkv_bytes + unpack_o_bytes + pack_do_bytes + unpack_dqkv_bytes
+    breakdown["pack_all"] = {"ms": pack_ms, "GB/s": gbps(pack_bytes, pack_ms),
+                             "frac_of_hbm_peak": gbps(pack_bytes, pack_ms) / HBM_PEAK_GBPS}
+
+    # Roofline of the dominant single-launch kernel: the attention forward
+    # (one launch per ulysses_attn_fwd call), timed with events on its stream.
+    dominant = max(("attn_fwd", "attn_bwd"), key=lambda k_: avg[k_])
+    roofline = {
+        "kernel": "attn_fwd_bf16_kernel",
+        "bound": "mfma",
+        "achieved": fwd_tf,
+        "peak": MFMA_BF16_PEAK_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": fwd_tf / MFMA_BF16_PEAK_TFLOPS,
+        "traffic": None,
+        "per_launch_flop": fwd_flop,
+        "note": f"largest entry point by time: {dominant}",
+    }
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, args.cpu_rows)
+
+    line = {
+        "metric": "causal attn fwd/bwd TFLOP/s at N=128K (4q/1kv heads, d=128); pack GB/s",
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD, "seqlen": N, "P": P, "rank": r, "bs": 1,
+                   "hq_local": hl, "hkv_local": kl, "head_dim": hd, "causal": True,
+                   "step": "pack QKV + attn fwd + unpack O + pack dO + attn bwd + unpack dQ/dK/dV"},
+        "breakdown": breakdown,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "input_gen_s": gen_s,
+        "git": git_sha(),
+    }
+    print(json.dumps(line))
+    return 0
+
+
+def cpu_baseline(w, n_rows):
+    """The oracle's forward on a bounded sample of query rows of the same
+    workload (all heads), timed on this host's cores; reported in the same
+    unit as the GPU (algorithmic TFLOP/s of the rows computed)."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    N = w.seqlen
+    rows = np.linspace(0, N - 1, n_rows).round().astype(np.int64)
+    q = synth.to_f64(w.head_tensor(synth.STREAM_Q, w.hq_local, scale=w.q_prescale), w.dtype)
+    k = synth.to_f64(w.head_tensor(synth.STREAM_K, w.hkv_local), w.dtype)
+    v = synth.to_f64(w.head_tensor(synth.STREAM_V, w.hkv_local), w.dtype)
+    t0 = time.perf_counter()
+    oracle.attn_fwd(q, k, v, w.softmax_scale, True, None, rows=rows)
+    dt = time.perf_counter() - t0
+    flop = 4.0 * w.head_dim * w.hq_local * float(np.sum(rows + 1))
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "seconds": dt,
+            "sample": f"attention forward for {n_rows} evenly spaced query rows of N={N} "
+                      f"(all {w.hq_local} heads), fp64, {flop:.3e} algorithmic flop"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

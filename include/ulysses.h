@@ -1,0 +1,174 @@
+/*
+ * libulysses -- one rank's share of an Ulysses sequence-parallel attention
+ * layer on an AMD Instinct MI355X (gfx950).
+ *
+ * The method (Hugging Face blog "Ulysses Sequence Parallelism: Training with
+ * Million-Token Contexts", section "The challenge of long-sequence
+ * training"; DeepSpeed blog "DeepSpeed Ulysses: system optimizations for
+ * training extremely long sequence Transformer models", design section):
+ * every rank holds a 1/P slice of the sequence with all heads; an
+ * all-to-all gives every rank all positions for 1/P of the heads; each rank
+ * runs ordinary attention for its heads; a second all-to-all restores the
+ * sequence slicing.  This library provides the per-rank pieces of that path:
+ *
+ *   ulysses_seq_to_head  -- assemble the P sequence chunks into the rank's
+ *                           full-sequence, head-sliced buffer
+ *   ulysses_head_to_seq  -- its inverse
+ *   ulysses_attn_fwd     -- causal (GQA, optionally document-masked)
+ *                           softmax attention, returning O and the LSE
+ *   ulysses_attn_bwd     -- its backward pass (dQ, dK, dV)
+ *
+ * Tensor layout is the pages' [sl, bs, hc, hs] (sequence, batch, heads, head
+ * size), contiguous row-major (DeepSpeed Ulysses SP + ALST integration guide,
+ * zwxr.cn, section on the attention adapter).
+ *
+ * Conventions for every entry point:
+ *  - Device buffers are owned by the caller.  The library never allocates or
+ *    frees memory and keeps no mutable global state; calls are re-entrant.
+ *  - Calls are asynchronous: they validate their arguments on the host,
+ *    enqueue kernels on `stream` and return.  Inputs must stay valid until
+ *    the stream work completes.  A NULL stream is the default stream.
+ *  - Argument validation runs before any HIP call.  On a validation error
+ *    nothing is launched and no output is touched.
+ *  - Device pointers must be 16-byte aligned; row sizes (head_dim * element
+ *    size) must be multiples of 16 bytes.
+ *  - Errors are returned as ulysses_status_t; no exception crosses the ABI.
+ *    ULYSSES_ERR_HIP reports a failed launch (the status hipLaunchKernel returns); faults
+ *    inside a kernel surface at the caller's next synchronisation.
+ */
+#ifndef ULYSSES_H
+#define ULYSSES_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ULYSSES_ABI_VERSION 1
+
+typedef enum {
+  ULYSSES_OK = 0,
+  ULYSSES_ERR_NULL = 1,           /* a required pointer is NULL */
+  ULYSSES_ERR_SHAPE = 2,          /* non-positive size, or head_dim not supported */
+  ULYSSES_ERR_DIVISIBILITY = 3,   /* head counts do not divide as the method requires */
+  ULYSSES_ERR_DTYPE = 4,          /* unknown element type */
+  ULYSSES_ERR_ALIGNMENT = 5,      /* pointer or row not 16-byte aligned */
+  ULYSSES_ERR_UNSUPPORTED = 6,    /* valid request this build does not implement */
+  ULYSSES_ERR_WORKSPACE = 7,      /* workspace NULL or smaller than required */
+  ULYSSES_ERR_HIP = 8             /* kernel launch failed */
+} ulysses_status_t;
+
+typedef enum {
+  ULYSSES_BF16 = 0,   /* bfloat16 storage, fp32 accumulation */
+  ULYSSES_FP32 = 1    /* float32 storage and arithmetic */
+} ulysses_dtype_t;
+
+/* ABI version of the loaded library (ULYSSES_ABI_VERSION it was built with). */
+int ulysses_abi_version(void);
+
+/* Static, NUL-terminated description of a status code.  Never NULL. */
+const char* ulysses_status_string(ulysses_status_t status);
+
+/*
+ * Sequence-sharded -> head-sharded exchange as rank `rank` sees it
+ * (Hugging Face Ulysses blog, "The challenge of long-sequence training":
+ * the first all-to-all leaves each GPU with every position for a subset of
+ * the heads; Transformers ALST guide walkthrough, two-GPU layout diagram).
+ *
+ *   chunks   host array of P device pointers (read during the call only).
+ *            Chunk c is [n_local, bs, heads, head_dim] and holds sequence
+ *            positions [c*n_local, (c+1)*n_local) with all heads.
+ *   out      device [P*n_local, bs, heads_l, head_dim]:
+ *              out[c*n_local + s, b, h, :] = chunks[c][s, b, src(h), :]
+ *            with heads_l = heads / P and src(h) = rank*heads_l + h when
+ *            heads >= P; when heads < P (GQA/MQA key/value heads, which the
+ *            integration guide says are replicated) heads_l = 1 and
+ *            src = floor(rank*heads/P).
+ *   Requires 1 <= P <= 64, 0 <= rank < P, n_local >= 0 (0 is a no-op whose
+ *   buffer pointers are not checked, so empty tensors may pass NULL),
+ *   bs >= 1, heads % P == 0 or P % heads == 0 (else ERR_DIVISIBILITY, the
+ *   pages' divisibility rule), out not overlapping any chunk.
+ *   The copy is bit-exact.
+ */
+ulysses_status_t ulysses_seq_to_head(const void* const* chunks, int P, int rank,
+                                     int64_t n_local, int bs, int heads, int head_dim,
+                                     ulysses_dtype_t dtype, void* out, hipStream_t stream);
+
+/*
+ * Head-sharded -> sequence-sharded exchange, the inverse of
+ * ulysses_seq_to_head (Hugging Face Ulysses blog: the second all-to-all
+ * returns to sequence sharding).
+ *
+ *   in       device [P*n_local, bs, heads/P, head_dim]
+ *   chunks   host array of P device pointers to [n_local, bs, heads,
+ *            head_dim]; only head slots [rank*heads/P, (rank+1)*heads/P) of
+ *            every chunk are written, the other ranks' slots are untouched.
+ *   Requires heads % P == 0 (else ERR_DIVISIBILITY); other rules as above.
+ */
+ulysses_status_t ulysses_head_to_seq(const void* in, int P, int rank, int64_t n_local, int bs,
+                                     int heads, int head_dim, ulysses_dtype_t dtype,
+                                     void* const* chunks, hipStream_t stream);
+
+/*
+ * Local attention over the full sequence for this rank's heads (Hugging
+ * Face Ulysses blog: each GPU runs standard attention for its heads;
+ * integration guide: causality comes from positions, not from a 4D mask,
+ * and packed samples must not attend across document boundaries).
+ *
+ *   q, o     device [seqlen, bs, hq, head_dim]
+ *   k, v     device [seqlen, bs, hkv, head_dim]; query head h uses key/value
+ *            head floor(h / (hq/hkv)).  Requires hq % hkv == 0.
+ *   causal   1: key j is visible to query i iff j <= i (and same document);
+ *            0: every key of the query's document is visible.
+ *   cu_seqlens  NULL (one document) or a device int32 array of n_docs+1
+ *            offsets 0 = cu[0] < cu[1] < ... < cu[n_docs] = seqlen; requires
+ *            bs == 1.  The kernels clamp what they read from it, so bad
+ *            contents give wrong results but no out-of-bounds access.
+ *   lse      device fp32 [bs, hq, seqlen]: natural-log log-sum-exp of the
+ *            scaled scores of each query row.
+ *   s_i,j = softmax_scale * <q_i, k_j>;  O_i = sum_j softmax_j(s_i,.) v_j.
+ *   softmax_scale  must be positive and finite (ERR_SHAPE otherwise).
+ *   dtype    ULYSSES_BF16: head_dim 64 or 128, bf16 matrix cores with fp32
+ *            accumulation, O rounded to nearest even.  ULYSSES_FP32:
+ *            head_dim 32, 64 or 128, fp32 throughout.
+ *   seqlen == 0 is a no-op.  n_docs must lie in [1, seqlen] when cu_seqlens
+ *   is given.
+ */
+ulysses_status_t ulysses_attn_fwd(const void* q, const void* k, const void* v, int64_t seqlen,
+                                  int bs, int hq, int hkv, int head_dim, ulysses_dtype_t dtype,
+                                  float softmax_scale, int causal, const int32_t* cu_seqlens,
+                                  int n_docs, void* o, float* lse, hipStream_t stream);
+
+/* Bytes of device workspace ulysses_attn_bwd needs for these sizes. */
+size_t ulysses_attn_bwd_workspace_size(int64_t seqlen, int bs, int hq, int hkv, int head_dim,
+                                       ulysses_dtype_t dtype);
+
+/*
+ * Backward pass of ulysses_attn_fwd: given O and LSE from the forward call
+ * and the upstream gradient dO (same layout as O), computes
+ *   D_i = <dO_i, O_i>,  P_ij = exp(s_ij - LSE_i),  dS_ij = P_ij (<dO_i, v_j> - D_i)
+ *   dQ_i = scale * sum_j dS_ij k_j
+ *   dK_j = scale * sum_{h in group(j)} sum_i dS_ij q_i
+ *   dV_j = sum_{h in group(j)} sum_i P_ij dO_i
+ * recomputing P from Q, K and the saved LSE (no N x N storage).
+ * dq has q's layout, dk/dv have k's; all in `dtype`.  Other arguments as in
+ * ulysses_attn_fwd.  `workspace` is device memory of at least
+ * ulysses_attn_bwd_workspace_size(...) bytes, 256-byte aligned, whose
+ * contents on entry do not matter.  dq, dk, dv are fully overwritten.
+ */
+ulysses_status_t ulysses_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                                  const float* lse, const void* dout, int64_t seqlen, int bs,
+                                  int hq, int hkv, int head_dim, ulysses_dtype_t dtype,
+                                  float softmax_scale, int causal, const int32_t* cu_seqlens,
+                                  int n_docs, void* dq, void* dk, void* dv, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ULYSSES_H */

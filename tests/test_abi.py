@@ -1,0 +1,134 @@
+"""C-ABI tests that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments before any HIP call (so these
+calls are safe without a device: no kernel is ever launched here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from helpers import ROOT, ensure_library
+import ulysses_sp_attention_amd as uly
+
+HEADER = os.path.join(ROOT, "include", "ulysses.h")
+FAKE = 0x10000          # 16-byte aligned stand-in device address, never dereferenced
+MISALIGNED = 0x10008
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return ensure_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ulysses_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(uly.EXPORTED_SYMBOLS)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_abi_version_and_status_strings(lib):
+    assert uly.ulysses_abi_version() == 1
+    for code in range(9):
+        s = uly.ulysses_status_string(code)
+        assert s and s != "unknown status"
+    assert uly.ulysses_status_string(1234) == "unknown status"
+
+
+def chunk_array(ptrs):
+    arr = (ctypes.c_void_p * len(ptrs))()
+    for i, p in enumerate(ptrs):
+        arr[i] = p
+    return arr
+
+
+@pytest.mark.parametrize("args,want", [
+    # (chunks, P, rank, n_local, bs, heads, head_dim, dtype, out) -> status
+    ((None, 2, 0, 4, 1, 4, 64, uly.FP32, FAKE), uly.ERR_NULL),
+    (("ok", 2, 0, 4, 1, 4, 64, uly.FP32, None), uly.ERR_NULL),
+    (("ok", 2, 0, 4, 1, 4, 64, 7, FAKE), uly.ERR_DTYPE),
+    (("ok", 2, 2, 4, 1, 4, 64, uly.FP32, FAKE), uly.ERR_SHAPE),
+    (("ok", 2, -1, 4, 1, 4, 64, uly.FP32, FAKE), uly.ERR_SHAPE),
+    (("ok", 2, 0, -1, 1, 4, 64, uly.FP32, FAKE), uly.ERR_SHAPE),
+    (("ok", 2, 0, 4, 0, 4, 64, uly.FP32, FAKE), uly.ERR_SHAPE),
+    (("ok", 2, 0, 4, 1, 3, 64, uly.FP32, FAKE), uly.ERR_DIVISIBILITY),
+    (("ok8", 8, 0, 4, 1, 12, 128, uly.BF16, FAKE), uly.ERR_DIVISIBILITY),
+    (("ok8", 8, 0, 4, 1, 3, 128, uly.BF16, FAKE), uly.ERR_DIVISIBILITY),
+    (("ok", 2, 0, 4, 1, 4, 4, uly.BF16, FAKE), uly.ERR_ALIGNMENT),
+    (("ok", 2, 0, 4, 1, 4, 64, uly.FP32, MISALIGNED), uly.ERR_ALIGNMENT),
+    (("bad", 2, 0, 4, 1, 4, 64, uly.FP32, FAKE), uly.ERR_ALIGNMENT),
+    (("null", 2, 0, 4, 1, 4, 64, uly.FP32, FAKE), uly.ERR_NULL),
+    (("ok", 2, 0, 0, 1, 4, 64, uly.FP32, FAKE), uly.OK),   # empty exchange: no launch
+])
+def test_seq_to_head_validation(lib, args, want):
+    chunks, P, rank, n, bs, heads, hd, dt, out = args
+    table = {"ok": [FAKE, FAKE + 4096], "ok8": [FAKE + 4096 * i for i in range(8)],
+             "bad": [FAKE, MISALIGNED], "null": [FAKE, None]}
+    arr = None if chunks is None else chunk_array(table[chunks])
+    assert lib.ulysses_seq_to_head(arr, P, rank, n, bs, heads, hd, dt, out, None) == want
+
+
+def test_head_to_seq_requires_heads_divisible_by_P(lib):
+    arr = chunk_array([FAKE + 4096 * i for i in range(8)])
+    # replicated key/value heads (heads < P) cannot be scattered back by one rank
+    assert lib.ulysses_head_to_seq(FAKE, 8, 0, 4, 1, 2, 128, uly.BF16, arr, None) == uly.ERR_DIVISIBILITY
+    assert lib.ulysses_head_to_seq(None, 8, 0, 4, 1, 8, 128, uly.BF16, arr, None) == uly.ERR_NULL
+    assert lib.ulysses_head_to_seq(FAKE, 8, 0, 0, 1, 8, 128, uly.BF16, arr, None) == uly.OK
+
+
+def fwd(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, N=128, bs=1, hq=4, hkv=1, hd=128, dt=uly.BF16, scale=0.1,
+             causal=1, cu=None, n_docs=0, o=FAKE, lse=FAKE)
+    a.update(kw)
+    return lib.ulysses_attn_fwd(a["q"], a["k"], a["v"], a["N"], a["bs"], a["hq"], a["hkv"], a["hd"],
+                                a["dt"], a["scale"], a["causal"], a["cu"], a["n_docs"], a["o"],
+                                a["lse"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=None), uly.ERR_NULL), (dict(lse=None), uly.ERR_NULL),
+    (dict(dt=5), uly.ERR_DTYPE),
+    (dict(hd=96), uly.ERR_SHAPE), (dict(hd=256), uly.ERR_SHAPE),
+    (dict(dt=uly.FP32, hd=48), uly.ERR_SHAPE),
+    (dict(scale=0.0), uly.ERR_SHAPE), (dict(scale=-1.0), uly.ERR_SHAPE),
+    (dict(scale=float("inf")), uly.ERR_SHAPE), (dict(scale=float("nan")), uly.ERR_SHAPE),
+    (dict(N=-1), uly.ERR_SHAPE), (dict(bs=0), uly.ERR_SHAPE),
+    (dict(hq=6, hkv=4), uly.ERR_DIVISIBILITY),
+    (dict(cu=FAKE, n_docs=2, bs=2), uly.ERR_SHAPE),
+    (dict(cu=FAKE, n_docs=0), uly.ERR_SHAPE),
+    (dict(cu=FAKE, n_docs=129), uly.ERR_SHAPE),
+    (dict(cu=FAKE + 2, n_docs=2), uly.ERR_ALIGNMENT),
+    (dict(q=MISALIGNED), uly.ERR_ALIGNMENT), (dict(o=MISALIGNED), uly.ERR_ALIGNMENT),
+    (dict(lse=FAKE + 2), uly.ERR_ALIGNMENT),
+    (dict(N=0), uly.OK),
+])
+def test_attn_fwd_validation(lib, kw, want):
+    assert fwd(lib, **kw) == want
+
+
+def test_attn_bwd_workspace_rules(lib):
+    need = lib.ulysses_attn_bwd_workspace_size(1000, 2, 4, 1, 128, uly.BF16)
+    assert need >= 1000 * 2 * 4 * 4 and need % 256 == 0
+    assert lib.ulysses_attn_bwd_workspace_size(1000, 2, 4, 3, 128, uly.BF16) == 0   # invalid shape
+    common = (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1000, 2, 4, 1, 128, uly.BF16, 0.1, 1, None, 0,
+              FAKE, FAKE, FAKE)
+    assert lib.ulysses_attn_bwd(*common, None, need, None) == uly.ERR_WORKSPACE
+    assert lib.ulysses_attn_bwd(*common, FAKE, need - 1, None) == uly.ERR_WORKSPACE
+    bad = list(common)
+    bad[5] = None   # dout
+    assert lib.ulysses_attn_bwd(*bad, FAKE, need, None) == uly.ERR_NULL
+    bad = list(common)
+    bad[16] = MISALIGNED   # dq
+    assert lib.ulysses_attn_bwd(*bad, FAKE, need, None) == uly.ERR_ALIGNMENT
+
+
+def test_binding_raises_without_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(uly, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        uly.load_library(str(tmp_path / "missing.so"))

@@ -1,0 +1,165 @@
+"""Python binding of libulysses (one rank's share of an Ulysses attention layer
+on AMD Instinct MI355X).
+
+Thin ctypes marshalling over the C-ABI declared in ``include/ulysses.h``:
+each function below has the name of the C entry point it calls, takes torch
+device tensors, passes their data pointers, sizes and the current HIP stream,
+and raises :class:`UlyssesError` when the library returns a non-OK status.
+All computation happens in the library's HIP kernels; torch only supplies
+device memory and the stream.  The library must have been built
+(``ulysses_sp_attention_amd._build.build_lib()``); importing the binding
+without it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libulysses.so")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_DIVISIBILITY, ERR_DTYPE, ERR_ALIGNMENT, ERR_UNSUPPORTED, \
+    ERR_WORKSPACE, ERR_HIP = range(9)
+BF16, FP32 = 0, 1
+_INVALID_DTYPE = 99
+
+# Every symbol include/ulysses.h declares.
+EXPORTED_SYMBOLS = (
+    "ulysses_abi_version", "ulysses_status_string", "ulysses_seq_to_head", "ulysses_head_to_seq",
+    "ulysses_attn_fwd", "ulysses_attn_bwd_workspace_size", "ulysses_attn_bwd",
+)
+
+
+class UlyssesError(RuntimeError):
+    def __init__(self, func: str, status: int, message: str):
+        super().__init__(f"{func}: {message} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libulysses.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    # torch ships its own HIP runtime (soname libamdhip64.so.7) and loads it
+    # by an unversioned name.  Importing torch first makes the library's
+    # dependency resolve to that same runtime, so tensors, streams and
+    # kernels live in one HIP instance; loading libulysses first would bring
+    # in a second runtime beside torch's.
+    import torch  # noqa: F401
+    if not os.path.exists(path):
+        raise RuntimeError(f"libulysses is not built ({path} missing); run "
+                           "ulysses_sp_attention_amd._build.build_lib()")
+    lib = ctypes.CDLL(path)
+    vp, ci, i64, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    lib.ulysses_abi_version.argtypes = []
+    lib.ulysses_abi_version.restype = ci
+    lib.ulysses_status_string.argtypes = [ci]
+    lib.ulysses_status_string.restype = ctypes.c_char_p
+    lib.ulysses_seq_to_head.argtypes = [vp, ci, ci, i64, ci, ci, ci, ci, vp, vp]
+    lib.ulysses_seq_to_head.restype = ci
+    lib.ulysses_head_to_seq.argtypes = [vp, ci, ci, i64, ci, ci, ci, ci, vp, vp]
+    lib.ulysses_head_to_seq.restype = ci
+    lib.ulysses_attn_fwd.argtypes = [vp, vp, vp, i64, ci, ci, ci, ci, ci, f32, ci, vp, ci, vp, vp, vp]
+    lib.ulysses_attn_fwd.restype = ci
+    lib.ulysses_attn_bwd_workspace_size.argtypes = [i64, ci, ci, ci, ci, ci]
+    lib.ulysses_attn_bwd_workspace_size.restype = sz
+    lib.ulysses_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, ci, ci, ci, ci, ci, f32, ci, vp, ci,
+                                     vp, vp, vp, vp, sz, vp]
+    lib.ulysses_attn_bwd.restype = ci
+    _lib = lib
+    return lib
+
+
+def _check(func: str, status: int) -> None:
+    if status != OK:
+        raise UlyssesError(func, status, ulysses_status_string(status))
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return FP32
+    return _INVALID_DTYPE   # the library reports ERR_DTYPE
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr_array(tensors):
+    arr = (ctypes.c_void_p * len(tensors))()
+    for i, t in enumerate(tensors):
+        arr[i] = t.data_ptr()
+    return arr
+
+
+def ulysses_abi_version() -> int:
+    return int(load_library().ulysses_abi_version())
+
+
+def ulysses_status_string(status: int) -> str:
+    return load_library().ulysses_status_string(status).decode()
+
+
+def ulysses_seq_to_head(chunks, rank: int, out, stream=None) -> None:
+    """chunks: P tensors [n_local, bs, heads, head_dim]; out: [P*n_local, bs, heads_l, head_dim]."""
+    n, bs, heads, hd = chunks[0].shape
+    st = load_library().ulysses_seq_to_head(
+        _ptr_array(chunks), len(chunks), rank, n, bs, heads, hd, _dtype_code(chunks[0]), _ptr(out),
+        _stream(stream))
+    _check("ulysses_seq_to_head", st)
+
+
+def ulysses_head_to_seq(inp, rank: int, chunks, stream=None) -> None:
+    """inp: [P*n_local, bs, heads/P, head_dim]; writes rank's head slots of the P chunks."""
+    n, bs, heads, hd = chunks[0].shape
+    st = load_library().ulysses_head_to_seq(
+        _ptr(inp), len(chunks), rank, n, bs, heads, hd, _dtype_code(inp), _ptr_array(chunks),
+        _stream(stream))
+    _check("ulysses_head_to_seq", st)
+
+
+def ulysses_attn_fwd(q, k, v, o, lse, softmax_scale: float, causal: bool = True,
+                     cu_seqlens=None, stream=None) -> None:
+    """q, o: [N, bs, hq, hd]; k, v: [N, bs, hkv, hd]; lse: fp32 [bs, hq, N];
+    cu_seqlens: optional device int32 [n_docs + 1]."""
+    N, bs, hq, hd = q.shape
+    hkv = k.shape[2]
+    n_docs = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
+    st = load_library().ulysses_attn_fwd(
+        _ptr(q), _ptr(k), _ptr(v), N, bs, hq, hkv, hd, _dtype_code(q), softmax_scale, int(causal),
+        _ptr(cu_seqlens), n_docs, _ptr(o), _ptr(lse), _stream(stream))
+    _check("ulysses_attn_fwd", st)
+
+
+def ulysses_attn_bwd_workspace_size(seqlen: int, bs: int, hq: int, hkv: int, head_dim: int,
+                                    dtype: int) -> int:
+    return int(load_library().ulysses_attn_bwd_workspace_size(seqlen, bs, hq, hkv, head_dim, dtype))
+
+
+def ulysses_attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, softmax_scale: float,
+                     causal: bool = True, cu_seqlens=None, stream=None) -> None:
+    """Gradients of ulysses_attn_fwd.  workspace: device tensor of at least
+    ulysses_attn_bwd_workspace_size(...) bytes."""
+    N, bs, hq, hd = q.shape
+    hkv = k.shape[2]
+    n_docs = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load_library().ulysses_attn_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), N, bs, hq, hkv, hd,
+        _dtype_code(q), softmax_scale, int(causal), _ptr(cu_seqlens), n_docs, _ptr(dq), _ptr(dk),
+        _ptr(dv), _ptr(workspace), ws_bytes, _stream(stream))
+    _check("ulysses_attn_bwd", st)

@@ -1,0 +1,193 @@
+// C-ABI of libulysses: argument validation and dispatch to the kernels.
+// Every check runs before the first HIP call, so a rejected call launches
+// nothing and leaves every output untouched.  Contracts are stated in
+// include/ulysses.h.
+#include "ulysses.h"
+
+#include <math.h>
+#include <stdint.h>
+
+#include "launch.h"
+
+namespace {
+
+using ulysses::AttnShape;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+int elem_size(ulysses_dtype_t dt) {
+  switch (dt) {
+    case ULYSSES_BF16: return 2;
+    case ULYSSES_FP32: return 4;
+    default: return 0;
+  }
+}
+
+ulysses_status_t from_hip(hipError_t e) { return e == hipSuccess ? ULYSSES_OK : ULYSSES_ERR_HIP; }
+
+// Shared checks of the exchange calls; fills the launch geometry.
+ulysses_status_t check_exchange(const void* const* chunks, int P, int rank, int64_t n_local, int bs,
+                                int heads, int head_dim, ulysses_dtype_t dtype, const void* headbuf,
+                                bool to_head, ulysses::ChunkTable* table, int64_t* chunk_row_bytes,
+                                int64_t* slot_bytes, int64_t* head_row_bytes) {
+  if (chunks == nullptr) return ULYSSES_ERR_NULL;
+  const int es = elem_size(dtype);
+  if (es == 0) return ULYSSES_ERR_DTYPE;
+  if (P < 1 || P > ulysses::kMaxChunks || rank < 0 || rank >= P || n_local < 0 || bs < 1 ||
+      heads < 1 || head_dim < 1)
+    return ULYSSES_ERR_SHAPE;
+  if (to_head ? (heads >= P ? heads % P != 0 : P % heads != 0) : heads % P != 0)
+    return ULYSSES_ERR_DIVISIBILITY;
+  if (n_local == 0) return ULYSSES_OK;   // nothing is read or written
+  if (headbuf == nullptr) return ULYSSES_ERR_NULL;
+  for (int c = 0; c < P; ++c)
+    if (chunks[c] == nullptr) return ULYSSES_ERR_NULL;
+  if (((int64_t)head_dim * es) % 16 != 0 || !aligned16(headbuf)) return ULYSSES_ERR_ALIGNMENT;
+  for (int c = 0; c < P; ++c)
+    if (!aligned16(chunks[c])) return ULYSSES_ERR_ALIGNMENT;
+  const int hl = heads >= P ? heads / P : 1;
+  const int src0 = heads >= P ? rank * hl : (int)(((int64_t)rank * heads) / P);
+  const int64_t row = (int64_t)head_dim * es;
+  *chunk_row_bytes = (int64_t)heads * row;
+  *slot_bytes = (int64_t)src0 * row;
+  *head_row_bytes = (int64_t)hl * row;
+  if ((uint64_t)n_local * (uint64_t)bs * (uint64_t)(*head_row_bytes / 16) >= (1ull << 32))
+    return ULYSSES_ERR_UNSUPPORTED;
+  for (int c = 0; c < P; ++c) table->ptr[c] = reinterpret_cast<uintptr_t>(chunks[c]);
+  return ULYSSES_OK;
+}
+
+// Shared checks of the attention calls.
+ulysses_status_t check_attn(int64_t seqlen, int bs, int hq, int hkv, int head_dim,
+                            ulysses_dtype_t dtype, float scale, int causal, const int32_t* cu,
+                            int n_docs, AttnShape* s) {
+  if (elem_size(dtype) == 0) return ULYSSES_ERR_DTYPE;
+  if (seqlen < 0 || bs < 1 || hq < 1 || hkv < 1) return ULYSSES_ERR_SHAPE;
+  if (dtype == ULYSSES_BF16 ? (head_dim != 64 && head_dim != 128)
+                            : (head_dim != 32 && head_dim != 64 && head_dim != 128))
+    return ULYSSES_ERR_SHAPE;
+  if (!(scale > 0.f) || !isfinite(scale)) return ULYSSES_ERR_SHAPE;
+  if (hq % hkv != 0) return ULYSSES_ERR_DIVISIBILITY;
+  if (cu != nullptr) {
+    if (bs != 1 || n_docs < 1 || n_docs > seqlen) return ULYSSES_ERR_SHAPE;
+    if (!aligned4(cu)) return ULYSSES_ERR_ALIGNMENT;
+  }
+  if ((int64_t)bs * hq > 65535) return ULYSSES_ERR_UNSUPPORTED;   // grid.y of the launches
+  s->N = seqlen;
+  s->bs = bs;
+  s->hq = hq;
+  s->hkv = hkv;
+  s->hd = head_dim;
+  s->scale = scale;
+  s->causal = causal ? 1 : 0;
+  s->cu = cu;
+  s->n_docs = cu ? n_docs : 0;
+  return ULYSSES_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ulysses_abi_version(void) { return ULYSSES_ABI_VERSION; }
+
+const char* ulysses_status_string(ulysses_status_t status) {
+  switch (status) {
+    case ULYSSES_OK: return "ok";
+    case ULYSSES_ERR_NULL: return "required pointer is NULL";
+    case ULYSSES_ERR_SHAPE: return "invalid or unsupported size";
+    case ULYSSES_ERR_DIVISIBILITY: return "head counts not divisible as required";
+    case ULYSSES_ERR_DTYPE: return "unknown element type";
+    case ULYSSES_ERR_ALIGNMENT: return "pointer or row not 16-byte aligned";
+    case ULYSSES_ERR_UNSUPPORTED: return "request not supported by this build";
+    case ULYSSES_ERR_WORKSPACE: return "workspace missing or too small";
+    case ULYSSES_ERR_HIP: return "HIP kernel launch failed";
+  }
+  return "unknown status";
+}
+
+ulysses_status_t ulysses_seq_to_head(const void* const* chunks, int P, int rank, int64_t n_local,
+                                     int bs, int heads, int head_dim, ulysses_dtype_t dtype,
+                                     void* out, hipStream_t stream) {
+  ulysses::ChunkTable table{};
+  int64_t crb, slot, hrb;
+  ulysses_status_t st = check_exchange(chunks, P, rank, n_local, bs, heads, head_dim, dtype, out,
+                                       true, &table, &crb, &slot, &hrb);
+  if (st != ULYSSES_OK) return st;
+  if (n_local == 0) return ULYSSES_OK;
+  return from_hip(ulysses::launch_exchange(true, table, P, static_cast<char*>(out),
+                                           n_local * bs, crb, slot, hrb, stream));
+}
+
+ulysses_status_t ulysses_head_to_seq(const void* in, int P, int rank, int64_t n_local, int bs,
+                                     int heads, int head_dim, ulysses_dtype_t dtype,
+                                     void* const* chunks, hipStream_t stream) {
+  ulysses::ChunkTable table{};
+  int64_t crb, slot, hrb;
+  ulysses_status_t st = check_exchange(chunks, P, rank, n_local, bs, heads, head_dim, dtype, in,
+                                       false, &table, &crb, &slot, &hrb);
+  if (st != ULYSSES_OK) return st;
+  if (n_local == 0) return ULYSSES_OK;
+  return from_hip(ulysses::launch_exchange(false, table, P, const_cast<char*>(static_cast<const char*>(in)),
+                                           n_local * bs, crb, slot, hrb, stream));
+}
+
+ulysses_status_t ulysses_attn_fwd(const void* q, const void* k, const void* v, int64_t seqlen,
+                                  int bs, int hq, int hkv, int head_dim, ulysses_dtype_t dtype,
+                                  float softmax_scale, int causal, const int32_t* cu_seqlens,
+                                  int n_docs, void* o, float* lse, hipStream_t stream) {
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || lse == nullptr)
+    return ULYSSES_ERR_NULL;
+  AttnShape s;
+  ulysses_status_t st = check_attn(seqlen, bs, hq, hkv, head_dim, dtype, softmax_scale, causal,
+                                   cu_seqlens, n_docs, &s);
+  if (st != ULYSSES_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned4(lse))
+    return ULYSSES_ERR_ALIGNMENT;
+  if (seqlen == 0) return ULYSSES_OK;
+  if (dtype == ULYSSES_BF16) return from_hip(ulysses::launch_attn_fwd_bf16(s, q, k, v, o, lse, stream));
+  return from_hip(ulysses::launch_attn_fwd_f32(s, static_cast<const float*>(q),
+                                               static_cast<const float*>(k),
+                                               static_cast<const float*>(v), static_cast<float*>(o),
+                                               lse, stream));
+}
+
+size_t ulysses_attn_bwd_workspace_size(int64_t seqlen, int bs, int hq, int hkv, int head_dim,
+                                       ulysses_dtype_t dtype) {
+  AttnShape s;
+  if (check_attn(seqlen, bs, hq, hkv, head_dim, dtype, 1.0f, 1, nullptr, 0, &s) != ULYSSES_OK)
+    return 0;
+  return ulysses::attn_bwd_workspace_bytes(s, dtype == ULYSSES_BF16);
+}
+
+ulysses_status_t ulysses_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                                  const float* lse, const void* dout, int64_t seqlen, int bs,
+                                  int hq, int hkv, int head_dim, ulysses_dtype_t dtype,
+                                  float softmax_scale, int causal, const int32_t* cu_seqlens,
+                                  int n_docs, void* dq, void* dk, void* dv, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || lse == nullptr ||
+      dout == nullptr || dq == nullptr || dk == nullptr || dv == nullptr)
+    return ULYSSES_ERR_NULL;
+  AttnShape s;
+  ulysses_status_t st = check_attn(seqlen, bs, hq, hkv, head_dim, dtype, softmax_scale, causal,
+                                   cu_seqlens, n_docs, &s);
+  if (st != ULYSSES_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned4(lse))
+    return ULYSSES_ERR_ALIGNMENT;
+  const size_t need = ulysses::attn_bwd_workspace_bytes(s, dtype == ULYSSES_BF16);
+  if (seqlen > 0 && (workspace == nullptr || workspace_bytes < need)) return ULYSSES_ERR_WORKSPACE;
+  if (seqlen > 0 && !aligned16(workspace)) return ULYSSES_ERR_ALIGNMENT;
+  if (seqlen == 0) return ULYSSES_OK;
+  if (dtype == ULYSSES_BF16)
+    return from_hip(ulysses::launch_attn_bwd_bf16(s, q, k, v, o, lse, dout, dq, dk, dv, workspace,
+                                                  stream));
+  return from_hip(ulysses::launch_attn_bwd_f32(
+      s, static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
+      static_cast<const float*>(o), lse, static_cast<const float*>(dout), static_cast<float*>(dq),
+      static_cast<float*>(dk), static_cast<float*>(dv), workspace, stream));
+}
+
+}  // extern "C"

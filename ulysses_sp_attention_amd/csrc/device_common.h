@@ -1,0 +1,102 @@
+// Device-side helpers shared by the gfx950 kernels of libulysses.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <tuple>
+#include <utility>
+
+namespace ulysses {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
+
+#define ULY_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// D(32x32) += A(32x16) * B(16x32), bf16 in, fp32 accumulate.
+// Lane layout (measured on gfx950): A lane l holds row l%32, B lane l holds
+// column l%32, each with 8 k-values; lanes l and l+32 carry the two k-halves
+// (any k order works as long as A and B agree).  Accumulator element i of
+// lane l is D[8*(i/4) + 4*(l/32) + i%4][l%32].
+__device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Transposing LDS read of four 16-bit values (ds_read_b64_tr_b16).  Within
+// each group of 16 lanes, lane u supplies the address of 4 consecutive
+// values (a row fragment); lane l of the group receives value (l % 4) of the
+// fragments loaded by lanes 4*j + l/4, for j = 0..3.
+__device__ __forceinline__ bf16x4_t lds_read_tr16(const void* p) {
+  i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ULY_LDS i16x4_t*)(p));
+  return __builtin_bit_cast(bf16x4_t, v);
+}
+
+__device__ __forceinline__ float wave_shfl_xor32(float x) {
+  // lanes l and l^32 exchange values
+  return __shfl_xor(x, 32, 64);
+}
+
+__device__ __forceinline__ bool wave_any(bool pred) {
+  return __any(pred);
+}
+
+// Start offset of the document holding position i: the largest cu[d] <= i
+// over d in [0, n_docs).  Values read from cu are clamped to [0, i].
+__device__ __forceinline__ int64_t doc_start_of(const int32_t* cu, int n_docs, int64_t i) {
+  if (cu == nullptr) return 0;
+  int lo = 0, hi = n_docs - 1;  // invariant: answer index in [lo, hi]
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if ((int64_t)cu[mid] <= i) lo = mid; else hi = mid - 1;
+  }
+  int64_t s = cu[lo];
+  if (s < 0) s = 0;
+  if (s > i) s = i;
+  return s;
+}
+
+// End offset (exclusive) of the document holding position i, clamped to
+// [i + 1, N].
+__device__ __forceinline__ int64_t doc_end_of(const int32_t* cu, int n_docs, int64_t i, int64_t N) {
+  if (cu == nullptr) return N;
+  int lo = 0, hi = n_docs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if ((int64_t)cu[mid] <= i) lo = mid; else hi = mid - 1;
+  }
+  int64_t e = cu[lo + 1];
+  if (e > N) e = N;
+  if (e < i + 1) e = i + 1;
+  return e;
+}
+
+template <typename Tuple, size_t... I>
+inline void fill_argv(Tuple& t, void** argv, std::index_sequence<I...>) {
+  ((argv[I] = static_cast<void*>(&std::get<I>(t))), ...);
+}
+
+// Launches `kernel` on `stream` and returns the launch status itself (not the
+// thread's sticky last-error state, which other HIP users may have left set).
+template <typename... KArgs, typename... Args>
+inline hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t shmem,
+                                hipStream_t stream, Args... args) {
+  static_assert(sizeof...(KArgs) == sizeof...(Args), "kernel argument count");
+  struct Pack {
+    std::tuple<KArgs...> v;
+  } pack{std::tuple<KArgs...>(args...)};
+  void* argv[sizeof...(KArgs) + 1];
+  fill_argv(pack.v, argv, std::index_sequence_for<KArgs...>{});
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv, shmem, stream);
+}
+
+}  // namespace ulysses
