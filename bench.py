@@ -31,6 +31,31 @@ MFMA_BF16_PEAK_TFLOPS = 2516.6   # MI355X dense bf16 matrix-core peak
 HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E peak
 WORKLOAD = "llama8b-share-128k"
 
+# Memory-side bytes per call of each attention entry point at this workload,
+# from rocprofv3 FETCH_SIZE and WRITE_SIZE (one counter per run), scaled by
+# what the same counters read for a plain 512 MiB device copy (FETCH x2.0,
+# WRITE x1.0); the table is in profiles/attn_step_llama8b-share-128k_hbm_traffic.md.
+# A figure is only reported while the kernel sources hash to what was
+# measured; after any change to them the roofline's traffic is null.
+MEASURED_TRAFFIC = {
+    "attn_bwd": {"bytes": 1.10929e11, "sources": ("attn_bwd.hip", "attn_f32.hip", "device_common.h"),
+                 "sha256_16": "cadde7633c30c211"},
+    "attn_fwd": {"bytes": 9.14025e9, "sources": ("attn_fwd.hip", "device_common.h"),
+                 "sha256_16": "f0162f41a3b8b7b0"},
+}
+
+
+def traffic_if_current(unit):
+    import hashlib
+    rec = MEASURED_TRAFFIC.get(unit)
+    if rec is None:
+        return None
+    h = hashlib.sha256()
+    for f in rec["sources"]:
+        with open(os.path.join(ROOT, "ulysses_sp_attention_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return rec["bytes"] if h.hexdigest()[:16] == rec["sha256_16"] else None
+
 
 def parse_args():
     ap = argparse.ArgumentParser()
@@ -40,6 +65,9 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=768,
                     help="query rows of the oracle's timed sample")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="before timing, run one plain device-to-device copy of MIB MiB "
+                         "(a known-size reference for hardware byte counters)")
     return ap.parse_args()
 
 
@@ -131,6 +159,15 @@ def main():
         uly.ulysses_head_to_seq(dv, r, cdv)
         mark(6)
 
+    if args.calibrate_copy:
+        nbytes = args.calibrate_copy << 20
+        src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -182,19 +219,29 @@ def main():
     breakdown["pack_all"] = {"ms": pack_ms, "GB/s": gbps(pack_bytes, pack_ms),
                              "frac_of_hbm_peak": gbps(pack_bytes, pack_ms) / HBM_PEAK_GBPS}
 
-    # Roofline of the dominant single-launch kernel: the attention forward
-    # (one launch per ulysses_attn_fwd call), timed with events on its stream.
-    dominant = max(("attn_fwd", "attn_bwd"), key=lambda k_: avg[k_])
+    # Roofline of the dominant unit of the step, timed with events on the
+    # stream its kernels run on.  The attention backward is one entry point
+    # (ulysses_attn_bwd) that enqueues three kernels back to back: the D
+    # row-dot, the dQ kernel and the dK/dV kernel; its algorithmic work is the
+    # five products of the backward (10 * hd flop per visible pair and head).
+    # The forward is one kernel (2 products, 4 * hd flop per pair and head).
+    units = {"attn_fwd": (fwd_flop, ["attn_fwd_bf16_kernel"]),
+             "attn_bwd": (bwd_flop, ["row_dot_kernel", "attn_bwd_dq_kernel", "attn_bwd_dkv_kernel"])}
+    dominant = max(units, key=lambda k_: avg[k_])
+    flop, kernels = units[dominant]
+    achieved = tflops(flop, avg[dominant])
     roofline = {
-        "kernel": "attn_fwd_bf16_kernel",
+        "kernel": dominant,
+        "launches": kernels,
         "bound": "mfma",
-        "achieved": fwd_tf,
+        "achieved": achieved,
         "peak": MFMA_BF16_PEAK_TFLOPS,
         "unit": "TFLOP/s",
-        "frac": fwd_tf / MFMA_BF16_PEAK_TFLOPS,
-        "traffic": None,
-        "per_launch_flop": fwd_flop,
-        "note": f"largest entry point by time: {dominant}",
+        "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
+        "traffic": traffic_if_current(dominant),
+        "traffic_unit": "bytes per call (memory side of L2)",
+        "per_launch_flop": flop,
+        "avg_ms": avg[dominant],
     }
 
     cpu = None

@@ -51,7 +51,7 @@ def _load():
     lib.oracle_attn_fwd.argtypes = [vp, vp, vp, i64, ci, ci, ci, ci, dbl, ci, vp, ci, vp, i64, vp, vp, vp]
     lib.oracle_attn_fwd.restype = ci
     lib.oracle_attn_bwd.argtypes = [vp, vp, vp, vp, i64, ci, ci, ci, ci, dbl, ci, vp, ci,
-                                    vp, i64, vp, i64, vp, vp, vp, vp, vp, vp]
+                                    vp, i64, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.oracle_attn_bwd.restype = ci
     _lib = lib
     return lib
@@ -131,11 +131,18 @@ def attn_fwd(q, k, v, scale: float, causal: bool = True, cu_seqlens=None, rows=N
 
 
 def attn_bwd(q, k, v, dout, scale: float, causal: bool = True, cu_seqlens=None,
-             dq_rows=None, dkv_cols=None, magnitude: bool = False):
-    """Returns (dQ, dK, dV), compact over the selected rows / columns.  With
-    magnitude=True returns (dQ, dK, dV, (M_dQ, M_dK, M_dV)): each output sum
-    re-evaluated with every term replaced by its absolute value."""
+             dq_rows=None, dkv_cols=None, magnitude: bool = False, o=None, lse=None):
+    """Returns (dQ, dK, dV), compact over the selected rows / columns.
+
+    o, lse: optional forward outputs to use in place of the oracle's own (full
+    [N, bs, hq, hd] and [bs, hq, N]), as a backward call receives them.
+    With magnitude=True returns (dQ, dK, dV, mags) where mags is a dict:
+    "dq", "dk", "dv" -- each output sum re-evaluated with every term replaced
+    by its absolute value; "dq_from_D", "dk_from_D" -- the sensitivity of dQ
+    and dK to the magnitude of D (see oracle.c)."""
     q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    o_in = None if o is None else _f64(o)
+    lse_in = None if lse is None else _f64(lse)
     N, bs, hq, hd = q.shape
     hkv = k.shape[2]
     cu = _cu64(cu_seqlens)
@@ -146,7 +153,8 @@ def attn_bwd(q, k, v, dout, scale: float, causal: bool = True, cu_seqlens=None,
     dq = np.empty((nq, bs, hq, hd))
     dk = np.empty((nk, bs, hkv, hd))
     dv = np.empty((nk, bs, hkv, hd))
-    mags = (np.empty_like(dq), np.empty_like(dk), np.empty_like(dv)) if magnitude else (None,) * 3
+    mags = ((np.empty_like(dq), np.empty_like(dk), np.empty_like(dv), np.empty_like(dq),
+             np.empty_like(dk)) if magnitude else (None,) * 5)
     # a zero-length selection still needs a valid (non-NULL) pointer
     dummy = np.zeros(1, np.int64)
     qr_p = None if qr is None else (qr if nq else dummy).ctypes.data
@@ -155,8 +163,11 @@ def attn_bwd(q, k, v, dout, scale: float, causal: bool = True, cu_seqlens=None,
         q.ctypes.data, k.ctypes.data, v.ctypes.data, dout.ctypes.data, N, bs, hq, hkv, hd,
         float(scale), int(causal), None if cu is None else cu.ctypes.data,
         0 if cu is None else len(cu) - 1, qr_p, nq, kc_p, nk,
+        None if o_in is None else o_in.ctypes.data, None if lse_in is None else lse_in.ctypes.data,
         dq.ctypes.data, dk.ctypes.data, dv.ctypes.data,
         *[None if m is None else m.ctypes.data for m in mags])
     if rc:
         raise ValueError("oracle_attn_bwd: bad arguments")
-    return (dq, dk, dv, mags) if magnitude else (dq, dk, dv)
+    if not magnitude:
+        return dq, dk, dv
+    return dq, dk, dv, dict(zip(("dq", "dk", "dv", "dq_from_D", "dk_from_D"), mags))

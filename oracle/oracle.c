@@ -263,16 +263,26 @@ int oracle_attn_fwd(const double* q, const double* k, const double* v, int64_t N
  * dq_rows: NULL for all positions, else the positions whose dQ is wanted
  * (dq is compact [t, bs, hq, hd]).  dkv_cols likewise for dK/dV
  * (compact [t, bs, hkv, hd]).  Pass n = 0 with a non-NULL pointer to skip.
+ * o_in, lse_in (optional): the forward's O ([N, bs, hq, hd]) and LSE
+ * ([bs, hq, N]) to use in place of this file's own values, as the backward
+ * receives them from a forward call: D_i = <dO_i, o_in_i> and
+ * P_ij = exp(s_ij - lse_in_i).
  * dq_mag, dk_mag, dv_mag (optional, NULL to skip; layouts as dq, dk, dv)
  * receive the magnitude of each output sum -- the same sum with every term
  * replaced by its absolute value:
  *   scale sum_j |dS_ij| |k_j|,  scale sum_h sum_i |dS_ij| |q_i|,  sum_h sum_i P_ij |dO_i|.
+ * dq_dmag, dk_dmag (optional) receive how strongly dQ and dK depend on D:
+ *   scale A_i sum_j P_ij |k_j|  and  scale sum_h sum_i P_ij A_i |q_i|,
+ * with A_i = sum_e |dO_ie| sum_j P_ij |v_je| the magnitude of D_i's sum; an
+ * error dD_i in D (e.g. from O rounded to a short format) moves dQ_i and
+ * dK_j by at most these times |dD_i| / A_i.
  */
 int oracle_attn_bwd(const double* q, const double* k, const double* v, const double* dout,
                     int64_t N, int bs, int hq, int hkv, int hd, double scale, int causal,
                     const int64_t* cu, int ndocs, const int64_t* dq_rows, int64_t n_dq,
-                    const int64_t* dkv_cols, int64_t n_dkv, double* dq, double* dk, double* dv,
-                    double* dq_mag, double* dk_mag, double* dv_mag) {
+                    const int64_t* dkv_cols, int64_t n_dkv, const double* o_in,
+                    const double* lse_in, double* dq, double* dk, double* dv, double* dq_mag,
+                    double* dk_mag, double* dv_mag, double* dq_dmag, double* dk_dmag) {
   if (N <= 0 || bs <= 0 || hq <= 0 || hkv <= 0 || hd <= 0 || hq % hkv) return -1;
   if (check_docs(cu, ndocs, N)) return -1;
   const attn_t a = {q, k, v, N, bs, hq, hkv, hd, scale, causal, cu, ndocs};
@@ -295,11 +305,14 @@ int oracle_attn_bwd(const double* q, const double* k, const double* v, const dou
   }
   double* LSE = (double*)malloc(sizeof(double) * (size_t)N * bs * hq);
   double* D = (double*)malloc(sizeof(double) * (size_t)N * bs * hq);
+  double* A = (double*)malloc(sizeof(double) * (size_t)N * bs * hq);
+  const int want_dmag = dq_dmag != NULL || dk_dmag != NULL;
   const int64_t total = N * bs * hq;
 #pragma omp parallel
   {
     double* s = (double*)malloc(sizeof(double) * (size_t)N);
     double* o = (double*)malloc(sizeof(double) * (size_t)hd);
+    double* om = (double*)malloc(sizeof(double) * (size_t)hd);
 #pragma omp for schedule(dynamic, 16)
     for (int64_t w = 0; w < total; ++w) {
       const int64_t i = w / (bs * hq);
@@ -307,13 +320,21 @@ int oracle_attn_bwd(const double* q, const double* k, const double* v, const dou
       const int b = (int)((w / hq) % bs);
       const int h = (int)(w % hq);
       const size_t idx = ((size_t)b * hq + h) * N + i;
-      LSE[idx] = row_forward(&a, i, b, h, s, o, NULL);
-      double d = 0.0;
-      for (int e = 0; e < hd; ++e) d += qv(&a, dout, hq, i, b, h, e) * o[e];
+      const int fwd = !(o_in && lse_in) || want_dmag;
+      const double lse = fwd ? row_forward(&a, i, b, h, s, o, om) : 0.0;
+      LSE[idx] = lse_in ? lse_in[idx] : lse;
+      double d = 0.0, mag = 0.0;
+      for (int e = 0; e < hd; ++e) {
+        const double oe = o_in ? qv(&a, o_in, hq, i, b, h, e) : o[e];
+        d += qv(&a, dout, hq, i, b, h, e) * oe;
+        if (fwd) mag += fabs(qv(&a, dout, hq, i, b, h, e)) * om[e];
+      }
       D[idx] = d;
+      A[idx] = mag;
     }
     free(s);
     free(o);
+    free(om);
   }
 
   /* dQ rows. */
@@ -328,9 +349,12 @@ int oracle_attn_bwd(const double* q, const double* k, const double* v, const dou
     const size_t idx = ((size_t)b * hq + h) * N + i;
     double* out = dq + (((size_t)t * bs + b) * hq + h) * hd;
     double* mag = dq_mag ? dq_mag + (((size_t)t * bs + b) * hq + h) * hd : NULL;
+    double* dmag = dq_dmag ? dq_dmag + (((size_t)t * bs + b) * hq + h) * hd : NULL;
     for (int e = 0; e < hd; ++e) out[e] = 0.0;
     if (mag)
       for (int e = 0; e < hd; ++e) mag[e] = 0.0;
+    if (dmag)
+      for (int e = 0; e < hd; ++e) dmag[e] = 0.0;
     int64_t lo, hi;
     key_range(&a, i, &lo, &hi);
     for (int64_t j = lo; j < hi; ++j) {
@@ -341,11 +365,14 @@ int oracle_attn_bwd(const double* q, const double* k, const double* v, const dou
       for (int e = 0; e < hd; ++e) {
         out[e] += ds * qv(&a, k, hkv, j, b, kh, e);
         if (mag) mag[e] += fabs(ds) * fabs(qv(&a, k, hkv, j, b, kh, e));
+        if (dmag) dmag[e] += p * A[idx] * fabs(qv(&a, k, hkv, j, b, kh, e));
       }
     }
     for (int e = 0; e < hd; ++e) out[e] *= scale;
     if (mag)
       for (int e = 0; e < hd; ++e) mag[e] *= scale;
+    if (dmag)
+      for (int e = 0; e < hd; ++e) dmag[e] *= scale;
   }
 
   /* dK, dV columns. */
@@ -361,7 +388,10 @@ int oracle_attn_bwd(const double* q, const double* k, const double* v, const dou
     double* ovv = dv + off;
     double* mk = dk_mag ? dk_mag + off : NULL;
     double* mv = dv_mag ? dv_mag + off : NULL;
+    double* dmk = dk_dmag ? dk_dmag + off : NULL;
     for (int e = 0; e < hd; ++e) okk[e] = ovv[e] = 0.0;
+    if (dmk)
+      for (int e = 0; e < hd; ++e) dmk[e] = 0.0;
     if (mk)
       for (int e = 0; e < hd; ++e) mk[e] = 0.0;
     if (mv)
@@ -380,14 +410,18 @@ int oracle_attn_bwd(const double* q, const double* k, const double* v, const dou
           ovv[e] += p * qv(&a, dout, hq, i, b, h, e);
           if (mk) mk[e] += fabs(ds) * fabs(qv(&a, q, hq, i, b, h, e));
           if (mv) mv[e] += p * fabs(qv(&a, dout, hq, i, b, h, e));
+          if (dmk) dmk[e] += p * A[idx] * fabs(qv(&a, q, hq, i, b, h, e));
         }
       }
     for (int e = 0; e < hd; ++e) okk[e] *= scale;
     if (mk)
       for (int e = 0; e < hd; ++e) mk[e] *= scale;
+    if (dmk)
+      for (int e = 0; e < hd; ++e) dmk[e] *= scale;
   }
   free(need);
   free(LSE);
   free(D);
+  free(A);
   return 0;
 }

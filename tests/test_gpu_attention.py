@@ -72,6 +72,33 @@ SMALL = [
 ]
 
 
+def bf16_round(x):
+    import torch
+    return torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16).double().numpy()
+
+
+def to_device_f(x, dtype):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+    return t.to(torch.bfloat16) if dtype == "bf16" else t
+
+
+def check_end_to_end(dtype, got, ref, rows=None, cols=None):
+    """GPU forward then backward against the exact gradient.  Besides its own
+    roundings, the backward sees O rounded to the storage format, so D_i is
+    off by up to 2u sum_e |dO_ie| (P|V|)_ie; the oracle's dq_from_D/dk_from_D
+    carry that through to dQ and dK."""
+    dq, dk, dv = (to_f64(t) for t in got)
+    if rows is not None:
+        dq = dq[rows]
+    if cols is not None:
+        dk, dv = dk[cols], dv[cols]
+    dq_ref, dk_ref, dv_ref, m = ref
+    assert_close(dq, dq_ref, dtype, "dQ (fwd+bwd)", m["dq"] + m["dq_from_D"])
+    assert_close(dk, dk_ref, dtype, "dK (fwd+bwd)", m["dk"] + m["dk_from_D"])
+    assert_close(dv, dv_ref, dtype, "dV (fwd+bwd)", m["dv"])
+
+
 def small_inputs(N, bs, hq, hkv, hd, dtype, seed):
     q = synth.normal(seed, 1, (N, bs, hq, hd), dtype=dtype, scale=0.5)
     k = synth.normal(seed, 2, (N, bs, hkv, hd), dtype=dtype)
@@ -90,12 +117,23 @@ def test_fwd_bwd_small_every_element(N, bs, hq, hkv, hd, dtype, causal, cu):
     o_ref, lse_ref, mo = oracle.attn_fwd(f[0], f[1], f[2], scale, causal, cu, magnitude=True)
     assert_close(to_f64(o), o_ref, dtype, "O", mo)
     assert_close(to_f64(lse), lse_ref, dtype, "LSE")
-    dq, dk, dv = gpu_bwd(qd, kd, vd, o, lse, dod, scale, causal, cu)
+    # Backward alone: both sides receive the oracle's O (rounded to the storage
+    # dtype) and LSE (fp32), so D and P start from the same values.
+    o_in = o_ref.astype(np.float32)
+    if dtype == "bf16":
+        o_in = bf16_round(o_ref)
+    lse_in = lse_ref.astype(np.float32)
+    dq, dk, dv = gpu_bwd(qd, kd, vd, to_device_f(o_in, dtype), to_device_f(lse_in, "f32"), dod,
+                         scale, causal, cu)
     dq_ref, dk_ref, dv_ref, m = oracle.attn_bwd(f[0], f[1], f[2], f[3], scale, causal, cu,
-                                                magnitude=True)
-    assert_close(to_f64(dq), dq_ref, dtype, "dQ", m[0])
-    assert_close(to_f64(dk), dk_ref, dtype, "dK", m[1])
-    assert_close(to_f64(dv), dv_ref, dtype, "dV", m[2])
+                                                magnitude=True, o=o_in, lse=lse_in)
+    assert_close(to_f64(dq), dq_ref, dtype, "dQ", m["dq"])
+    assert_close(to_f64(dk), dk_ref, dtype, "dK", m["dk"])
+    assert_close(to_f64(dv), dv_ref, dtype, "dV", m["dv"])
+    # Forward then backward on the GPU against the exact gradient.
+    dq, dk, dv = gpu_bwd(qd, kd, vd, o, lse, dod, scale, causal, cu)
+    check_end_to_end(dtype, (dq, dk, dv), oracle.attn_bwd(f[0], f[1], f[2], f[3], scale, causal,
+                                                          cu, magnitude=True))
 
 
 def test_fwd_bwd_are_deterministic():
@@ -138,11 +176,8 @@ def test_bwd_full_size_packed_documents():
     rows = sample_rows(w.seqlen, w.seed, n_first=128, n_last=128, n_rand=256)
     cols = np.concatenate([np.arange(cu[-3], cu[-1]), np.arange(0, 64)]).astype(np.int64)
     f = [synth.to_f64(x, w.dtype) for x in (q, k, v, do)]
-    dq_ref, dk_ref, dv_ref, m = oracle.attn_bwd(*f, w.softmax_scale, True, cu, dq_rows=rows,
-                                                dkv_cols=cols, magnitude=True)
-    assert_close(to_f64(pick(dq, rows)), dq_ref, w.dtype, "dQ rows", m[0])
-    assert_close(to_f64(pick(dk, cols)), dk_ref, w.dtype, "dK cols", m[1])
-    assert_close(to_f64(pick(dv, cols)), dv_ref, w.dtype, "dV cols", m[2])
+    ref = oracle.attn_bwd(*f, w.softmax_scale, True, cu, dq_rows=rows, dkv_cols=cols, magnitude=True)
+    check_end_to_end(w.dtype, (pick(dq, rows), pick(dk, cols), pick(dv, cols)), ref)
 
 
 def test_bwd_full_size_llama8b_128k():
@@ -156,11 +191,9 @@ def test_bwd_full_size_llama8b_128k():
     rows = sample_rows(w.seqlen, w.seed, n_first=64, n_last=64, n_rand=64)
     cols = np.arange(w.seqlen - 512, w.seqlen, dtype=np.int64)
     f = [synth.to_f64(x, w.dtype) for x in (q, k, v, do)]
-    dq_ref, dk_ref, dv_ref, m = oracle.attn_bwd(*f, w.softmax_scale, True, None, dq_rows=rows,
-                                                dkv_cols=cols, magnitude=True)
-    assert_close(to_f64(pick(dq, rows)), dq_ref, w.dtype, "dQ rows", m[0])
-    assert_close(to_f64(pick(dk, cols)), dk_ref, w.dtype, "dK cols", m[1])
-    assert_close(to_f64(pick(dv, cols)), dv_ref, w.dtype, "dV cols", m[2])
+    ref = oracle.attn_bwd(*f, w.softmax_scale, True, None, dq_rows=rows, dkv_cols=cols,
+                          magnitude=True)
+    check_end_to_end(w.dtype, (pick(dq, rows), pick(dk, cols), pick(dv, cols)), ref)
     # sum_j dV_j = sum over the group's heads and all rows of dO (softmax rows sum to 1)
     dv_sum = to_f64(dv).sum(axis=0)[:, 0]
     want = f[3].sum(axis=(0, 2))

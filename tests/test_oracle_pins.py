@@ -396,7 +396,8 @@ def test_magnitudes_match_torch_absolute_sums(causal, cu):
     g = hq // hkv
     q, k, v, do = rand(N, 1, hq, hd), rand(N, 1, hkv, hd), rand(N, 1, hkv, hd), rand(N, 1, hq, hd)
     _, _, mo = oracle.attn_fwd(q, k, v, scale, causal, cu, magnitude=True)
-    _, _, _, (mdq, mdk, mdv) = oracle.attn_bwd(q, k, v, do, scale, causal, cu, magnitude=True)
+    _, _, _, m = oracle.attn_bwd(q, k, v, do, scale, causal, cu, magnitude=True)
+    mdq, mdk, mdv = m["dq"], m["dk"], m["dv"]
     mask = torch.from_numpy(allowed_mask(N, causal, cu))
     kr = torch.from_numpy(np.repeat(k[:, 0], g, axis=1))   # [N, hq, hd]
     vr = torch.from_numpy(np.repeat(v[:, 0], g, axis=1))
@@ -415,6 +416,12 @@ def test_magnitudes_match_torch_absolute_sums(causal, cu):
     np.testing.assert_allclose(mdq[:, 0], want_mdq.numpy(), rtol=1e-10, atol=1e-11)
     np.testing.assert_allclose(mdk[:, 0], want_mdk.numpy(), rtol=1e-10, atol=1e-11)
     np.testing.assert_allclose(mdv[:, 0], want_mdv.numpy(), rtol=1e-11, atol=1e-12)
+    # sensitivity to D: A_i = sum_e |dO_ie| (P |V|)_ie
+    A = (tdo.abs() * want_mo).sum(-1)                        # [N, hq]
+    want_dq_d = scale * A[:, :, None] * torch.einsum("hij,jhe->ihe", pa, kr.abs())
+    want_dk_d = scale * torch.einsum("hij,ih,ihe->jhe", pa, A, tq.abs()).reshape(N, hkv, g, hd).sum(2)
+    np.testing.assert_allclose(m["dq_from_D"][:, 0], want_dq_d.numpy(), rtol=1e-10, atol=1e-11)
+    np.testing.assert_allclose(m["dk_from_D"][:, 0], want_dk_d.numpy(), rtol=1e-10, atol=1e-11)
 
 
 def test_magnitudes_bound_the_values_and_equal_them_for_same_sign_terms():
@@ -423,6 +430,34 @@ def test_magnitudes_bound_the_values_and_equal_them_for_same_sign_terms():
     v_pos, do_pos = np.abs(rand(N, 1, 1, hd)), np.abs(rand(N, 1, 2, hd))
     o, _, mo = oracle.attn_fwd(q, k, v_pos, 0.5, True, magnitude=True)
     np.testing.assert_allclose(mo, o, rtol=1e-13)            # all terms positive
-    dq, dk, dv, (mdq, mdk, mdv) = oracle.attn_bwd(q, k, v_pos, do_pos, 0.5, True, magnitude=True)
+    dq, dk, dv, m = oracle.attn_bwd(q, k, v_pos, do_pos, 0.5, True, magnitude=True)
+    mdq, mdk, mdv = m["dq"], m["dk"], m["dv"]
     np.testing.assert_allclose(mdv, dv, rtol=1e-13)
     assert np.all(mdq >= np.abs(dq) - 1e-12) and np.all(mdk >= np.abs(dk) - 1e-12)
+
+
+def test_bwd_with_given_forward_outputs():
+    """The backward as a call receives it: O and LSE passed in.  Passing the
+    oracle's own values changes nothing; shifting O changes D_i by <dO_i, dO_>
+    and moves dQ_i by -scale dD_i sum_j P_ij k_j (attention of q over k with
+    values k) and dK_j by -scale sum_i P_ij dD_i q_i, leaving dV unchanged."""
+    N, hd, cu, scale = 28, 8, [0, 11, 28], 0.7
+    q, k, v, do = rand(N, 1, 2, hd), rand(N, 1, 1, hd), rand(N, 1, 1, hd), rand(N, 1, 2, hd)
+    o, lse = oracle.attn_fwd(q, k, v, scale, True, cu)
+    base = oracle.attn_bwd(q, k, v, do, scale, True, cu)
+    same = oracle.attn_bwd(q, k, v, do, scale, True, cu, o=o, lse=lse)
+    for a, b in zip(base, same):
+        np.testing.assert_allclose(b, a, rtol=1e-12, atol=1e-13)
+    delta = 0.01 * rand(N, 1, 2, hd)
+    dq2, dk2, dv2 = oracle.attn_bwd(q, k, v, do, scale, True, cu, o=o + delta, lse=lse)
+    dD = np.sum(do * delta, axis=-1)                         # [N, 1, 2]
+    pk, _ = oracle.attn_fwd(q, k, k, scale, True, cu)        # sum_j P_ij k_j
+    np.testing.assert_allclose(dq2 - base[0], -scale * dD[..., None] * pk, rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(dv2, base[2], rtol=1e-12, atol=1e-13)
+    mask = allowed_mask(N, True, cu)
+    want_dk = np.zeros_like(k)
+    for h in range(2):
+        s_ = scale * q[:, 0, h] @ k[:, 0, 0].T
+        P = np.where(mask, np.exp(s_ - lse[0, h][:, None]), 0.0)
+        want_dk[:, 0, 0] += -scale * P.T @ (dD[:, 0, h][:, None] * q[:, 0, h])
+    np.testing.assert_allclose(dk2 - base[1], want_dk, rtol=1e-9, atol=1e-12)
