@@ -56,11 +56,6 @@ struct BwdParams {
   int64_t num_blocks;
 };
 
-template <int kChunks, int kRowBytes>
-__device__ __forceinline__ int swz(int row, int ch) {
-  return row * kRowBytes + ((ch ^ (row & (kChunks - 1))) << 4);
-}
-
 // A operand (rows = head dim, k = 16 sequence positions starting at row0)
 // read transposed from a row-major swizzled LDS tile: lane l gets the
 // values of column d = 32*db + l%32 at the 8 sequence rows matching the
@@ -211,12 +206,16 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_kernel(BwdParams p) {
         dp = mfma32(*reinterpret_cast<const bf16x8_t*>(lds_v + off), df[ks], dp);
       }
       bf16x8_t dsf[2];
+      // visible keys of this row as offsets into the 32-key block, clamped
+      const int64_t jb = j0 + kb * 32;
+      const int lo = (int)(my_lo - jb < -1 ? -1 : (my_lo - jb > 33 ? 33 : my_lo - jb));
+      const int hi = (int)(my_hi - jb < -1 ? -1 : (my_hi - jb > 33 ? 33 : my_hi - jb));
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         float pv = __builtin_amdgcn_exp2f(fmaf(s[i], p.scale_log2, -lse2));
         if (need_mask) {
-          const int64_t j = j0 + kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-          if (j < my_lo || j >= my_hi) pv = 0.f;
+          const int j = 8 * (i >> 2) + 4 * half + (i & 3);
+          if (j < lo || j >= hi) pv = 0.f;
         }
         dsf[i >> 3][i & 7] = (__bf16)(pv * (dp[i] - Di));
       }
@@ -248,28 +247,44 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_kernel(BwdParams p) {
 // ------------------------------------------------------------------------
 // dK, dV
 // ------------------------------------------------------------------------
-template <int HD>
+// A workgroup of WAVES waves owns WAVES * KB * 32 key rows of one key/value
+// head; each wave owns KB blocks of 32 rows and keeps their K fragments and
+// its dK^T, dV^T accumulators in registers.  V for the workgroup's rows stays
+// in LDS (B operand of dP = dO V^T).  The workgroup walks the visible query
+// positions in tiles of BQ, from the last tile down to the first, and within
+// a tile every query head of the GQA group; each (tile, head) step stages Q,
+// dO, LSE and D in LDS once for all its keys, and every Q or dO fragment a
+// wave reads from LDS feeds all KB of its key blocks.  Walking queries from
+// the end keeps the workgroups resident at the same time on the same query
+// tiles, so those tiles are shared through L2.  The launch uses 4 waves of
+// one 32-row block each (128 keys, one wave per SIMD): larger shapes do not
+// fit the register file without spilling.
+template <int HD, int WAVES = 4, int KB = 2, int BQ = 64>
 struct DkvCfg {
-  static constexpr int kWaves = 4;
+  static constexpr int kWaves = WAVES;
   static constexpr int kThreads = 64 * kWaves;
-  static constexpr int kBK = 32 * kWaves;   // key rows per block
-  static constexpr int kBQ = 32;            // query rows per tile
+  static constexpr int kKB = KB;              // 32-row key blocks per wave
+  static constexpr int kBK = 32 * kKB * kWaves;   // key rows per workgroup
+  static constexpr int kBQ = BQ;              // query rows per step
   static constexpr int kChunks = HD / 8;
   static constexpr int kRowBytes = HD * 2;
+  static constexpr int kVBytes = kBK * kRowBytes;
   static constexpr int kTileBytes = kBQ * kRowBytes;
   static constexpr int kKS = HD / 16;
   static constexpr int kDB = HD / 32;
-  static constexpr int kLoads = kBQ * kChunks / kThreads;
+  static constexpr int kLoads = kBQ * kChunks / kThreads;   // per tensor per step
+  static constexpr int kVLoads = kBK * kChunks / kThreads;
   static_assert(kLoads >= 1 && kBQ * kChunks % kThreads == 0, "tile loads");
 };
 
-template <int HD>
-__global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(BwdParams p) {
-  using C = DkvCfg<HD>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * C::kTileBytes + 2 * C::kBQ * 4];
-  char* lds_q = smem;
-  char* lds_do = smem + C::kTileBytes;
-  float* lds_lse = reinterpret_cast<float*>(smem + 2 * C::kTileBytes);
+template <int HD, int WAVES, int KB, int BQ>
+__global__ __launch_bounds__(64 * WAVES) void attn_bwd_dkv_kernel(BwdParams p) {
+  using C = DkvCfg<HD, WAVES, KB, BQ>;
+  __shared__ __attribute__((aligned(16))) char smem[C::kVBytes + 2 * C::kTileBytes + 2 * C::kBQ * 4];
+  char* lds_v = smem;
+  char* lds_q = smem + C::kVBytes;
+  char* lds_do = lds_q + C::kTileBytes;
+  float* lds_lse = reinterpret_cast<float*>(lds_do + C::kTileBytes);
   float* lds_D = lds_lse + C::kBQ;
 
   const int tid = threadIdx.x;
@@ -281,58 +296,69 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(BwdParams p) {
   const int64_t N = p.N;
   const int kh = blockIdx.y % p.hkv;
   const int b = blockIdx.y / p.hkv;
-  const int64_t k0 = (int64_t)blockIdx.x * C::kBK;   // lightest blocks (largest keys) last
-  const int64_t kw = k0 + 32 * wave;
-  const int64_t kj = kw + r32;
+  const int64_t k0 = (int64_t)blockIdx.x * C::kBK;   // heaviest (smallest keys) first
+  const int64_t kw = k0 + 32 * C::kKB * wave;       // first key row of this wave
 
   const int64_t q_tok = (int64_t)p.bs * p.hq * HD;
   const int64_t kv_tok = (int64_t)p.bs * p.hkv * HD;
   const int64_t kvoff = ((int64_t)b * p.hkv + kh) * HD;
 
-  // K and V rows of this lane (B operands of S = Q K^T and dP = dO V^T).
-  bf16x8_t kf[C::kKS], vf[C::kKS];
+  // K rows of this lane (B operand of S = Q K^T), one per key block.
+  bf16x8_t kf[C::kKB][C::kKS];
+  int64_t my_lo[C::kKB], my_hi[C::kKB];
 #pragma unroll
-  for (int ks = 0; ks < C::kKS; ++ks) {
-    if (kj < N) {
-      kf[ks] = *reinterpret_cast<const bf16x8_t*>(p.k + kj * kv_tok + kvoff + 16 * ks + 8 * half);
-      vf[ks] = *reinterpret_cast<const bf16x8_t*>(p.v + kj * kv_tok + kvoff + 16 * ks + 8 * half);
-    } else {
-      kf[ks] = bf16x8_t{};
-      vf[ks] = bf16x8_t{};
-    }
+  for (int kb = 0; kb < C::kKB; ++kb) {
+    const int64_t kj = kw + 32 * kb + r32;
+#pragma unroll
+    for (int ks = 0; ks < C::kKS; ++ks)
+      kf[kb][ks] = kj < N ? *reinterpret_cast<const bf16x8_t*>(p.k + kj * kv_tok + kvoff + 16 * ks + 8 * half)
+                          : bf16x8_t{};
+    // queries that see key kj: [causal ? kj : doc_start(kj), doc_end(kj))
+    my_lo[kb] = kj < N ? (p.causal ? kj : doc_start_of(p.cu, p.n_docs, kj)) : 0;
+    my_hi[kb] = kj < N ? doc_end_of(p.cu, p.n_docs, kj, N) : 0;
+  }
+  // V rows of the whole workgroup into LDS.
+#pragma unroll
+  for (int i = 0; i < C::kVLoads; ++i) {
+    const int cid = tid + i * C::kThreads;
+    const int row = cid / C::kChunks;
+    const int ch = cid % C::kChunks;
+    const int64_t j = k0 + row;
+    const u32x4_t val = j < N ? *reinterpret_cast<const u32x4_t*>(p.v + j * kv_tok + kvoff + ch * 8)
+                              : u32x4_t{};
+    *reinterpret_cast<u32x4_t*>(lds_v + swz<C::kChunks, C::kRowBytes>(row, ch)) = val;
   }
 
-  // Queries that see key j: [causal ? j : doc_start(j), doc_end(j)).
   const int64_t k_last = (k0 + C::kBK < N ? k0 + C::kBK : N) - 1;
   const int64_t q_lo = p.causal ? k0 : doc_start_of(p.cu, p.n_docs, k0);
   const int64_t q_hi = doc_end_of(p.cu, p.n_docs, k_last, N);
   const bool wave_active = kw < N;
-  const int64_t w_last = wave_active ? (kw + 31 < N ? kw + 31 : N - 1) : 0;
+  const int64_t w_last = wave_active ? (kw + 32 * C::kKB - 1 < N ? kw + 32 * C::kKB - 1 : N - 1) : 0;
   const int64_t w_lo = wave_active ? (p.causal ? kw : doc_start_of(p.cu, p.n_docs, kw)) : 0;
   const int64_t w_hi = wave_active ? doc_end_of(p.cu, p.n_docs, w_last, N) : 0;
   // Queries seen by every key of the wave: [full_lo, full_hi).
   const int64_t full_lo = wave_active ? (p.causal ? w_last : doc_start_of(p.cu, p.n_docs, w_last)) : 0;
   const int64_t full_hi = wave_active ? doc_end_of(p.cu, p.n_docs, kw, N) : 0;
-  const int64_t my_lo = kj < N ? (p.causal ? kj : doc_start_of(p.cu, p.n_docs, kj)) : 0;
-  const int64_t my_hi = kj < N ? doc_end_of(p.cu, p.n_docs, kj, N) : 0;
 
-  const int64_t qt_begin = q_lo / C::kBQ;
-  const int64_t qt_end = (q_hi + C::kBQ - 1) / C::kBQ;
-  const int64_t it_begin = qt_begin * p.g;
-  const int64_t it_end = qt_end * p.g;
+  const int64_t qt_lo = q_lo / C::kBQ;
+  const int64_t qt_hi = (q_hi + C::kBQ - 1) / C::kBQ;
+  // Steps run from the last query tile down: step n is tile qt_hi-1-n/g, head n%g.
+  const int64_t n_steps = (qt_hi - qt_lo) * p.g;
 
-  f32x16_t acc_dk[C::kDB], acc_dv[C::kDB];
+  f32x16_t acc_dk[C::kKB][C::kDB], acc_dv[C::kKB][C::kDB];
 #pragma unroll
-  for (int db = 0; db < C::kDB; ++db) {
-    acc_dk[db] = f32x16_t{};
-    acc_dv[db] = f32x16_t{};
-  }
+  for (int kb = 0; kb < C::kKB; ++kb)
+#pragma unroll
+    for (int db = 0; db < C::kDB; ++db) {
+      acc_dk[kb][db] = f32x16_t{};
+      acc_dv[kb][db] = f32x16_t{};
+    }
 
   u32x4_t qst[C::kLoads], dst[C::kLoads];
   float sst = 0.f;
-  auto load_tile = [&](int64_t it) {
-    const int64_t i0 = (it / p.g) * C::kBQ;
-    const int h = kh * p.g + (int)(it % p.g);
+  auto load_step = [&](int64_t n) {
+    const int64_t i0 = (qt_hi - 1 - n / p.g) * C::kBQ;
+    const int h = kh * p.g + (int)(n % p.g);
     const int64_t qoff = ((int64_t)b * p.hq + h) * HD;
 #pragma unroll
     for (int i = 0; i < C::kLoads; ++i) {
@@ -353,7 +379,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(BwdParams p) {
       sst = qi < N ? (tid < C::kBQ ? p.lse[idx] * kLog2e : p.D[idx]) : 0.f;
     }
   };
-  auto store_tile = [&]() {
+  auto store_step = [&]() {
 #pragma unroll
     for (int i = 0; i < C::kLoads; ++i) {
       const int cid = tid + i * C::kThreads;
@@ -364,70 +390,111 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(BwdParams p) {
     if (tid < 2 * C::kBQ) lds_lse[tid] = sst;   // lds_D follows lds_lse
   };
 
-  if (it_begin < it_end) load_tile(it_begin);
-  for (int64_t it = it_begin; it < it_end; ++it) {
+  if (n_steps > 0) load_step(0);
+  for (int64_t n = 0; n < n_steps; ++n) {
     __syncthreads();
-    store_tile();
+    store_step();
     __syncthreads();
-    if (it + 1 < it_end) load_tile(it + 1);
-    const int64_t i0 = (it / p.g) * C::kBQ;
+    if (n + 1 < n_steps) load_step(n + 1);
+    const int64_t i0 = (qt_hi - 1 - n / p.g) * C::kBQ;
     if (!wave_active || i0 >= w_hi || i0 + C::kBQ <= w_lo) continue;
-    const bool need_mask = i0 < full_lo || i0 + C::kBQ > full_hi;
 
-    // S = Q K^T, dP = dO V^T: lane holds key kj and 16 query rows.
-    f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+#pragma unroll 1
+    for (int sub = 0; sub < C::kBQ / 32; ++sub) {
+      const int64_t s0 = i0 + 32 * sub;
+      if (s0 >= w_hi || s0 + 32 <= w_lo) continue;
+      const bool need_mask = s0 < full_lo || s0 + 32 > full_hi;
+      // S = Q K^T and dP = dO V^T for both key blocks: lane holds key
+      // kw + 32 kb + lane%32 and 16 query rows.
+      f32x16_t s[C::kKB], dp[C::kKB];
 #pragma unroll
-    for (int ks = 0; ks < C::kKS; ++ks) {
-      const int off = swz<C::kChunks, C::kRowBytes>(r32, 2 * ks + half);
-      s = mfma32(*reinterpret_cast<const bf16x8_t*>(lds_q + off), kf[ks], s);
-      dp = mfma32(*reinterpret_cast<const bf16x8_t*>(lds_do + off), vf[ks], dp);
-    }
-    bf16x8_t pf[2], dsf[2];
+      for (int kb = 0; kb < C::kKB; ++kb) {
+        s[kb] = f32x16_t{};
+        dp[kb] = f32x16_t{};
+      }
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const int qr0 = 8 * r4 + 4 * half;
-      const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(lds_lse + qr0);
-      const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(lds_D + qr0);
+      for (int ks = 0; ks < C::kKS; ++ks) {
+        const int off = swz<C::kChunks, C::kRowBytes>(32 * sub + r32, 2 * ks + half);
+        const bf16x8_t qa = *reinterpret_cast<const bf16x8_t*>(lds_q + off);
+        const bf16x8_t da = *reinterpret_cast<const bf16x8_t*>(lds_do + off);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = 4 * r4 + e;
-        float pv = __builtin_amdgcn_exp2f(fmaf(s[i], p.scale_log2, -l4[e]));
-        if (need_mask) {
-          const int64_t qpos = i0 + qr0 + e;
-          if (qpos < my_lo || qpos >= my_hi) pv = 0.f;
+        for (int kb = 0; kb < C::kKB; ++kb) {
+          s[kb] = mfma32(qa, kf[kb][ks], s[kb]);
+          const bf16x8_t vb = *reinterpret_cast<const bf16x8_t*>(
+              lds_v + swz<C::kChunks, C::kRowBytes>(32 * (C::kKB * wave + kb) + r32, 2 * ks + half));
+          dp[kb] = mfma32(da, vb, dp[kb]);
         }
-        pf[i >> 3][i & 7] = (__bf16)pv;
-        dsf[i >> 3][i & 7] = (__bf16)(pv * (dp[i] - d4[e]));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // visible queries of each key as offsets into the 32-row sub-tile
+      int lo[C::kKB], hi[C::kKB];
+#pragma unroll
+      for (int kb = 0; kb < C::kKB; ++kb) {
+        lo[kb] = (int)(my_lo[kb] - s0 < -1 ? -1 : (my_lo[kb] - s0 > 33 ? 33 : my_lo[kb] - s0));
+        hi[kb] = (int)(my_hi[kb] - s0 < -1 ? -1 : (my_hi[kb] - s0 > 33 ? 33 : my_hi[kb] - s0));
+      }
+      // P and dS for 16 query rows at a time (B operands), then
+      // dV^T += dO^T P and dK^T += Q^T dS over those rows.
+#pragma unroll
+      for (int ks2 = 0; ks2 < 2; ++ks2) {
+        bf16x8_t pf[C::kKB], dsf[C::kKB];
+#pragma unroll
+        for (int r2 = 0; r2 < 2; ++r2) {
+          const int r4 = 2 * ks2 + r2;
+          const int qr0 = 32 * sub + 8 * r4 + 4 * half;
+          const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(lds_lse + qr0);
+          const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(lds_D + qr0);
+#pragma unroll
+          for (int kb = 0; kb < C::kKB; ++kb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int i = 4 * r4 + e;
+              float pv = __builtin_amdgcn_exp2f(fmaf(s[kb][i], p.scale_log2, -l4[e]));
+              if (need_mask) {
+                const int qr = qr0 - 32 * sub + e;   // row within the sub-tile
+                if (qr < lo[kb] || qr >= hi[kb]) pv = 0.f;
+              }
+              pf[kb][4 * r2 + e] = (__bf16)pv;
+              dsf[kb][4 * r2 + e] = (__bf16)(pv * (dp[kb][i] - d4[e]));
+            }
+        }
+#pragma unroll
+        for (int db = 0; db < C::kDB; ++db) {
+          const bf16x8_t dot =
+              load_tr_operand<C::kChunks, C::kRowBytes>(lds_do, 32 * sub + 16 * ks2, db, lane);
+          const bf16x8_t qt =
+              load_tr_operand<C::kChunks, C::kRowBytes>(lds_q, 32 * sub + 16 * ks2, db, lane);
+#pragma unroll
+          for (int kb = 0; kb < C::kKB; ++kb) {
+            acc_dv[kb][db] = mfma32(dot, pf[kb], acc_dv[kb][db]);
+            acc_dk[kb][db] = mfma32(qt, dsf[kb], acc_dk[kb][db]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
-    // dV^T += dO^T P, dK^T += Q^T dS
-#pragma unroll
-    for (int ks2 = 0; ks2 < 2; ++ks2)
-#pragma unroll
-      for (int db = 0; db < C::kDB; ++db) {
-        const bf16x8_t dot = load_tr_operand<C::kChunks, C::kRowBytes>(lds_do, 16 * ks2, db, lane);
-        acc_dv[db] = mfma32(dot, pf[ks2], acc_dv[db]);
-        const bf16x8_t qt = load_tr_operand<C::kChunks, C::kRowBytes>(lds_q, 16 * ks2, db, lane);
-        acc_dk[db] = mfma32(qt, dsf[ks2], acc_dk[db]);
-      }
   }
 
-  if (kj >= N) return;
-  __bf16* dkrow = p.dk + kj * kv_tok + kvoff;
-  __bf16* dvrow = p.dv + kj * kv_tok + kvoff;
 #pragma unroll
-  for (int db = 0; db < C::kDB; ++db)
+  for (int kb = 0; kb < C::kKB; ++kb) {
+    const int64_t kj = kw + 32 * kb + r32;
+    if (kj >= N) continue;
+    __bf16* dkrow = p.dk + kj * kv_tok + kvoff;
+    __bf16* dvrow = p.dv + kj * kv_tok + kvoff;
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      bf16x4_t wk, wv;
+    for (int db = 0; db < C::kDB; ++db)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        wk[e] = (__bf16)(acc_dk[db][4 * r4 + e] * p.scale);
-        wv[e] = (__bf16)acc_dv[db][4 * r4 + e];
+      for (int r4 = 0; r4 < 4; ++r4) {
+        bf16x4_t wk, wv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          wk[e] = (__bf16)(acc_dk[kb][db][4 * r4 + e] * p.scale);
+          wv[e] = (__bf16)acc_dv[kb][db][4 * r4 + e];
+        }
+        *reinterpret_cast<bf16x4_t*>(dkrow + db * 32 + 8 * r4 + 4 * half) = wk;
+        *reinterpret_cast<bf16x4_t*>(dvrow + db * 32 + 8 * r4 + 4 * half) = wv;
       }
-      *reinterpret_cast<bf16x4_t*>(dkrow + db * 32 + 8 * r4 + 4 * half) = wk;
-      *reinterpret_cast<bf16x4_t*>(dvrow + db * 32 + 8 * r4 + 4 * half) = wv;
-    }
+  }
 }
 
 template <int HD, int GPACK>
@@ -486,9 +553,9 @@ hipError_t launch_attn_bwd_bf16(const AttnShape& s, const void* q, const void* k
   };
   auto dkv_launch = [&](auto hd_tag) -> hipError_t {
     constexpr int HD = decltype(hd_tag)::value;
-    using C = DkvCfg<HD>;
+    using C = DkvCfg<HD, 4, 1, 64>;
     dim3 grid((uint32_t)((s.N + C::kBK - 1) / C::kBK), (uint32_t)(s.bs * s.hkv));
-    return launch_kernel(attn_bwd_dkv_kernel<HD>, grid, dim3(C::kThreads), 0, stream, p);
+    return launch_kernel(attn_bwd_dkv_kernel<HD, 4, 1, 64>, grid, dim3(C::kThreads), 0, stream, p);
   };
   if (s.hd == 128) {
     if ((e = dq_launch(std::integral_constant<int, 128>{})) != hipSuccess) return e;

@@ -27,8 +27,8 @@
 //  * Key tiles entirely above the diagonal (or outside the documents of a
 //    block) are never visited; per wave, tiles entirely masked for its rows
 //    are skipped; only tiles crossing a boundary apply the element mask.
-//  * LDS rows are XOR-swizzled in 16-byte chunks so the per-row MFMA reads
-//    of 32 different rows fall in different banks.
+//  * LDS rows are swizzled in 16-byte chunks (swz in device_common.h) so both
+//    the row reads of K and the transposing reads of V avoid bank conflicts.
 //  * Blocks are launched heaviest (largest positions) first.
 #include <math.h>
 
@@ -67,12 +67,6 @@ struct FwdCfg {
   static constexpr int kLoads = kBC * kChunks / kThreads;  // 16-byte loads per tensor per tile
   static_assert(kLoads >= 1 && kBC * kChunks % kThreads == 0, "tile loads");
 };
-
-// Byte offset of 16-byte chunk `ch` of row `row` in a swizzled LDS tile.
-template <int kChunks, int kRowBytes>
-__device__ __forceinline__ int swz(int row, int ch) {
-  return row * kRowBytes + ((ch ^ (row & (kChunks - 1))) << 4);
-}
 
 template <int HD, int GPACK>
 __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdParams p) {
@@ -194,12 +188,15 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdParams p) {
     // Element mask on tiles that cross a boundary of some row of the wave.
     const bool need_mask = j0 < full_lo || j0 + C::kBC > full_hi;
     if (need_mask) {
+      // visible keys of this row as offsets into the tile, clamped to [-1, 65]
+      const int lo = (int)(my_lo - j0 < -1 ? -1 : (my_lo - j0 > 65 ? 65 : my_lo - j0));
+      const int hi = (int)(my_hi - j0 < -1 ? -1 : (my_hi - j0 > 65 ? 65 : my_hi - j0));
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int64_t j = j0 + kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-          if (j < my_lo || j >= my_hi) s[kb][i] = -INFINITY;
+          const int j = kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+          if (j < lo || j >= hi) s[kb][i] = -INFINITY;
         }
     }
 

@@ -41,9 +41,27 @@ __device__ __forceinline__ bf16x4_t lds_read_tr16(const void* p) {
   return __builtin_bit_cast(bf16x4_t, v);
 }
 
+// Lanes l and l^32 exchange values.
 __device__ __forceinline__ float wave_shfl_xor32(float x) {
-  // lanes l and l^32 exchange values
   return __shfl_xor(x, 32, 64);
+}
+
+// Byte offset of 16-byte chunk `ch` of row `row` in an LDS tile of rows of
+// kChunks chunks.  The chunk index is XORed with a per-row value f(row) that
+// takes all 16 values over any 16 consecutive rows (so 16 lanes reading one
+// chunk column of 16 rows hit 16 different bank groups) and, over any 4
+// consecutive rows starting at a multiple of 4, differs in its upper two bits
+// (so the transposing reads, which take 4 rows x 4 chunks per 16 or 32
+// lanes, also hit distinct bank groups).  For 8-chunk rows the same holds
+// with 8 values.
+template <int kChunks, int kRowBytes>
+__device__ __forceinline__ int swz(int row, int ch) {
+  int f;
+  if constexpr (kChunks == 16)
+    f = ((row & 3) << 2) | ((row >> 2) & 3);
+  else
+    f = ((row & 1) << 2) | ((row >> 1) & 3);
+  return row * kRowBytes + ((ch ^ f) << 4);
 }
 
 __device__ __forceinline__ bool wave_any(bool pred) {
