@@ -196,38 +196,63 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_kernel(BwdParams p) {
 
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      // S^T = K Q^T and dP^T = V dO^T for 32 keys.
+      // S^T = K Q^T and dP^T = V dO^T for 32 keys; the K and V fragments of
+      // each k-step are read from LDS two steps ahead of their products.
       f32x16_t s = f32x16_t{}, dp = f32x16_t{};
-      const int row = kb * 32 + r32;
+      {
+        const int row = kb * 32 + r32;
+        auto frags = [&](int ks, bf16x8_t& kfr, bf16x8_t& vfr) {
+          const int off = swz<C::kChunks, C::kRowBytes>(row, 2 * ks + half);
+          kfr = *reinterpret_cast<const bf16x8_t*>(lds_k + off);
+          vfr = *reinterpret_cast<const bf16x8_t*>(lds_v + off);
+        };
+        bf16x8_t kb3[3], vb3[3];
+        frags(0, kb3[0], vb3[0]);
+        frags(1, kb3[1], vb3[1]);
 #pragma unroll
-      for (int ks = 0; ks < C::kKS; ++ks) {
-        const int off = swz<C::kChunks, C::kRowBytes>(row, 2 * ks + half);
-        s = mfma32(*reinterpret_cast<const bf16x8_t*>(lds_k + off), qf[ks], s);
-        dp = mfma32(*reinterpret_cast<const bf16x8_t*>(lds_v + off), df[ks], dp);
+        for (int ks = 0; ks < C::kKS; ++ks) {
+          if (ks + 2 < C::kKS) frags(ks + 2, kb3[(ks + 2) % 3], vb3[(ks + 2) % 3]);
+          s = mfma32(kb3[ks % 3], qf[ks], s);
+          dp = mfma32(vb3[ks % 3], df[ks], dp);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
       bf16x8_t dsf[2];
-      // visible keys of this row as offsets into the 32-key block, clamped
-      const int64_t jb = j0 + kb * 32;
-      const int lo = (int)(my_lo - jb < -1 ? -1 : (my_lo - jb > 33 ? 33 : my_lo - jb));
-      const int hi = (int)(my_hi - jb < -1 ? -1 : (my_hi - jb > 33 ? 33 : my_hi - jb));
+      if (need_mask) {
+        // visible keys of this row as offsets into the 32-key block, clamped;
+        // invisible scores become -inf so their P and dS are exactly 0
+        const int64_t jb = j0 + kb * 32;
+        const int lo = (int)(my_lo - jb < -1 ? -1 : (my_lo - jb > 33 ? 33 : my_lo - jb));
+        const int hi = (int)(my_hi - jb < -1 ? -1 : (my_hi - jb > 33 ? 33 : my_hi - jb));
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int j = 8 * (i >> 2) + 4 * half + (i & 3);
+          if (j < lo || j >= hi) s[i] = -INFINITY;
+        }
+      }
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        float pv = __builtin_amdgcn_exp2f(fmaf(s[i], p.scale_log2, -lse2));
-        if (need_mask) {
-          const int j = 8 * (i >> 2) + 4 * half + (i & 3);
-          if (j < lo || j >= hi) pv = 0.f;
-        }
+        const float pv = __builtin_amdgcn_exp2f(fmaf(s[i], p.scale_log2, -lse2));
         dsf[i >> 3][i & 7] = (__bf16)(pv * (dp[i] - Di));
       }
-      // dQ^T += K^T dS^T
+      // dQ^T += K^T dS^T; K^T fragments by transposing LDS reads, two
+      // products ahead, four independent accumulator chains.
+      {
+        constexpr int kSteps = 2 * C::kDB;   // (ks2, db) pairs, db fastest
+        auto ktfrag = [&](int idx) {
+          return load_tr_operand<C::kChunks, C::kRowBytes>(lds_k, kb * 32 + 16 * (idx / C::kDB),
+                                                           idx % C::kDB, lane);
+        };
+        bf16x8_t buf[3];
+        buf[0] = ktfrag(0);
+        buf[1] = ktfrag(1);
 #pragma unroll
-      for (int ks2 = 0; ks2 < 2; ++ks2)
-#pragma unroll
-        for (int db = 0; db < C::kDB; ++db) {
-          const bf16x8_t kt =
-              load_tr_operand<C::kChunks, C::kRowBytes>(lds_k, kb * 32 + 16 * ks2, db, lane);
-          acc[db] = mfma32(kt, dsf[ks2], acc[db]);
+        for (int idx = 0; idx < kSteps; ++idx) {
+          if (idx + 2 < kSteps) buf[(idx + 2) % 3] = ktfrag(idx + 2);
+          acc[idx % C::kDB] = mfma32(buf[idx % 3], dsf[idx / C::kDB], acc[idx % C::kDB]);
+          __builtin_amdgcn_sched_barrier(0);
         }
+      }
     }
   }
 
@@ -277,7 +302,7 @@ struct DkvCfg {
   static_assert(kLoads >= 1 && kBQ * kChunks % kThreads == 0, "tile loads");
 };
 
-template <int HD, int WAVES, int KB, int BQ>
+template <int HD, int WAVES, int KB, int BQ, int PF>
 __global__ __launch_bounds__(64 * WAVES) void attn_bwd_dkv_kernel(BwdParams p) {
   using C = DkvCfg<HD, WAVES, KB, BQ>;
   __shared__ __attribute__((aligned(16))) char smem[C::kVBytes + 2 * C::kTileBytes + 2 * C::kBQ * 4];
@@ -404,35 +429,76 @@ __global__ __launch_bounds__(64 * WAVES) void attn_bwd_dkv_kernel(BwdParams p) {
       const int64_t s0 = i0 + 32 * sub;
       if (s0 >= w_hi || s0 + 32 <= w_lo) continue;
       const bool need_mask = s0 < full_lo || s0 + 32 > full_hi;
-      // S = Q K^T and dP = dO V^T for both key blocks: lane holds key
-      // kw + 32 kb + lane%32 and 16 query rows.
+      // S = Q K^T and dP = dO V^T for every key block: lane holds key
+      // kw + 32 kb + lane%32 and 16 query rows.  The Q, dO and V fragments of
+      // each k-step are read from LDS PF steps ahead of their products.
       f32x16_t s[C::kKB], dp[C::kKB];
 #pragma unroll
       for (int kb = 0; kb < C::kKB; ++kb) {
         s[kb] = f32x16_t{};
         dp[kb] = f32x16_t{};
       }
+      {
+        struct Frags {
+          bf16x8_t qa, da, vb[C::kKB];
+        };
+        auto frags = [&](int ks) {
+          Frags f;
+          const int off = swz<C::kChunks, C::kRowBytes>(32 * sub + r32, 2 * ks + half);
+          f.qa = *reinterpret_cast<const bf16x8_t*>(lds_q + off);
+          f.da = *reinterpret_cast<const bf16x8_t*>(lds_do + off);
 #pragma unroll
-      for (int ks = 0; ks < C::kKS; ++ks) {
-        const int off = swz<C::kChunks, C::kRowBytes>(32 * sub + r32, 2 * ks + half);
-        const bf16x8_t qa = *reinterpret_cast<const bf16x8_t*>(lds_q + off);
-        const bf16x8_t da = *reinterpret_cast<const bf16x8_t*>(lds_do + off);
+          for (int kb = 0; kb < C::kKB; ++kb)
+            f.vb[kb] = *reinterpret_cast<const bf16x8_t*>(
+                lds_v + swz<C::kChunks, C::kRowBytes>(32 * (C::kKB * wave + kb) + r32, 2 * ks + half));
+          return f;
+        };
+        Frags buf[PF + 1];
+#pragma unroll
+        for (int i = 0; i < PF; ++i) buf[i] = frags(i);
+#pragma unroll
+        for (int ks = 0; ks < C::kKS; ++ks) {
+          if (ks + PF < C::kKS) buf[(ks + PF) % (PF + 1)] = frags(ks + PF);
+          const Frags& f = buf[ks % (PF + 1)];
+#pragma unroll
+          for (int kb = 0; kb < C::kKB; ++kb) {
+            s[kb] = mfma32(f.qa, kf[kb][ks], s[kb]);
+            dp[kb] = mfma32(f.da, f.vb[kb], dp[kb]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      // On sub-tiles that cross a boundary, scores of invisible (query, key)
+      // pairs become -inf, so their P and dS are exactly 0.
+      if (need_mask) {
 #pragma unroll
         for (int kb = 0; kb < C::kKB; ++kb) {
-          s[kb] = mfma32(qa, kf[kb][ks], s[kb]);
-          const bf16x8_t vb = *reinterpret_cast<const bf16x8_t*>(
-              lds_v + swz<C::kChunks, C::kRowBytes>(32 * (C::kKB * wave + kb) + r32, 2 * ks + half));
-          dp[kb] = mfma32(da, vb, dp[kb]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      // visible queries of each key as offsets into the 32-row sub-tile
-      int lo[C::kKB], hi[C::kKB];
+          // visible queries of this key as offsets into the 32-row sub-tile
+          const int lo = (int)(my_lo[kb] - s0 < -1 ? -1 : (my_lo[kb] - s0 > 33 ? 33 : my_lo[kb] - s0));
+          const int hi = (int)(my_hi[kb] - s0 < -1 ? -1 : (my_hi[kb] - s0 > 33 ? 33 : my_hi[kb] - s0));
 #pragma unroll
-      for (int kb = 0; kb < C::kKB; ++kb) {
-        lo[kb] = (int)(my_lo[kb] - s0 < -1 ? -1 : (my_lo[kb] - s0 > 33 ? 33 : my_lo[kb] - s0));
-        hi[kb] = (int)(my_hi[kb] - s0 < -1 ? -1 : (my_hi[kb] - s0 > 33 ? 33 : my_hi[kb] - s0));
+          for (int i = 0; i < 16; ++i) {
+            const int qr = 8 * (i >> 2) + 4 * half + (i & 3);
+            if (qr < lo || qr >= hi) s[kb][i] = -INFINITY;
+          }
+        }
       }
+      // dO^T and Q^T fragments (transposing LDS reads) for the (16-row step,
+      // head-dim block) products, read PF products ahead.
+      struct TrFrags {
+        bf16x8_t dot, qt;
+      };
+      constexpr int kTrSteps = 2 * C::kDB;
+      auto trfrags = [&](int idx) {
+        TrFrags f;
+        const int ks2 = idx / C::kDB, db = idx % C::kDB;
+        f.dot = load_tr_operand<C::kChunks, C::kRowBytes>(lds_do, 32 * sub + 16 * ks2, db, lane);
+        f.qt = load_tr_operand<C::kChunks, C::kRowBytes>(lds_q, 32 * sub + 16 * ks2, db, lane);
+        return f;
+      };
+      TrFrags tbuf[PF + 1];
+#pragma unroll
+      for (int i = 0; i < PF; ++i) tbuf[i] = trfrags(i);
       // P and dS for 16 query rows at a time (B operands), then
       // dV^T += dO^T P and dK^T += Q^T dS over those rows.
 #pragma unroll
@@ -449,25 +515,20 @@ __global__ __launch_bounds__(64 * WAVES) void attn_bwd_dkv_kernel(BwdParams p) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int i = 4 * r4 + e;
-              float pv = __builtin_amdgcn_exp2f(fmaf(s[kb][i], p.scale_log2, -l4[e]));
-              if (need_mask) {
-                const int qr = qr0 - 32 * sub + e;   // row within the sub-tile
-                if (qr < lo[kb] || qr >= hi[kb]) pv = 0.f;
-              }
+              const float pv = __builtin_amdgcn_exp2f(fmaf(s[kb][i], p.scale_log2, -l4[e]));
               pf[kb][4 * r2 + e] = (__bf16)pv;
               dsf[kb][4 * r2 + e] = (__bf16)(pv * (dp[kb][i] - d4[e]));
             }
         }
 #pragma unroll
         for (int db = 0; db < C::kDB; ++db) {
-          const bf16x8_t dot =
-              load_tr_operand<C::kChunks, C::kRowBytes>(lds_do, 32 * sub + 16 * ks2, db, lane);
-          const bf16x8_t qt =
-              load_tr_operand<C::kChunks, C::kRowBytes>(lds_q, 32 * sub + 16 * ks2, db, lane);
+          const int idx = ks2 * C::kDB + db;
+          if (idx + PF < kTrSteps) tbuf[(idx + PF) % (PF + 1)] = trfrags(idx + PF);
+          const TrFrags& f = tbuf[idx % (PF + 1)];
 #pragma unroll
           for (int kb = 0; kb < C::kKB; ++kb) {
-            acc_dv[kb][db] = mfma32(dot, pf[kb], acc_dv[kb][db]);
-            acc_dk[kb][db] = mfma32(qt, dsf[kb], acc_dk[kb][db]);
+            acc_dv[kb][db] = mfma32(f.dot, pf[kb], acc_dv[kb][db]);
+            acc_dk[kb][db] = mfma32(f.qt, dsf[kb], acc_dk[kb][db]);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -555,7 +616,7 @@ hipError_t launch_attn_bwd_bf16(const AttnShape& s, const void* q, const void* k
     constexpr int HD = decltype(hd_tag)::value;
     using C = DkvCfg<HD, 4, 1, 64>;
     dim3 grid((uint32_t)((s.N + C::kBK - 1) / C::kBK), (uint32_t)(s.bs * s.hkv));
-    return launch_kernel(attn_bwd_dkv_kernel<HD, 4, 1, 64>, grid, dim3(C::kThreads), 0, stream, p);
+    return launch_kernel(attn_bwd_dkv_kernel<HD, 4, 1, 64, 2>, grid, dim3(C::kThreads), 0, stream, p);
   };
   if (s.hd == 128) {
     if ((e = dq_launch(std::integral_constant<int, 128>{})) != hipSuccess) return e;

@@ -28,7 +28,10 @@
 //    block) are never visited; per wave, tiles entirely masked for its rows
 //    are skipped; only tiles crossing a boundary apply the element mask.
 //  * LDS rows are swizzled in 16-byte chunks (swz in device_common.h) so both
-//    the row reads of K and the transposing reads of V avoid bank conflicts.
+//    the row reads of K and the transposing reads of V avoid bank conflicts;
+//    every fragment is read two products ahead of the MFMA that uses it, and
+//    consecutive MFMAs go to different accumulators, so LDS latency and MFMA
+//    dependency latency overlap the matrix work.
 //  * Blocks are launched heaviest (largest positions) first.
 #include <math.h>
 
@@ -171,17 +174,27 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdParams p) {
     const int64_t j0 = t * C::kBC;
     if (!wave_active || j0 >= w_hi || j0 + C::kBC <= w_lo) continue;
 
-    // S^T[kv][q] = K Q^T for the two 32-key halves of the tile.
+    // S^T[kv][q] = K Q^T for the two 32-key halves of the tile: the two
+    // accumulator chains alternate, and each K fragment is read from LDS two
+    // products ahead of its use.
     f32x16_t s[2];
+    s[0] = f32x16_t{};
+    s[1] = f32x16_t{};
+    {
+      constexpr int kSteps = 2 * C::kKS;   // (ks, kb) pairs, kb fastest
+      auto kfrag = [&](int idx) {
+        const int ks = idx >> 1, kb = idx & 1;
+        return *reinterpret_cast<const bf16x8_t*>(
+            lds_k + swz<C::kChunks, C::kRowBytes>(kb * 32 + r32, 2 * ks + half));
+      };
+      bf16x8_t buf[3];
+      buf[0] = kfrag(0);
+      buf[1] = kfrag(1);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16_t{};
-      const int row = kb * 32 + r32;
-#pragma unroll
-      for (int ks = 0; ks < C::kKS; ++ks) {
-        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(
-            lds_k + swz<C::kChunks, C::kRowBytes>(row, 2 * ks + half));
-        s[kb] = mfma32(kf, qf[ks], s[kb]);
+      for (int idx = 0; idx < kSteps; ++idx) {
+        if (idx + 2 < kSteps) buf[(idx + 2) % 3] = kfrag(idx + 2);
+        s[idx & 1] = mfma32(buf[idx % 3], qf[idx >> 1], s[idx & 1]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
 
@@ -231,13 +244,14 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdParams p) {
         pf[2 * kb + (i >> 3)][i & 7] = (__bf16)e;
       }
 
-    // O^T[d][q] += V^T P^T; V^T fragments via the transposing LDS read.
+    // O^T[d][q] += V^T P^T; V^T fragments via the transposing LDS read, two
+    // products ahead of their use, four independent accumulator chains.
     const int grp = lane >> 4;
     const int u = lane & 15;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-      for (int db = 0; db < C::kDB; ++db) {
+    {
+      constexpr int kSteps = 4 * C::kDB;   // (ks, db) pairs, db fastest
+      auto vfrag = [&](int idx) {
+        const int ks = idx / C::kDB, db = idx % C::kDB;
         bf16x4_t part[2];
 #pragma unroll
         for (int jh = 0; jh < 2; ++jh) {
@@ -246,8 +260,16 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdParams p) {
           const int off = swz<C::kChunks, C::kRowBytes>(row, col >> 3) + ((col >> 2) & 1) * 8;
           part[jh] = lds_read_tr16(lds_v + off);
         }
-        const bf16x8_t vf = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
-        acc_o[db] = mfma32(vf, pf[ks], acc_o[db]);
+        return __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
+      };
+      bf16x8_t buf[3];
+      buf[0] = vfrag(0);
+      buf[1] = vfrag(1);
+#pragma unroll
+      for (int idx = 0; idx < kSteps; ++idx) {
+        if (idx + 2 < kSteps) buf[(idx + 2) % 3] = vfrag(idx + 2);
+        acc_o[idx % C::kDB] = mfma32(buf[idx % 3], pf[idx / C::kDB], acc_o[idx % C::kDB]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
