@@ -75,6 +75,32 @@ __device__ __forceinline__ bf16x8_t load_tr_operand(const char* tile, int row0, 
   return __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// The same reads with the lane's offsets computed once: the swizzle depends
+// on the low four row bits only, so for row0 a multiple of 16 the address is
+// tile + row0 * kRowBytes + a per-lane offset for each (8-row half, db).
+template <int kChunks, int kRowBytes, int kDB>
+struct TrReader {
+  int off[2][kDB];
+  __device__ __forceinline__ explicit TrReader(int lane) {
+    const int grp = lane >> 4;
+    const int u = lane & 15;
+#pragma unroll
+    for (int jh = 0; jh < 2; ++jh)
+#pragma unroll
+      for (int db = 0; db < kDB; ++db) {
+        const int row = 8 * jh + 4 * (grp >> 1) + (u >> 2);
+        const int col = db * 32 + 16 * (grp & 1) + 4 * (u & 3);
+        off[jh][db] = swz<kChunks, kRowBytes>(row, col >> 3) + ((col >> 2) & 1) * 8;
+      }
+  }
+  __device__ __forceinline__ bf16x8_t load(const char* tile, int row0, int db) const {
+    const char* base = tile + row0 * kRowBytes;
+    const bf16x4_t a = lds_read_tr16(base + off[0][db]);
+    const bf16x4_t b = lds_read_tr16(base + off[1][db]);
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+};
+
 // ------------------------------------------------------------------------
 // dQ
 // ------------------------------------------------------------------------
@@ -272,49 +298,64 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_kernel(BwdParams p) {
 // ------------------------------------------------------------------------
 // dK, dV
 // ------------------------------------------------------------------------
-// A workgroup of WAVES waves owns WAVES * KB * 32 key rows of one key/value
-// head; each wave owns KB blocks of 32 rows and keeps their K fragments and
-// its dK^T, dV^T accumulators in registers.  V for the workgroup's rows stays
-// in LDS (B operand of dP = dO V^T).  The workgroup walks the visible query
-// positions in tiles of BQ, from the last tile down to the first, and within
-// a tile every query head of the GQA group; each (tile, head) step stages Q,
-// dO, LSE and D in LDS once for all its keys, and every Q or dO fragment a
-// wave reads from LDS feeds all KB of its key blocks.  Walking queries from
-// the end keeps the workgroups resident at the same time on the same query
-// tiles, so those tiles are shared through L2.  The launch uses 4 waves of
-// one 32-row block each (128 keys, one wave per SIMD): larger shapes do not
-// fit the register file without spilling.
-template <int HD, int WAVES = 4, int KB = 2, int BQ = 64>
+// dK, dV.  A workgroup of 8 waves owns 128 key rows of one key/value head as
+// 4 blocks of 32.  Each block is worked by the two waves that share a SIMD
+// (waves w and w + 4):
+//   the P wave holds the block's K rows and, for every 64-query step,
+//     computes S = Q K^T, P = exp(S - LSE) (handed over through LDS in fp32)
+//     and dV^T += dO^T P;
+//   the dS wave holds the V rows and, in the same phase, finishes the
+//     previous step (dS = P (dP - D), dK^T += Q^T dS) before computing
+//     dP = dO V^T of the current one.
+// Running the dS wave one step behind its partner leaves independent matrix
+// products in every phase for one wave while the other does exponentials or
+// dS arithmetic; one barrier per step hands P over.  Each wave carries one
+// accumulator set, so two waves fit per SIMD.
+// Steps walk the visible queries from the last 64-row tile down, over every
+// query head of the GQA group within a tile, so the GQA sum stays in
+// registers; no atomics, deterministic.  Q and dO tiles arrive by direct
+// global-to-LDS copies one step ahead; Q stays one step longer (the dS wave
+// reads Q^T a phase late), so it rotates through three buffers, and dO, LSE
+// and D through two.
+template <int HD>
 struct DkvCfg {
-  static constexpr int kWaves = WAVES;
+  static constexpr int kPairs = 4;
+  static constexpr int kWaves = 2 * kPairs;
   static constexpr int kThreads = 64 * kWaves;
-  static constexpr int kKB = KB;              // 32-row key blocks per wave
-  static constexpr int kBK = 32 * kKB * kWaves;   // key rows per workgroup
-  static constexpr int kBQ = BQ;              // query rows per step
+  static constexpr int kBK = 32 * kPairs;   // key rows per workgroup
+  static constexpr int kBQ = 64;            // query rows per step
+  static constexpr int kSubs = kBQ / 32;
+  static_assert(kSubs == 2, "the interleaved schedules take two 32-row sub-tiles per step");
   static constexpr int kChunks = HD / 8;
   static constexpr int kRowBytes = HD * 2;
-  static constexpr int kVBytes = kBK * kRowBytes;
   static constexpr int kTileBytes = kBQ * kRowBytes;
+  static constexpr int kQBufs = 3, kDoBufs = 2;
+  static constexpr int kDoOff = kQBufs * kTileBytes;
+  static constexpr int kLseOff = kDoOff + kDoBufs * kTileBytes;
+  static constexpr int kDOff = kLseOff + kDoBufs * kBQ * 4;
+  static constexpr int kPOff = kDOff + kDoBufs * kBQ * 4;
+  static constexpr int kPSub = 16 * 64 * 4;          // a 32 x 32 fp32 P tile
+  static constexpr int kPBytes = kSubs * kPSub;      // one step of one pair
+  static constexpr int kSmem = kPOff + kPairs * 2 * kPBytes;
   static constexpr int kKS = HD / 16;
   static constexpr int kDB = HD / 32;
-  static constexpr int kLoads = kBQ * kChunks / kThreads;   // per tensor per step
-  static constexpr int kVLoads = kBK * kChunks / kThreads;
-  static_assert(kLoads >= 1 && kBQ * kChunks % kThreads == 0, "tile loads");
+  // The dS waves issue the copies of the next step, one 1 KB copy per wave
+  // per tensor and part, in kParts parts spread over their work.
+  static constexpr int kParts = kTileBytes / (16 * 64 * kPairs);
+  static_assert(kParts >= 1 && kParts <= 4 && kTileBytes % (16 * 64 * kPairs) == 0, "tile copies");
+  static_assert(2 * kBQ <= 64 * kPairs, "LSE and D staging");
 };
 
-template <int HD, int WAVES, int KB, int BQ, int PF>
-__global__ __launch_bounds__(64 * WAVES) void attn_bwd_dkv_kernel(BwdParams p) {
-  using C = DkvCfg<HD, WAVES, KB, BQ>;
-  __shared__ __attribute__((aligned(16))) char smem[C::kVBytes + 2 * C::kTileBytes + 2 * C::kBQ * 4];
-  char* lds_v = smem;
-  char* lds_q = smem + C::kVBytes;
-  char* lds_do = lds_q + C::kTileBytes;
-  float* lds_lse = reinterpret_cast<float*>(lds_do + C::kTileBytes);
-  float* lds_D = lds_lse + C::kBQ;
+template <int HD, int PF>
+__global__ __launch_bounds__(512) void attn_bwd_dkv_kernel(BwdParams p) {
+  using C = DkvCfg<HD>;
+  __shared__ __attribute__((aligned(16))) char smem[C::kSmem];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pair = wave & (C::kPairs - 1);
+  const bool p_wave = wave < C::kPairs;
   const int half = lane >> 5;
   const int r32 = lane & 31;
 
@@ -322,241 +363,300 @@ __global__ __launch_bounds__(64 * WAVES) void attn_bwd_dkv_kernel(BwdParams p) {
   const int kh = blockIdx.y % p.hkv;
   const int b = blockIdx.y / p.hkv;
   const int64_t k0 = (int64_t)blockIdx.x * C::kBK;   // heaviest (smallest keys) first
-  const int64_t kw = k0 + 32 * C::kKB * wave;       // first key row of this wave
+  const int64_t kw = k0 + 32 * pair;                // first key row of this pair
+  const int64_t kj = kw + r32;                      // this lane's key row
 
   const int64_t q_tok = (int64_t)p.bs * p.hq * HD;
   const int64_t kv_tok = (int64_t)p.bs * p.hkv * HD;
   const int64_t kvoff = ((int64_t)b * p.hkv + kh) * HD;
 
-  // K rows of this lane (B operand of S = Q K^T), one per key block.
-  bf16x8_t kf[C::kKB][C::kKS];
-  int64_t my_lo[C::kKB], my_hi[C::kKB];
+  // B operand rows of this lane: K (S = Q K^T) or V (dP = dO V^T).
+  const __bf16* brows = p_wave ? p.k : p.v;
+  bf16x8_t bfrag[C::kKS];
 #pragma unroll
-  for (int kb = 0; kb < C::kKB; ++kb) {
-    const int64_t kj = kw + 32 * kb + r32;
-#pragma unroll
-    for (int ks = 0; ks < C::kKS; ++ks)
-      kf[kb][ks] = kj < N ? *reinterpret_cast<const bf16x8_t*>(p.k + kj * kv_tok + kvoff + 16 * ks + 8 * half)
-                          : bf16x8_t{};
-    // queries that see key kj: [causal ? kj : doc_start(kj), doc_end(kj))
-    my_lo[kb] = kj < N ? (p.causal ? kj : doc_start_of(p.cu, p.n_docs, kj)) : 0;
-    my_hi[kb] = kj < N ? doc_end_of(p.cu, p.n_docs, kj, N) : 0;
-  }
-  // V rows of the whole workgroup into LDS.
-#pragma unroll
-  for (int i = 0; i < C::kVLoads; ++i) {
-    const int cid = tid + i * C::kThreads;
-    const int row = cid / C::kChunks;
-    const int ch = cid % C::kChunks;
-    const int64_t j = k0 + row;
-    const u32x4_t val = j < N ? *reinterpret_cast<const u32x4_t*>(p.v + j * kv_tok + kvoff + ch * 8)
-                              : u32x4_t{};
-    *reinterpret_cast<u32x4_t*>(lds_v + swz<C::kChunks, C::kRowBytes>(row, ch)) = val;
-  }
+  for (int ks = 0; ks < C::kKS; ++ks)
+    bfrag[ks] = kj < N ? *reinterpret_cast<const bf16x8_t*>(brows + kj * kv_tok + kvoff + 16 * ks + 8 * half)
+                       : bf16x8_t{};
+  // queries that see key kj: [causal ? kj : doc_start(kj), doc_end(kj))
+  const int64_t my_lo = kj < N ? (p.causal ? kj : doc_start_of(p.cu, p.n_docs, kj)) : 0;
+  const int64_t my_hi = kj < N ? doc_end_of(p.cu, p.n_docs, kj, N) : 0;
 
+  // Workgroup- and pair-level bounds, held in scalar registers.
   const int64_t k_last = (k0 + C::kBK < N ? k0 + C::kBK : N) - 1;
-  const int64_t q_lo = p.causal ? k0 : doc_start_of(p.cu, p.n_docs, k0);
-  const int64_t q_hi = doc_end_of(p.cu, p.n_docs, k_last, N);
-  const bool wave_active = kw < N;
-  const int64_t w_last = wave_active ? (kw + 32 * C::kKB - 1 < N ? kw + 32 * C::kKB - 1 : N - 1) : 0;
-  const int64_t w_lo = wave_active ? (p.causal ? kw : doc_start_of(p.cu, p.n_docs, kw)) : 0;
-  const int64_t w_hi = wave_active ? doc_end_of(p.cu, p.n_docs, w_last, N) : 0;
-  // Queries seen by every key of the wave: [full_lo, full_hi).
-  const int64_t full_lo = wave_active ? (p.causal ? w_last : doc_start_of(p.cu, p.n_docs, w_last)) : 0;
-  const int64_t full_hi = wave_active ? doc_end_of(p.cu, p.n_docs, kw, N) : 0;
+  const int64_t q_lo = wave_uniform(p.causal ? k0 : doc_start_of(p.cu, p.n_docs, k0));
+  const int64_t q_hi = wave_uniform(doc_end_of(p.cu, p.n_docs, k_last, N));
+  const bool pair_active = kw < N;
+  const int64_t w_last = pair_active ? (kw + 31 < N ? kw + 31 : N - 1) : 0;
+  const int64_t w_lo = wave_uniform(pair_active ? (p.causal ? kw : doc_start_of(p.cu, p.n_docs, kw)) : 0);
+  const int64_t w_hi = wave_uniform(pair_active ? doc_end_of(p.cu, p.n_docs, w_last, N) : 0);
+  // Queries seen by every key of the pair: [full_lo, full_hi).
+  const int64_t full_lo =
+      wave_uniform(pair_active ? (p.causal ? w_last : doc_start_of(p.cu, p.n_docs, w_last)) : 0);
+  const int64_t full_hi = wave_uniform(pair_active ? doc_end_of(p.cu, p.n_docs, kw, N) : 0);
 
   const int64_t qt_lo = q_lo / C::kBQ;
   const int64_t qt_hi = (q_hi + C::kBQ - 1) / C::kBQ;
-  // Steps run from the last query tile down: step n is tile qt_hi-1-n/g, head n%g.
   const int64_t n_steps = (qt_hi - qt_lo) * p.g;
 
-  f32x16_t acc_dk[C::kKB][C::kDB], acc_dv[C::kKB][C::kDB];
+  // Stages step (query tile t, head kh*g + hh): Q into Q buffer qb and dO
+  // into dO buffer db by direct copies issued by the dS waves (rows past N
+  // repeat row N-1; every pair that reads them is masked), in kParts parts
+  // so that the copies interleave with matrix products instead of queueing
+  // at once; LSE (log2 units) and D through registers of the dS waves,
+  // published by publish_stats once the copies have landed.
+  const int dtid = tid - 64 * C::kPairs;   // thread index among the dS waves
+  // Tile row and source chunk of this lane's 16 bytes in each part, and
+  // their element offset within the step's rows.
+  int part_row[C::kParts];
+  int64_t part_off[C::kParts];
 #pragma unroll
-  for (int kb = 0; kb < C::kKB; ++kb)
-#pragma unroll
-    for (int db = 0; db < C::kDB; ++db) {
-      acc_dk[kb][db] = f32x16_t{};
-      acc_dv[kb][db] = f32x16_t{};
-    }
-
-  u32x4_t qst[C::kLoads], dst[C::kLoads];
+  for (int j = 0; j < C::kParts; ++j) {
+    const int piece = (j * C::kPairs + pair) * 64 + lane;
+    part_row[j] = piece / C::kChunks;
+    const int ch = (piece % C::kChunks) ^ swz_f<C::kChunks>(part_row[j]);
+    part_off[j] = part_row[j] * q_tok + ch * 8;
+  }
   float sst = 0.f;
-  auto load_step = [&](int64_t n) {
-    const int64_t i0 = (qt_hi - 1 - n / p.g) * C::kBQ;
-    const int h = kh * p.g + (int)(n % p.g);
+  auto issue_part = [&](int j, int64_t t, int hh, int qb, int db) {
+    const int h = kh * p.g + hh;
     const int64_t qoff = ((int64_t)b * p.hq + h) * HD;
-#pragma unroll
-    for (int i = 0; i < C::kLoads; ++i) {
-      const int cid = tid + i * C::kThreads;
-      const int64_t qi = i0 + cid / C::kChunks;
-      const int ch = cid % C::kChunks;
-      if (qi < N) {
-        qst[i] = *reinterpret_cast<const u32x4_t*>(p.q + qi * q_tok + qoff + ch * 8);
-        dst[i] = *reinterpret_cast<const u32x4_t*>(p.dout + qi * q_tok + qoff + ch * 8);
-      } else {
-        qst[i] = u32x4_t{};
-        dst[i] = u32x4_t{};
-      }
-    }
-    if (tid < 2 * C::kBQ) {
-      const int64_t qi = i0 + (tid % C::kBQ);
-      const int64_t idx = ((int64_t)b * p.hq + h) * N + qi;
-      sst = qi < N ? (tid < C::kBQ ? p.lse[idx] * kLog2e : p.D[idx]) : 0.f;
+    const int64_t i0 = t * C::kBQ;
+    const int slot = (j * C::kPairs + pair) * 64;   // first 16-byte slot of this copy
+    int64_t e = i0 * q_tok + qoff + part_off[j];
+    if (i0 + C::kBQ > N && i0 + part_row[j] >= N)   // last tile: repeat row N-1
+      e -= (i0 + part_row[j] - (N - 1)) * q_tok;
+    load_lds16(p.q + e, smem + qb * C::kTileBytes + slot * 16);
+    load_lds16(p.dout + e, smem + C::kDoOff + db * C::kTileBytes + slot * 16);
+    if (j == 0 && dtid >= 0 && dtid < 2 * C::kBQ) {
+      const int64_t qs = i0 + (dtid % C::kBQ);
+      const int64_t idx = ((int64_t)b * p.hq + h) * N + qs;
+      // LSE in log2 units; D negated (it seeds the dP accumulator)
+      sst = qs < N ? (dtid < C::kBQ ? p.lse[idx] * kLog2e : -p.D[idx]) : 0.f;
     }
   };
-  auto store_step = [&]() {
-#pragma unroll
-    for (int i = 0; i < C::kLoads; ++i) {
-      const int cid = tid + i * C::kThreads;
-      const int off = swz<C::kChunks, C::kRowBytes>(cid / C::kChunks, cid % C::kChunks);
-      *reinterpret_cast<u32x4_t*>(lds_q + off) = qst[i];
-      *reinterpret_cast<u32x4_t*>(lds_do + off) = dst[i];
-    }
-    if (tid < 2 * C::kBQ) lds_lse[tid] = sst;   // lds_D follows lds_lse
+  auto publish_stats = [&](int qb, int db) {
+    if (dtid >= 0 && dtid < C::kBQ)
+      reinterpret_cast<float*>(smem + C::kLseOff)[db * C::kBQ + dtid] = sst;
+    else if (dtid >= C::kBQ && dtid < 2 * C::kBQ)
+      reinterpret_cast<float*>(smem + C::kDOff)[db * C::kBQ + dtid - C::kBQ] = sst;
   };
 
-  if (n_steps > 0) load_step(0);
-  for (int64_t n = 0; n < n_steps; ++n) {
-    __syncthreads();
-    store_step();
-    __syncthreads();
-    if (n + 1 < n_steps) load_step(n + 1);
-    const int64_t i0 = (qt_hi - 1 - n / p.g) * C::kBQ;
-    if (!wave_active || i0 >= w_hi || i0 + C::kBQ <= w_lo) continue;
+  const TrReader<C::kChunks, C::kRowBytes, C::kDB> tr(lane);
 
-#pragma unroll 1
-    for (int sub = 0; sub < C::kBQ / 32; ++sub) {
-      const int64_t s0 = i0 + 32 * sub;
-      if (s0 >= w_hi || s0 + 32 <= w_lo) continue;
-      const bool need_mask = s0 < full_lo || s0 + 32 > full_hi;
-      // S = Q K^T and dP = dO V^T for every key block: lane holds key
-      // kw + 32 kb + lane%32 and 16 query rows.  The Q, dO and V fragments of
-      // each k-step are read from LDS PF steps ahead of their products.
-      f32x16_t s[C::kKB], dp[C::kKB];
+  if (n_steps > 0 && !p_wave) {
 #pragma unroll
-      for (int kb = 0; kb < C::kKB; ++kb) {
-        s[kb] = f32x16_t{};
-        dp[kb] = f32x16_t{};
-      }
-      {
-        struct Frags {
-          bf16x8_t qa, da, vb[C::kKB];
-        };
-        auto frags = [&](int ks) {
-          Frags f;
-          const int off = swz<C::kChunks, C::kRowBytes>(32 * sub + r32, 2 * ks + half);
-          f.qa = *reinterpret_cast<const bf16x8_t*>(lds_q + off);
-          f.da = *reinterpret_cast<const bf16x8_t*>(lds_do + off);
+    for (int j = 0; j < C::kParts; ++j) issue_part(j, qt_hi - 1, 0, 0, 0);
+    wait_vmem();
+    publish_stats(0, 0);
+  }
+  __syncthreads();
+
+  // The step loop, instantiated once per role so that each role's
+  // accumulators stay in place; both instances pass the same barriers.
+  auto run = [&](auto role) {
+    constexpr bool kP = decltype(role)::value;
+    f32x16_t acc[C::kDB];   // dV^T (P waves) or dK^T (dS waves)
 #pragma unroll
-          for (int kb = 0; kb < C::kKB; ++kb)
-            f.vb[kb] = *reinterpret_cast<const bf16x8_t*>(
-                lds_v + swz<C::kChunks, C::kRowBytes>(32 * (C::kKB * wave + kb) + r32, 2 * ks + half));
-          return f;
-        };
-        Frags buf[PF + 1];
+    for (int db = 0; db < C::kDB; ++db) acc[db] = f32x16_t{};
+    f32x16_t dp_prev[C::kSubs];   // dS waves: dP - D of the previous step
 #pragma unroll
-        for (int i = 0; i < PF; ++i) buf[i] = frags(i);
-#pragma unroll
-        for (int ks = 0; ks < C::kKS; ++ks) {
-          if (ks + PF < C::kKS) buf[(ks + PF) % (PF + 1)] = frags(ks + PF);
-          const Frags& f = buf[ks % (PF + 1)];
-#pragma unroll
-          for (int kb = 0; kb < C::kKB; ++kb) {
-            s[kb] = mfma32(f.qa, kf[kb][ks], s[kb]);
-            dp[kb] = mfma32(f.da, f.vb[kb], dp[kb]);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-      // On sub-tiles that cross a boundary, scores of invisible (query, key)
-      // pairs become -inf, so their P and dS are exactly 0.
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < C::kKB; ++kb) {
-          // visible queries of this key as offsets into the 32-row sub-tile
-          const int lo = (int)(my_lo[kb] - s0 < -1 ? -1 : (my_lo[kb] - s0 > 33 ? 33 : my_lo[kb] - s0));
-          const int hi = (int)(my_hi[kb] - s0 < -1 ? -1 : (my_hi[kb] - s0 > 33 ? 33 : my_hi[kb] - s0));
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int qr = 8 * (i >> 2) + 4 * half + (i & 3);
-            if (qr < lo || qr >= hi) s[kb][i] = -INFINITY;
-          }
-        }
-      }
-      // dO^T and Q^T fragments (transposing LDS reads) for the (16-row step,
-      // head-dim block) products, read PF products ahead.
-      struct TrFrags {
-        bf16x8_t dot, qt;
+    for (int sub = 0; sub < C::kSubs; ++sub) dp_prev[sub] = f32x16_t{};
+
+    int64_t t = qt_hi - 1;
+    int hh = 0, qb = 0, db = 0;
+    bool prev_vis = false;
+    int prev_qb = 0;
+    for (int64_t n = 0; n <= n_steps; ++n) {
+      const bool cur = n < n_steps;
+      const bool has_next = n + 1 < n_steps;
+      const int nqb = qb == C::kQBufs - 1 ? 0 : qb + 1;
+      const int ndb = db ^ 1;
+      const int64_t nt = hh + 1 < p.g ? t : t - 1;
+      const int nhh = hh + 1 < p.g ? hh + 1 : 0;
+      // dS waves: part i of the next step's copies goes out at point i.
+      auto issue_at = [&](int i) {
+        if (!kP && has_next && i < C::kParts) issue_part(i, nt, nhh, nqb, ndb);
       };
-      constexpr int kTrSteps = 2 * C::kDB;
-      auto trfrags = [&](int idx) {
-        TrFrags f;
-        const int ks2 = idx / C::kDB, db = idx % C::kDB;
-        f.dot = load_tr_operand<C::kChunks, C::kRowBytes>(lds_do, 32 * sub + 16 * ks2, db, lane);
-        f.qt = load_tr_operand<C::kChunks, C::kRowBytes>(lds_q, 32 * sub + 16 * ks2, db, lane);
-        return f;
-      };
-      TrFrags tbuf[PF + 1];
+      const int64_t i0 = t * C::kBQ;
+      const bool vis = cur && pair_active && i0 < w_hi && i0 + C::kBQ > w_lo;
+      const char* tq = smem + qb * C::kTileBytes;
+      const char* tdo = smem + C::kDoOff + db * C::kTileBytes;
+      char* pbuf = smem + C::kPOff + (2 * pair + (int)(n & 1)) * C::kPBytes;
+
+      if constexpr (kP) {
+        if (vis) {
+          const float* tlse = reinterpret_cast<const float*>(smem + C::kLseOff) + db * C::kBQ;
+          // S = Q K^T for both 32-row sub-tiles: lane holds key kj and 16
+          // query rows of each.
+          f32x16_t s[C::kSubs];
 #pragma unroll
-      for (int i = 0; i < PF; ++i) tbuf[i] = trfrags(i);
-      // P and dS for 16 query rows at a time (B operands), then
-      // dV^T += dO^T P and dK^T += Q^T dS over those rows.
+          for (int sub = 0; sub < C::kSubs; ++sub) s[sub] = f32x16_t{};
+          {
+            // A fragments read PF products ahead, over both sub-tiles.
+            constexpr int kN = C::kSubs * C::kKS;
+            auto afrag = [&](int i) {
+              return *reinterpret_cast<const bf16x8_t*>(
+                  tq + swz<C::kChunks, C::kRowBytes>(32 * (i / C::kKS) + r32, 2 * (i % C::kKS) + half));
+            };
+            bf16x8_t buf[PF + 1];
 #pragma unroll
-      for (int ks2 = 0; ks2 < 2; ++ks2) {
-        bf16x8_t pf[C::kKB], dsf[C::kKB];
+            for (int i = 0; i < PF; ++i) buf[i] = afrag(i);
 #pragma unroll
-        for (int r2 = 0; r2 < 2; ++r2) {
-          const int r4 = 2 * ks2 + r2;
-          const int qr0 = 32 * sub + 8 * r4 + 4 * half;
-          const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(lds_lse + qr0);
-          const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(lds_D + qr0);
-#pragma unroll
-          for (int kb = 0; kb < C::kKB; ++kb)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int i = 4 * r4 + e;
-              const float pv = __builtin_amdgcn_exp2f(fmaf(s[kb][i], p.scale_log2, -l4[e]));
-              pf[kb][4 * r2 + e] = (__bf16)pv;
-              dsf[kb][4 * r2 + e] = (__bf16)(pv * (dp[kb][i] - d4[e]));
+            for (int i = 0; i < kN; ++i) {
+              if (i + PF < kN) buf[(i + PF) % (PF + 1)] = afrag(i + PF);
+              s[i / C::kKS] = mfma32(buf[i % (PF + 1)], bfrag[i % C::kKS], s[i / C::kKS]);
+              __builtin_amdgcn_sched_barrier(0);
             }
-        }
-#pragma unroll
-        for (int db = 0; db < C::kDB; ++db) {
-          const int idx = ks2 * C::kDB + db;
-          if (idx + PF < kTrSteps) tbuf[(idx + PF) % (PF + 1)] = trfrags(idx + PF);
-          const TrFrags& f = tbuf[idx % (PF + 1)];
-#pragma unroll
-          for (int kb = 0; kb < C::kKB; ++kb) {
-            acc_dv[kb][db] = mfma32(f.dot, pf[kb], acc_dv[kb][db]);
-            acc_dk[kb][db] = mfma32(f.qt, dsf[kb], acc_dk[kb][db]);
           }
-          __builtin_amdgcn_sched_barrier(0);
+          bf16x8_t pf[C::kSubs][2];
+#pragma unroll
+          for (int sub = 0; sub < C::kSubs; ++sub) {
+            const int64_t s0 = i0 + 32 * sub;
+            // On sub-tiles that cross a boundary (or that this pair does
+            // not see at all), scores of invisible (query, key) pairs become
+            // -inf, so their P is exactly 0.
+            if (s0 < full_lo || s0 + 32 > full_hi) {
+              const int lo = (int)(my_lo - s0 < -1 ? -1 : (my_lo - s0 > 33 ? 33 : my_lo - s0));
+              const int hi = (int)(my_hi - s0 < -1 ? -1 : (my_hi - s0 > 33 ? 33 : my_hi - s0));
+#pragma unroll
+              for (int i = 0; i < 16; ++i) {
+                const int qr = 8 * (i >> 2) + 4 * half + (i & 3);
+                if (qr < lo || qr >= hi) s[sub][i] = -INFINITY;
+              }
+            }
+            float* pt = reinterpret_cast<float*>(pbuf + sub * C::kPSub);
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+              const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(tlse + 32 * sub + 8 * r4 + 4 * half);
+              f32x4_t p4;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                p4[e] = __builtin_amdgcn_exp2f(fmaf(s[sub][4 * r4 + e], p.scale_log2, -l4[e]));
+                pf[sub][r4 >> 1][4 * (r4 & 1) + e] = (__bf16)p4[e];
+              }
+              *reinterpret_cast<f32x4_t*>(pt + 4 * (64 * r4 + lane)) = p4;
+            }
+            // dV^T += dO^T P over the sub-tile's two 16-row steps, the
+            // transposed A fragments read PF products ahead.
+            {
+              constexpr int kN = 2 * C::kDB;
+              auto tfrag = [&](int i) { return tr.load(tdo, 32 * sub + 16 * (i / C::kDB), i % C::kDB); };
+              bf16x8_t buf[PF + 1];
+#pragma unroll
+              for (int i = 0; i < PF; ++i) buf[i] = tfrag(i);
+#pragma unroll
+              for (int i = 0; i < kN; ++i) {
+                if (i + PF < kN) buf[(i + PF) % (PF + 1)] = tfrag(i + PF);
+                acc[i % C::kDB] = mfma32(buf[i % (PF + 1)], pf[sub][i / C::kDB], acc[i % C::kDB]);
+                __builtin_amdgcn_sched_barrier(0);
+              }
+            }
+          }
         }
+      } else {
+        // Finish the previous step, one sub-tile at a time:
+        // dS = P (dP - D), dK^T += Q^T dS; the next step's copies go out
+        // between the stages.
+        issue_at(0);
+        const char* pq = smem + prev_qb * C::kTileBytes;
+        const char* ppbuf = smem + C::kPOff + (2 * pair + (int)((n - 1) & 1)) * C::kPBytes;
+#pragma unroll
+        for (int sub = 0; sub < C::kSubs; ++sub) {
+          if (prev_vis) {
+            const float* pt = reinterpret_cast<const float*>(ppbuf + sub * C::kPSub);
+            bf16x8_t dsf[2];
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+              const f32x4_t p4 = *reinterpret_cast<const f32x4_t*>(pt + 4 * (64 * r4 + lane));
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                dsf[r4 >> 1][4 * (r4 & 1) + e] = (__bf16)(p4[e] * dp_prev[sub][4 * r4 + e]);
+            }
+            {
+              constexpr int kN = 2 * C::kDB;
+              auto tfrag = [&](int i) { return tr.load(pq, 32 * sub + 16 * (i / C::kDB), i % C::kDB); };
+              bf16x8_t buf[PF + 1];
+#pragma unroll
+              for (int i = 0; i < PF; ++i) buf[i] = tfrag(i);
+#pragma unroll
+              for (int i = 0; i < kN; ++i) {
+                if (i + PF < kN) buf[(i + PF) % (PF + 1)] = tfrag(i + PF);
+                acc[i % C::kDB] = mfma32(buf[i % (PF + 1)], dsf[i / C::kDB], acc[i % C::kDB]);
+                __builtin_amdgcn_sched_barrier(0);
+              }
+            }
+          }
+          issue_at(1 + sub);
+        }
+        issue_at(3);
+        // dP - D = dO V^T - D for both sub-tiles (the accumulators start at
+        // -D), finished in the next phase; A fragments read PF products
+        // ahead.
+        if (vis) {
+          const float* tnd = reinterpret_cast<const float*>(smem + C::kDOff) + db * C::kBQ;
+          constexpr int kN = C::kSubs * C::kKS;
+          auto afrag = [&](int i) {
+            return *reinterpret_cast<const bf16x8_t*>(
+                tdo + swz<C::kChunks, C::kRowBytes>(32 * (i / C::kKS) + r32, 2 * (i % C::kKS) + half));
+          };
+#pragma unroll
+          for (int sub = 0; sub < C::kSubs; ++sub)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+              const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(tnd + 32 * sub + 8 * r4 + 4 * half);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) dp_prev[sub][4 * r4 + e] = d4[e];
+            }
+          bf16x8_t buf[PF + 1];
+#pragma unroll
+          for (int i = 0; i < PF; ++i) buf[i] = afrag(i);
+#pragma unroll
+          for (int i = 0; i < kN; ++i) {
+            if (i + PF < kN) buf[(i + PF) % (PF + 1)] = afrag(i + PF);
+            dp_prev[i / C::kKS] = mfma32(buf[i % (PF + 1)], bfrag[i % C::kKS], dp_prev[i / C::kKS]);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
+
+      if (has_next && !kP) {
+        wait_vmem();   // this wave's copies of the next step have landed
+        publish_stats(nqb, ndb);
+      }
+      __syncthreads();
+
+      prev_vis = vis;
+      prev_qb = qb;
+      qb = nqb;
+      db = ndb;
+      if (++hh == p.g) {
+        hh = 0;
+        --t;
       }
     }
-  }
 
+    if (kj < N) {
+      __bf16* row = (kP ? p.dv : p.dk) + kj * kv_tok + kvoff;
+      const float mul = kP ? 1.f : p.scale;
 #pragma unroll
-  for (int kb = 0; kb < C::kKB; ++kb) {
-    const int64_t kj = kw + 32 * kb + r32;
-    if (kj >= N) continue;
-    __bf16* dkrow = p.dk + kj * kv_tok + kvoff;
-    __bf16* dvrow = p.dv + kj * kv_tok + kvoff;
+      for (int d = 0; d < C::kDB; ++d)
 #pragma unroll
-    for (int db = 0; db < C::kDB; ++db)
+        for (int r4 = 0; r4 < 4; ++r4) {
+          bf16x4_t w;
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        bf16x4_t wk, wv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          wk[e] = (__bf16)(acc_dk[kb][db][4 * r4 + e] * p.scale);
-          wv[e] = (__bf16)acc_dv[kb][db][4 * r4 + e];
+          for (int e = 0; e < 4; ++e) w[e] = (__bf16)(acc[d][4 * r4 + e] * mul);
+          *reinterpret_cast<bf16x4_t*>(row + d * 32 + 8 * r4 + 4 * half) = w;
         }
-        *reinterpret_cast<bf16x4_t*>(dkrow + db * 32 + 8 * r4 + 4 * half) = wk;
-        *reinterpret_cast<bf16x4_t*>(dvrow + db * 32 + 8 * r4 + 4 * half) = wv;
-      }
-  }
+    }
+  };
+  if (p_wave)
+    run(std::true_type{});
+  else
+    run(std::false_type{});
 }
+
+// LDS fragments read this many products ahead in the dK/dV kernel.
+constexpr int kDkvPrefetch = 3;
 
 template <int HD, int GPACK>
 hipError_t launch_dq(BwdParams p, const AttnShape& s, hipStream_t stream) {
@@ -614,9 +714,9 @@ hipError_t launch_attn_bwd_bf16(const AttnShape& s, const void* q, const void* k
   };
   auto dkv_launch = [&](auto hd_tag) -> hipError_t {
     constexpr int HD = decltype(hd_tag)::value;
-    using C = DkvCfg<HD, 4, 1, 64>;
+    using C = DkvCfg<HD>;
     dim3 grid((uint32_t)((s.N + C::kBK - 1) / C::kBK), (uint32_t)(s.bs * s.hkv));
-    return launch_kernel(attn_bwd_dkv_kernel<HD, 4, 1, 64, 2>, grid, dim3(C::kThreads), 0, stream, p);
+    return launch_kernel(attn_bwd_dkv_kernel<HD, kDkvPrefetch>, grid, dim3(C::kThreads), 0, stream, p);
   };
   if (s.hd == 128) {
     if ((e = dq_launch(std::integral_constant<int, 128>{})) != hipSuccess) return e;

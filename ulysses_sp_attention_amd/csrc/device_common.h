@@ -54,14 +54,33 @@ __device__ __forceinline__ float wave_shfl_xor32(float x) {
 // (so the transposing reads, which take 4 rows x 4 chunks per 16 or 32
 // lanes, also hit distinct bank groups).  For 8-chunk rows the same holds
 // with 8 values.
+template <int kChunks>
+__device__ __forceinline__ int swz_f(int row) {
+  if constexpr (kChunks == 16)
+    return ((row & 3) << 2) | ((row >> 2) & 3);
+  else
+    return ((row & 1) << 2) | ((row >> 1) & 3);
+}
 template <int kChunks, int kRowBytes>
 __device__ __forceinline__ int swz(int row, int ch) {
-  int f;
-  if constexpr (kChunks == 16)
-    f = ((row & 3) << 2) | ((row >> 2) & 3);
-  else
-    f = ((row & 1) << 2) | ((row >> 1) & 3);
-  return row * kRowBytes + ((ch ^ f) << 4);
+  return row * kRowBytes + ((ch ^ swz_f<kChunks>(row)) << 4);
+}
+
+// Direct global-to-LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
+// lane l's 16 bytes from `src` land at lds_dst + 16 l, where lds_dst must be
+// the same for the whole wave.  Completion is tracked by the vector memory
+// counter only, so the reader waits with wait_vmem() before a barrier.
+__device__ __forceinline__ void load_lds16(const void* src, void* lds_dst) {
+  __builtin_amdgcn_global_load_lds(src, (ULY_LDS void*)lds_dst, 16, 0, 0);
+}
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// A value the whole wave agrees on, moved to scalar registers so that
+// branches on it stay scalar branches.
+__device__ __forceinline__ int64_t wave_uniform(int64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
 __device__ __forceinline__ bool wave_any(bool pred) {
