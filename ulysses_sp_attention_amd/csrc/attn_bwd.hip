@@ -75,32 +75,6 @@ __device__ __forceinline__ bf16x8_t load_tr_operand(const char* tile, int row0, 
   return __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// The same reads with the lane's offsets computed once: the swizzle depends
-// on the low four row bits only, so for row0 a multiple of 16 the address is
-// tile + row0 * kRowBytes + a per-lane offset for each (8-row half, db).
-template <int kChunks, int kRowBytes, int kDB>
-struct TrReader {
-  int off[2][kDB];
-  __device__ __forceinline__ explicit TrReader(int lane) {
-    const int grp = lane >> 4;
-    const int u = lane & 15;
-#pragma unroll
-    for (int jh = 0; jh < 2; ++jh)
-#pragma unroll
-      for (int db = 0; db < kDB; ++db) {
-        const int row = 8 * jh + 4 * (grp >> 1) + (u >> 2);
-        const int col = db * 32 + 16 * (grp & 1) + 4 * (u & 3);
-        off[jh][db] = swz<kChunks, kRowBytes>(row, col >> 3) + ((col >> 2) & 1) * 8;
-      }
-  }
-  __device__ __forceinline__ bf16x8_t load(const char* tile, int row0, int db) const {
-    const char* base = tile + row0 * kRowBytes;
-    const bf16x4_t a = lds_read_tr16(base + off[0][db]);
-    const bf16x4_t b = lds_read_tr16(base + off[1][db]);
-    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-  }
-};
-
 // ------------------------------------------------------------------------
 // dQ
 // ------------------------------------------------------------------------

@@ -75,6 +75,36 @@ __device__ __forceinline__ void load_lds16(const void* src, void* lds_dst) {
 }
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// A operand of v_mfma_f32_32x32x16_bf16 (rows = head dim, k = 16 sequence
+// positions from row0) read transposed, with ds_read_b64_tr_b16, from a
+// row-major swizzled LDS tile: lane l gets column d = 32*db + l%32 at the 8
+// sequence rows that match the accumulator layout of the other operand.  The
+// swizzle depends on the low four row bits only, so for row0 a multiple of 16
+// the address is tile + row0 * kRowBytes + a per-lane offset for each (8-row
+// half, db), computed once.
+template <int kChunks, int kRowBytes, int kDB>
+struct TrReader {
+  int off[2][kDB];
+  __device__ __forceinline__ explicit TrReader(int lane) {
+    const int grp = lane >> 4;
+    const int u = lane & 15;
+#pragma unroll
+    for (int jh = 0; jh < 2; ++jh)
+#pragma unroll
+      for (int db = 0; db < kDB; ++db) {
+        const int row = 8 * jh + 4 * (grp >> 1) + (u >> 2);
+        const int col = db * 32 + 16 * (grp & 1) + 4 * (u & 3);
+        off[jh][db] = swz<kChunks, kRowBytes>(row, col >> 3) + ((col >> 2) & 1) * 8;
+      }
+  }
+  __device__ __forceinline__ bf16x8_t load(const char* tile, int row0, int db) const {
+    const char* base = tile + row0 * kRowBytes;
+    const bf16x4_t a = lds_read_tr16(base + off[0][db]);
+    const bf16x4_t b = lds_read_tr16(base + off[1][db]);
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+};
+
 // A value the whole wave agrees on, moved to scalar registers so that
 // branches on it stay scalar branches.
 __device__ __forceinline__ int64_t wave_uniform(int64_t x) {
