@@ -4,12 +4,12 @@
 One step is the whole rank-share path over one batch of synthetic input,
 inputs already resident in HBM:
 
-  forward : seq_to_head(Q), seq_to_head(K), seq_to_head(V)   (8 chunks each)
+  forward : seq_to_head of Q, K and V in one batched launch   (8 chunks each)
             attention forward (O, LSE)
             head_to_seq(O)
   backward: seq_to_head(dO)
             attention backward (dQ, dK, dV)
-            head_to_seq(dQ), head_to_seq(dK), head_to_seq(dV)
+            head_to_seq of dQ, dK and dV in one batched launch
 
 Workload: the Llama-8B-shaped rank share at P=8 and N=131072 (32 query /
 8 key-value heads globally, so 4 query heads and 1 key/value head per rank,
@@ -142,9 +142,7 @@ def main():
             if ev is not None:
                 ev[i].record(stream)
         mark(0)
-        uly.ulysses_seq_to_head(cq, r, q)
-        uly.ulysses_seq_to_head(ck, r, k)
-        uly.ulysses_seq_to_head(cv, r, v)
+        uly.ulysses_seq_to_head_batch([(cq, q), (ck, k), (cv, v)], r)
         mark(1)
         uly.ulysses_attn_fwd(q, k, v, o, lse, scale, True)
         mark(2)
@@ -154,9 +152,7 @@ def main():
         mark(4)
         uly.ulysses_attn_bwd(q, k, v, o, lse, do, dq, dk, dv, ws, scale, True)
         mark(5)
-        uly.ulysses_head_to_seq(dq, r, cdq)
-        uly.ulysses_head_to_seq(dk, r, cdk)
-        uly.ulysses_head_to_seq(dv, r, cdv)
+        uly.ulysses_head_to_seq_batch([(dq, cdq), (dk, cdk), (dv, cdv)], r)
         mark(6)
 
     if args.calibrate_copy:

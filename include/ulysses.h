@@ -14,6 +14,8 @@
  *   ulysses_seq_to_head  -- assemble the P sequence chunks into the rank's
  *                           full-sequence, head-sliced buffer
  *   ulysses_head_to_seq  -- its inverse
+ *   ulysses_seq_to_head_batch, ulysses_head_to_seq_batch
+ *                        -- the same for up to four tensors in one launch
  *   ulysses_attn_fwd     -- causal (GQA, optionally document-masked)
  *                           softmax attention, returning O and the LSE
  *   ulysses_attn_bwd     -- its backward pass (dQ, dK, dV)
@@ -48,7 +50,7 @@
 extern "C" {
 #endif
 
-#define ULYSSES_ABI_VERSION 1
+#define ULYSSES_ABI_VERSION 2
 
 typedef enum {
   ULYSSES_OK = 0,
@@ -112,6 +114,44 @@ ulysses_status_t ulysses_seq_to_head(const void* const* chunks, int P, int rank,
 ulysses_status_t ulysses_head_to_seq(const void* in, int P, int rank, int64_t n_local, int bs,
                                      int heads, int head_dim, ulysses_dtype_t dtype,
                                      void* const* chunks, hipStream_t stream);
+
+/*
+ * Up to ULYSSES_MAX_BATCH exchanges of one layer in a single launch (the
+ * Ulysses all-to-all moves the query, key and value projections together,
+ * and the gradients back; Hugging Face Ulysses blog, "The challenge of
+ * long-sequence training").  Tensor i behaves exactly as the single-tensor
+ * call with its own head count; P, rank, n_local, bs, head_dim and dtype are
+ * shared.  One launch instead of several saves the launch and tail time of
+ * the small key/value tensors.
+ */
+#define ULYSSES_MAX_BATCH 4
+
+typedef struct {
+  void* const* chunks; /* host array of P device pointers, chunk c [n_local, bs, heads,
+                          head_dim]: read by ulysses_seq_to_head_batch; only this rank's
+                          head slots written by ulysses_head_to_seq_batch */
+  void* head;          /* device [P*n_local, bs, heads_l, head_dim]: written by
+                          ulysses_seq_to_head_batch, read by ulysses_head_to_seq_batch */
+  int heads;           /* this tensor's global head count */
+} ulysses_exchange_tensor_t;
+
+/*
+ *   tensors    host array of n_tensors descriptors (read during the call only)
+ *   n_tensors  1 .. ULYSSES_MAX_BATCH (ERR_SHAPE otherwise; ERR_NULL if
+ *              tensors is NULL)
+ *   Every descriptor is checked as the single-tensor call checks its
+ *   arguments, in order, before anything is launched; the first failing
+ *   status is returned.  Outputs of different tensors must not overlap each
+ *   other or any input.  n_local == 0 is a no-op.
+ */
+ulysses_status_t ulysses_seq_to_head_batch(const ulysses_exchange_tensor_t* tensors,
+                                           int n_tensors, int P, int rank, int64_t n_local,
+                                           int bs, int head_dim, ulysses_dtype_t dtype,
+                                           hipStream_t stream);
+ulysses_status_t ulysses_head_to_seq_batch(const ulysses_exchange_tensor_t* tensors,
+                                           int n_tensors, int P, int rank, int64_t n_local,
+                                           int bs, int head_dim, ulysses_dtype_t dtype,
+                                           hipStream_t stream);
 
 /*
  * Local attention over the full sequence for this rank's heads (Hugging

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert uly.ulysses_abi_version() == 1
+    assert uly.ulysses_abi_version() == uly.ABI_VERSION
     for code in range(9):
         s = uly.ulysses_status_string(code)
         assert s and s != "unknown status"
@@ -132,3 +132,44 @@ def test_binding_raises_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(uly, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
         uly.load_library(str(tmp_path / "missing.so"))
+
+
+def batch_descs(specs):
+    """specs: [(chunk table key or None, head pointer, heads)] -> ctypes array + keep-alive."""
+    table = {"ok": [FAKE, FAKE + 4096], "ok8": [FAKE + 4096 * i for i in range(8)],
+             "bad": [FAKE, MISALIGNED], "null": [FAKE, None]}
+    descs = (uly.ExchangeTensor * max(1, len(specs)))()
+    keep = []
+    for i, (key, head, heads) in enumerate(specs):
+        arr = None if key is None else chunk_array(table[key])
+        keep.append(arr)
+        descs[i].chunks = None if arr is None else ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
+        descs[i].head = head
+        descs[i].heads = heads
+    return descs, keep
+
+
+@pytest.mark.parametrize("specs,n,n_local,want", [
+    # every failing case is rejected before any launch
+    ([("ok", FAKE, 4)], 0, 4, uly.ERR_SHAPE),
+    ([("ok", FAKE, 4)] * 4, 5, 4, uly.ERR_SHAPE),
+    ([("ok", FAKE, 4), ("ok", FAKE + 65536, 3)], 2, 4, uly.ERR_DIVISIBILITY),
+    ([("ok", FAKE, 4), (None, FAKE + 65536, 4)], 2, 4, uly.ERR_NULL),
+    ([("ok", FAKE, 4), ("null", FAKE + 65536, 4)], 2, 4, uly.ERR_NULL),
+    ([("ok", FAKE, 4), ("ok", MISALIGNED, 4)], 2, 4, uly.ERR_ALIGNMENT),
+    ([("bad", FAKE, 4), ("ok", FAKE + 65536, 4)], 2, 4, uly.ERR_ALIGNMENT),
+    ([("ok", FAKE, 4), ("ok", None, 4)], 2, 4, uly.ERR_NULL),
+    ([("ok", FAKE, 4), ("ok", FAKE + 65536, 2)], 2, 0, uly.OK),   # empty: no launch
+])
+def test_batch_exchange_validation(lib, specs, n, n_local, want):
+    descs, keep = batch_descs(specs)
+    for fn in (lib.ulysses_seq_to_head_batch, lib.ulysses_head_to_seq_batch):
+        assert fn(descs, n, 2, 0, n_local, 1, 64, uly.FP32, None) == want
+
+
+def test_batch_exchange_null_table_and_head_to_seq_divisibility(lib):
+    assert lib.ulysses_seq_to_head_batch(None, 1, 2, 0, 4, 1, 64, uly.FP32, None) == uly.ERR_NULL
+    # replicated key/value heads (heads < P) are fine for seq_to_head, not for head_to_seq
+    descs, keep = batch_descs([("ok8", FAKE, 8), ("ok8", FAKE + 65536, 2)])
+    assert lib.ulysses_head_to_seq_batch(descs, 2, 8, 0, 4, 1, 128, uly.BF16, None) == \
+        uly.ERR_DIVISIBILITY

@@ -108,3 +108,52 @@ def test_full_size_pack_unpack_bit_exact(name):
                 assert np.array_equal(host_storage(dev_chunks[c]), want_chunks[c]), f"chunk {c}"
             del dev_chunks
         torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("P,n,bs,hd,heads_list,dtype", [
+    (8, 64, 1, 128, (32, 8, 8), "bf16"),        # one layer's Q, K, V at the Llama-8B shape
+    (8, 33, 2, 128, (32, 2, 2, 32), "bf16"),    # replicated key/value heads, ragged n, four tensors
+    (2, 40, 1, 64, (4, 2), "f32"),
+])
+def test_batched_seq_to_head_matches_oracle_per_tensor(P, n, bs, hd, heads_list, dtype):
+    import torch
+    import ulysses_sp_attention_amd as uly
+    fulls = [synth.normal(90 + i, 1, (P * n, bs, h, hd), dtype=dtype) for i, h in enumerate(heads_list)]
+    chunk_sets = [[np.ascontiguousarray(f[c * n:(c + 1) * n]) for c in range(P)] for f in fulls]
+    for rank in range(P):
+        pairs = []
+        for chunks, h in zip(chunk_sets, heads_list):
+            dev = [to_device(c, dtype) for c in chunks]
+            hl = h // P if h >= P else 1
+            out = torch.full((P * n, bs, hl, hd), float("nan"), dtype=dev[0].dtype, device="cuda")
+            pairs.append((dev, out))
+        uly.ulysses_seq_to_head_batch(pairs, rank)
+        torch.cuda.synchronize()
+        for i, (chunks, (_, out)) in enumerate(zip(chunk_sets, pairs)):
+            want = oracle.seq_to_head(chunks, rank)
+            assert storage_bytes(out) == want.tobytes(), f"rank {rank} tensor {i}"
+
+
+@pytest.mark.parametrize("P,n,bs,hd,heads_list,dtype", [
+    (8, 64, 1, 128, (32, 8, 8), "bf16"),        # dQ, dK, dV of one layer
+    (4, 17, 3, 64, (4, 8), "bf16"),
+])
+def test_batched_head_to_seq_matches_oracle_and_leaves_other_slots(P, n, bs, hd, heads_list, dtype):
+    import torch
+    import ulysses_sp_attention_amd as uly
+    for rank in range(P):
+        pairs, expect = [], []
+        for i, h in enumerate(heads_list):
+            hl = h // P
+            canary = synth.normal(95 + i, 2, (n, bs, h, hd), dtype=dtype)
+            x = synth.normal(96 + i, 3 + rank, (P * n, bs, hl, hd), dtype=dtype)
+            dev_chunks = [to_device(canary, dtype) for _ in range(P)]
+            pairs.append((to_device(x, dtype), dev_chunks))
+            want = [canary.copy() for _ in range(P)]
+            oracle.head_to_seq(x, want, rank)
+            expect.append(want)
+        uly.ulysses_head_to_seq_batch(pairs, rank)
+        torch.cuda.synchronize()
+        for i, ((_, dev_chunks), want) in enumerate(zip(pairs, expect)):
+            for c in range(P):
+                assert storage_bytes(dev_chunks[c]) == want[c].tobytes(), f"rank {rank} tensor {i} chunk {c}"

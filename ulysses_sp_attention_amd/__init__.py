@@ -21,13 +21,22 @@ LIB_PATH = os.path.join(_PKG, "libulysses.so")
 OK, ERR_NULL, ERR_SHAPE, ERR_DIVISIBILITY, ERR_DTYPE, ERR_ALIGNMENT, ERR_UNSUPPORTED, \
     ERR_WORKSPACE, ERR_HIP = range(9)
 BF16, FP32 = 0, 1
+ABI_VERSION = 2   # ULYSSES_ABI_VERSION this binding is written for
 _INVALID_DTYPE = 99
 
 # Every symbol include/ulysses.h declares.
 EXPORTED_SYMBOLS = (
     "ulysses_abi_version", "ulysses_status_string", "ulysses_seq_to_head", "ulysses_head_to_seq",
+    "ulysses_seq_to_head_batch", "ulysses_head_to_seq_batch",
     "ulysses_attn_fwd", "ulysses_attn_bwd_workspace_size", "ulysses_attn_bwd",
 )
+MAX_BATCH = 4   # ULYSSES_MAX_BATCH
+
+
+class ExchangeTensor(ctypes.Structure):
+    """ulysses_exchange_tensor_t: P chunk pointers, the head buffer, global heads."""
+    _fields_ = [("chunks", ctypes.POINTER(ctypes.c_void_p)), ("head", ctypes.c_void_p),
+                ("heads", ctypes.c_int)]
 
 
 class UlyssesError(RuntimeError):
@@ -63,6 +72,9 @@ def load_library(path: str = LIB_PATH):
     lib.ulysses_seq_to_head.restype = ci
     lib.ulysses_head_to_seq.argtypes = [vp, ci, ci, i64, ci, ci, ci, ci, vp, vp]
     lib.ulysses_head_to_seq.restype = ci
+    for name in ("ulysses_seq_to_head_batch", "ulysses_head_to_seq_batch"):
+        getattr(lib, name).argtypes = [ctypes.POINTER(ExchangeTensor), ci, ci, ci, i64, ci, ci, ci, vp]
+        getattr(lib, name).restype = ci
     lib.ulysses_attn_fwd.argtypes = [vp, vp, vp, i64, ci, ci, ci, ci, ci, f32, ci, vp, ci, vp, vp, vp]
     lib.ulysses_attn_fwd.restype = ci
     lib.ulysses_attn_bwd_workspace_size.argtypes = [i64, ci, ci, ci, ci, ci]
@@ -130,6 +142,49 @@ def ulysses_head_to_seq(inp, rank: int, chunks, stream=None) -> None:
         _ptr(inp), len(chunks), rank, n, bs, heads, hd, _dtype_code(inp), _ptr_array(chunks),
         _stream(stream))
     _check("ulysses_head_to_seq", st)
+
+
+def _batch_descs(pairs):
+    """[(chunks, head_tensor)] -> ctypes array of ExchangeTensor (+ keep-alive list)."""
+    descs = (ExchangeTensor * len(pairs))()
+    keep = []
+    n, bs, _, hd = pairs[0][0][0].shape
+    for chunks, head in pairs:
+        # the library takes one (P, n_local, bs, head_dim, dtype) for the whole batch
+        if len(chunks) != len(pairs[0][0]) or head.dtype != pairs[0][1].dtype or any(
+                (c.shape[0], c.shape[1], c.shape[3]) != (n, bs, hd) or c.dtype != head.dtype
+                for c in chunks):
+            raise ValueError("batched exchange: tensors differ in P, n_local, bs, head_dim or dtype")
+    for i, (chunks, head) in enumerate(pairs):
+        arr = _ptr_array(chunks)
+        keep.append(arr)
+        descs[i].chunks = ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
+        descs[i].head = head.data_ptr()
+        descs[i].heads = chunks[0].shape[2]
+    return descs, keep
+
+
+def ulysses_seq_to_head_batch(pairs, rank: int, stream=None) -> None:
+    """pairs: up to MAX_BATCH (chunks, out) as for ulysses_seq_to_head, moved in one launch.
+    All tensors share P, n_local, bs, head_dim and dtype; head counts may differ."""
+    n, bs, _, hd = pairs[0][0][0].shape
+    descs, keep = _batch_descs(pairs)
+    st = load_library().ulysses_seq_to_head_batch(
+        descs, len(pairs), len(pairs[0][0]), rank, n, bs, hd, _dtype_code(pairs[0][0][0]),
+        _stream(stream))
+    del keep
+    _check("ulysses_seq_to_head_batch", st)
+
+
+def ulysses_head_to_seq_batch(pairs, rank: int, stream=None) -> None:
+    """pairs: up to MAX_BATCH (inp, chunks) as for ulysses_head_to_seq, moved in one launch."""
+    n, bs, _, hd = pairs[0][1][0].shape
+    descs, keep = _batch_descs([(chunks, inp) for inp, chunks in pairs])
+    st = load_library().ulysses_head_to_seq_batch(
+        descs, len(pairs), len(pairs[0][1]), rank, n, bs, hd, _dtype_code(pairs[0][0]),
+        _stream(stream))
+    del keep
+    _check("ulysses_head_to_seq_batch", st)
 
 
 def ulysses_attn_fwd(q, k, v, o, lse, softmax_scale: float, causal: bool = True,

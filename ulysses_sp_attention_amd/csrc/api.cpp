@@ -86,6 +86,30 @@ ulysses_status_t check_attn(int64_t seqlen, int bs, int hq, int hkv, int head_di
   return ULYSSES_OK;
 }
 
+ulysses_status_t exchange_batch(bool to_head, const ulysses_exchange_tensor_t* tensors, int n,
+                                int P, int rank, int64_t n_local, int bs, int head_dim,
+                                ulysses_dtype_t dtype, hipStream_t stream) {
+  if (tensors == nullptr) return ULYSSES_ERR_NULL;
+  if (n < 1 || n > ULYSSES_MAX_BATCH) return ULYSSES_ERR_SHAPE;
+  ulysses::ExchangeTensor t[ULYSSES_MAX_BATCH];
+  for (int i = 0; i < n; ++i) {
+    t[i] = ulysses::ExchangeTensor{};
+    int64_t crb = 0, slot = 0, hrb = 0;
+    const ulysses_status_t st =
+        check_exchange(tensors[i].chunks, P, rank, n_local, bs, tensors[i].heads, head_dim, dtype,
+                       tensors[i].head, to_head, &t[i].chunks, &crb, &slot, &hrb);
+    if (st != ULYSSES_OK) return st;
+    t[i].head_buf = static_cast<char*>(tensors[i].head);
+    t[i].chunk_row_bytes = crb;
+    t[i].slot_bytes = slot;
+    t[i].head_row_bytes = hrb;
+  }
+  if (n_local == 0) return ULYSSES_OK;
+  return from_hip(ulysses::launch_exchange_batch(to_head, t, n, P, n_local * bs, stream));
+}
+
+static_assert(ULYSSES_MAX_BATCH == ulysses::kMaxBatch, "batch limit");
+
 }  // namespace
 
 extern "C" {
@@ -131,6 +155,20 @@ ulysses_status_t ulysses_head_to_seq(const void* in, int P, int rank, int64_t n_
   if (n_local == 0) return ULYSSES_OK;
   return from_hip(ulysses::launch_exchange(false, table, P, const_cast<char*>(static_cast<const char*>(in)),
                                            n_local * bs, crb, slot, hrb, stream));
+}
+
+ulysses_status_t ulysses_seq_to_head_batch(const ulysses_exchange_tensor_t* tensors,
+                                           int n_tensors, int P, int rank, int64_t n_local,
+                                           int bs, int head_dim, ulysses_dtype_t dtype,
+                                           hipStream_t stream) {
+  return exchange_batch(true, tensors, n_tensors, P, rank, n_local, bs, head_dim, dtype, stream);
+}
+
+ulysses_status_t ulysses_head_to_seq_batch(const ulysses_exchange_tensor_t* tensors,
+                                           int n_tensors, int P, int rank, int64_t n_local,
+                                           int bs, int head_dim, ulysses_dtype_t dtype,
+                                           hipStream_t stream) {
+  return exchange_batch(false, tensors, n_tensors, P, rank, n_local, bs, head_dim, dtype, stream);
 }
 
 ulysses_status_t ulysses_attn_fwd(const void* q, const void* k, const void* v, int64_t seqlen,

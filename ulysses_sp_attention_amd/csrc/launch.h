@@ -20,6 +20,20 @@ struct ChunkTable {
 //   head_row_bytes  : bytes of one (position, batch) row of the head buffer
 //                     (heads_l * head_dim * esize), a multiple of 16
 //   rows_per_chunk  : n_local * bs
+constexpr int kMaxBatch = 4;
+
+// One tensor of an exchange launch (see launch_exchange for the meaning).
+struct ExchangeTensor {
+  ChunkTable chunks;
+  char* head_buf;
+  int64_t chunk_row_bytes, slot_bytes, head_row_bytes;
+};
+
+// Moves n (1..kMaxBatch) tensors in one launch; every tensor has P chunks of
+// rows_per_chunk rows.
+hipError_t launch_exchange_batch(bool to_head, const ExchangeTensor* tensors, int n, int P,
+                                 int64_t rows_per_chunk, hipStream_t stream);
+
 hipError_t launch_exchange(bool to_head, const ChunkTable& chunks, int P, char* head_buf,
                            int64_t rows_per_chunk, int64_t chunk_row_bytes, int64_t slot_bytes,
                            int64_t head_row_bytes, hipStream_t stream);
