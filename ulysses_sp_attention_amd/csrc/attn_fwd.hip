@@ -20,20 +20,37 @@
 //  * The same accumulator, rounded to bf16, is directly the B operand of
 //    O^T += V^T P^T; V^T comes from LDS through the gfx950 transposing read
 //    (ds_read_b64_tr_b16), so V is stored in LDS in its natural row layout.
+//  * Matrix and vector work alternate between the two waves that share a
+//    SIMD (waves w and w+4).  Work is cut into phases separated by
+//    workgroup barriers; in every phase one wave of each SIMD issues only
+//    matrix products (the scores of key tile t and the PV product of tile
+//    t-1, 32 MFMAs) while its partner runs only the softmax of a tile (mask,
+//    row max, exponentials, row sum, bf16 rounding), which the SIMD executes
+//    alongside the partner's MFMAs.  The second group of waves runs one
+//    phase behind the first.  Each group has its own copy of the loop, and
+//    every pair of phases has the same shape, so the compiler keeps the
+//    loop free of spills and of conservative memory waits.
+//  * K and V tiles reach LDS by direct global-to-LDS copies (no registers
+//    spent on staging), issued by the waves in pieces spread through their
+//    softmax phase, two pairs of phases ahead of use, into four rotating
+//    buffers per tensor (128 KiB of LDS at head size 128).
 //  * Online softmax in the exp2 domain with scale*log2(e) folded into one
 //    FMA per score.  The running max is only raised when a row's max grows by
 //    more than 8 (a factor 256), so O and the row sum are rarely rescaled;
-//    any reference max gives the same result in exact arithmetic.
+//    any reference max gives the same result in exact arithmetic.  The row
+//    max of a lane pair uses v_permlane32_swap.
 //  * Key tiles entirely above the diagonal (or outside the documents of a
-//    block) are never visited; per wave, tiles entirely masked for its rows
-//    are skipped; only tiles crossing a boundary apply the element mask.
+//    block) are never visited.  Every wave walks all tiles of its block;
+//    tiles crossing a boundary of some row of the wave (or not seen by it at
+//    all) get an element mask that adds a penalty instead of comparing, so
+//    the rarely taken mask code holds no compare masks in scalar registers.
 //  * LDS rows are swizzled in 16-byte chunks (swz in device_common.h) so both
 //    the row reads of K and the transposing reads of V avoid bank conflicts;
-//    every fragment is read two products ahead of the MFMA that uses it, and
-//    consecutive MFMAs go to different accumulators, so LDS latency and MFMA
-//    dependency latency overlap the matrix work.
+//    fragments are read several products ahead of the MFMA that uses them.
 //  * Blocks are launched heaviest (largest positions) first.
 #include <math.h>
+
+#include <type_traits>
 
 #include "device_common.h"
 #include "launch.h"
@@ -67,24 +84,29 @@ struct FwdCfg {
   static constexpr int kTileBytes = kBC * kRowBytes;
   static constexpr int kKS = HD / 16;                // k-steps of S^T = K Q^T
   static constexpr int kDB = HD / 32;                // 32-wide blocks of head dim
-  static constexpr int kLoads = kBC * kChunks / kThreads;  // 16-byte loads per tensor per tile
-  static_assert(kLoads >= 1 && kBC * kChunks % kThreads == 0, "tile loads");
+  static constexpr int kBufs = 4;                    // rotating LDS buffers per tensor
+  // One wave-wide direct copy moves 1 KiB (64 lanes x 16 bytes).
+  static constexpr int kRowsPerCopy = 1024 / kRowBytes;
+  static constexpr int kCopiesPerWave = kTileBytes / 1024 / kWaves;   // per tensor and tile
+  static constexpr int kPrefetch = 4;                // fragments read ahead of their MFMA
+  static_assert(kCopiesPerWave >= 1 && kTileBytes % (1024 * kWaves) == 0, "tile copies");
 };
 
 template <int HD, int GPACK>
 __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdParams p) {
   using C = FwdCfg<HD, GPACK>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * C::kTileBytes];
-  char* lds_k = smem;
-  char* lds_v = smem + C::kTileBytes;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * C::kBufs * C::kTileBytes];
+  char* const lds_k0 = smem;                               // K buffers
+  char* const lds_v0 = smem + C::kBufs * C::kTileBytes;    // V buffers
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5;      // which k-half / row-quad of the MFMA layout
   const int r32 = lane & 31;
+  const int group = wave >> 2;     // waves w and w+4 share a SIMD
 
-  const int64_t N = p.N;
+  const int64_t N = wave_uniform(p.N);
   const int64_t pb = p.num_pos_blocks - 1 - (int64_t)blockIdx.x;   // heaviest first
   const int ngroups = p.g / GPACK;
   int y = blockIdx.y;
@@ -101,8 +123,11 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdParams p) {
   const int64_t q_tok = (int64_t)p.bs * p.hq * HD;
   const int64_t kv_tok = (int64_t)p.bs * p.hkv * HD;
   const __bf16* qbase = p.q + ((int64_t)b * p.hq + h) * HD;
-  const __bf16* kbase = p.k + ((int64_t)b * p.hkv + kh) * HD;
-  const __bf16* vbase = p.v + ((int64_t)b * p.hkv + kh) * HD;
+  // (Kept in scalar registers: the copies take their base from there.)
+  const __bf16* kbase = reinterpret_cast<const __bf16*>(
+      wave_uniform(reinterpret_cast<int64_t>(p.k + ((int64_t)b * p.hkv + kh) * HD)));
+  const __bf16* vbase = reinterpret_cast<const __bf16*>(
+      wave_uniform(reinterpret_cast<int64_t>(p.v + ((int64_t)b * p.hkv + kh) * HD)));
 
   // Q fragments (B operand of S^T): lane holds Q[qi][16 ks + 8 half + 0..7].
   bf16x8_t qf[C::kKS];
@@ -114,102 +139,152 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdParams p) {
       qf[ks] = bf16x8_t{};
   }
 
-  // Key range of the whole block, of this wave, and of this lane's row.
+  // Key range of the whole block, and the keys of this wave and lane.  Every
+  // wave walks all key tiles of its block (so all waves share one schedule);
+  // tiles a wave does not see are masked out entirely.
   const int64_t blk_last = (p0 + C::kBP < N ? p0 + C::kBP : N) - 1;
   const int64_t kv_lo = doc_start_of(p.cu, p.n_docs, p0);
   const int64_t kv_hi = p.causal ? blk_last + 1 : doc_end_of(p.cu, p.n_docs, blk_last, N);
   const bool wave_active = pw < N;
   const int64_t w_last = wave_active ? (pw + 31 < N ? pw + 31 : N - 1) : 0;
-  const int64_t w_lo = wave_active ? doc_start_of(p.cu, p.n_docs, pw) : 0;
-  const int64_t w_hi = wave_active ? (p.causal ? w_last + 1 : doc_end_of(p.cu, p.n_docs, w_last, N)) : 0;
   // Keys visible to every row of the wave: [full_lo, full_hi).
-  const int64_t full_lo = wave_active ? doc_start_of(p.cu, p.n_docs, w_last) : 0;
-  const int64_t full_hi = wave_active ? (p.causal ? pw + 1 : doc_end_of(p.cu, p.n_docs, pw, N)) : 0;
-  const int64_t my_lo = qi < N ? doc_start_of(p.cu, p.n_docs, qi) : 0;
-  const int64_t my_hi = qi < N ? (p.causal ? qi + 1 : doc_end_of(p.cu, p.n_docs, qi, N)) : 0;
+  const int64_t full_lo = wave_uniform(wave_active ? doc_start_of(p.cu, p.n_docs, w_last) : 0);
+  const int64_t full_hi = wave_uniform(
+      wave_active ? (p.causal ? pw + 1 : doc_end_of(p.cu, p.n_docs, pw, N)) : 0);
+  // Visible keys of this lane's row, relative to the block's first key.
+  const int64_t key0 = wave_uniform((kv_lo / C::kBC) * C::kBC);
+  const int my_lo = qi < N ? (int)(doc_start_of(p.cu, p.n_docs, qi) - key0) : 0;
+  const int my_hi =
+      qi < N ? (int)((p.causal ? qi + 1 : doc_end_of(p.cu, p.n_docs, qi, N)) - key0) : 0;
 
-  const int64_t t_begin = kv_lo / C::kBC;
-  const int64_t t_end = (kv_hi + C::kBC - 1) / C::kBC;
+  // Key tiles of the block: t_begin .. t_begin + n_tiles - 1.
+  const int64_t t_begin = wave_uniform(kv_lo / C::kBC);
+  const int n_tiles = (int)wave_uniform((kv_hi + C::kBC - 1) / C::kBC - t_begin);
+
+  // K and V tiles reach LDS by direct global-to-LDS copies: a wave moves its
+  // share of a tile (kCopiesPerWave slices of 1 KiB, 16 bytes per lane).
+  // Slice c of the tile lands at bytes [1024 c, 1024 c + 1024) of the
+  // buffer, lane l at +16 l, so lane l fetches the source chunk that the
+  // swizzle places there.  Rows past the sequence end re-read row N-1: those
+  // keys are masked for every query, so only their finiteness matters.
+  const int64_t row_bytes = kv_tok * 2;
+  // Lane byte offsets of this wave's slices within a tile that lies wholly
+  // inside the sequence (the usual case; the last tile of a sequence whose
+  // length is not a multiple of kBC clamps its rows instead).
+  // Tile-level decisions use 32-bit offsets from the block's first key (the
+  // scalar unit has no 64-bit ordered compare).
+  const int keys_left = (int)wave_uniform(N - key0);      // keys from key0 to the end
+  const int m_tail = keys_left / C::kBC;                   // first tile running past N
+  const int flo = (int)wave_uniform(full_lo - key0);
+  const int fhi = (int)wave_uniform(full_hi - key0);
+  uint32_t slice_off[C::kCopiesPerWave];
+#pragma unroll
+  for (int c = 0; c < C::kCopiesPerWave; ++c) {
+    const int cidx = wave * C::kCopiesPerWave + c;
+    const int row0 = cidx * C::kRowsPerCopy + lane / C::kChunks;
+    const int col_bytes = ((lane % C::kChunks) ^ swz_f<C::kChunks>(row0)) * 16;
+    slice_off[c] = (uint32_t)(row0 * row_bytes) + (uint32_t)col_bytes;
+  }
+  auto copy_slice = [&](const __bf16* base, char* buf, int m, int c) __attribute__((always_inline)) {
+    const int64_t j0 = (t_begin + m) * C::kBC;
+    const char* tile =
+        reinterpret_cast<const char*>(wave_uniform((int64_t)base + j0 * row_bytes));
+    const int cidx = wave * C::kCopiesPerWave + c;
+    uint32_t off = slice_off[c];
+    if (m >= m_tail) {   // the tile runs past the sequence end
+      const int last = keys_left - 1 - m * C::kBC;
+      const int row0 = cidx * C::kRowsPerCopy + lane / C::kChunks;
+      const int col_bytes = ((lane % C::kChunks) ^ swz_f<C::kChunks>(row0)) * 16;
+      const int row = row0 < last ? row0 : last;
+      off = (uint32_t)(row * row_bytes) + (uint32_t)col_bytes;
+    }
+    copy_lds16_async_sbase(tile, off, buf + cidx * 1024);
+  };
+  auto copy_tile = [&](const __bf16* base, char* buf, int m) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < C::kCopiesPerWave; ++c) copy_slice(base, buf, m, c);
+  };
 
   f32x16_t acc_o[C::kDB];
 #pragma unroll
   for (int db = 0; db < C::kDB; ++db) acc_o[db] = f32x16_t{};
   float m_run = -INFINITY;   // reference max, log2 domain
   float l_run = 0.f;         // this lane's share of the row sum
-
-  u32x4_t kst[C::kLoads], vst[C::kLoads];
-  auto load_tile = [&](int64_t t) {
+  f32x16_t s[2];             // scores of a tile, from its matrix to its vector phase
+  bf16x8_t pf[4];            // bf16 probabilities of a tile, awaiting its PV product
 #pragma unroll
-    for (int i = 0; i < C::kLoads; ++i) {
-      const int cid = tid + i * C::kThreads;
-      const int row = cid / C::kChunks;
-      const int ch = cid % C::kChunks;
-      const int64_t j = t * C::kBC + row;
-      if (j < N) {
-        kst[i] = *reinterpret_cast<const u32x4_t*>(kbase + j * kv_tok + ch * 8);
-        vst[i] = *reinterpret_cast<const u32x4_t*>(vbase + j * kv_tok + ch * 8);
+  for (int i = 0; i < 4; ++i) pf[i] = bf16x8_t{};
+
+  // --- matrix phase: S = scores of tile m (QK), O += P(m-1) V(m-1) (PV) ---
+  // LDS byte offsets of this lane's fragments.  The swizzle depends on the
+  // low four row bits only, so the 32-key half kb of a K read and the 16-key
+  // step ks of a V read add constant offsets.
+  int koff[C::kKS];
+#pragma unroll
+  for (int ks = 0; ks < C::kKS; ++ks) koff[ks] = swz<C::kChunks, C::kRowBytes>(r32, 2 * ks + half);
+  const TrReader<C::kChunks, C::kRowBytes, C::kDB> vtr(lane);
+  auto kfrag = [&](const char* lk, int idx) __attribute__((always_inline)) {
+    const int ks = idx >> 1, kb = idx & 1;
+    return *reinterpret_cast<const bf16x8_t*>(lk + kb * 32 * C::kRowBytes + koff[ks]);
+  };
+  auto vfrag = [&](const char* lv, int idx) __attribute__((always_inline)) { return vtr.load(lv, 16 * (idx / C::kDB), idx % C::kDB); };
+  auto matrix_phase = [&](auto qk_tag, auto pv_tag, const char* lk, const char* lv) __attribute__((always_inline)) {
+    constexpr bool kQK = decltype(qk_tag)::value;
+    constexpr bool kPV = decltype(pv_tag)::value;
+    constexpr int NQ = kQK ? 2 * C::kKS : 0;   // (ks, kb) pairs, kb fastest
+    constexpr int NP = kPV ? 4 * C::kDB : 0;   // (ks, db) pairs, db fastest
+    constexpr int NS = NQ + NP;
+    constexpr int PF = C::kPrefetch < NS ? C::kPrefetch : NS;
+    auto frag = [&](int idx) __attribute__((always_inline)) { return idx < NQ ? kfrag(lk, idx) : vfrag(lv, idx - NQ); };
+    bf16x8_t buf[PF + 1];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) buf[i] = frag(i);
+#pragma unroll
+    for (int idx = 0; idx < NS; ++idx) {
+      if (idx + PF < NS) buf[(idx + PF) % (PF + 1)] = frag(idx + PF);
+      if (idx < NQ) {
+        const f32x16_t c = idx < 2 ? f32x16_t{} : s[idx & 1];
+        s[idx & 1] = mfma32(buf[idx % (PF + 1)], qf[idx >> 1], c);
       } else {
-        kst[i] = u32x4_t{};
-        vst[i] = u32x4_t{};
+        const int i = idx - NQ;
+        acc_o[i % C::kDB] = mfma32(buf[idx % (PF + 1)], pf[i / C::kDB], acc_o[i % C::kDB]);
       }
-    }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int i = 0; i < C::kLoads; ++i) {
-      const int cid = tid + i * C::kThreads;
-      const int off = swz<C::kChunks, C::kRowBytes>(cid / C::kChunks, cid % C::kChunks);
-      *reinterpret_cast<u32x4_t*>(lds_k + off) = kst[i];
-      *reinterpret_cast<u32x4_t*>(lds_v + off) = vst[i];
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  if (t_begin < t_end) load_tile(t_begin);
-  for (int64_t t = t_begin; t < t_end; ++t) {
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (t + 1 < t_end) load_tile(t + 1);
-
-    const int64_t j0 = t * C::kBC;
-    if (!wave_active || j0 >= w_hi || j0 + C::kBC <= w_lo) continue;
-
-    // S^T[kv][q] = K Q^T for the two 32-key halves of the tile: the two
-    // accumulator chains alternate, and each K fragment is read from LDS two
-    // products ahead of its use.
-    f32x16_t s[2];
-    s[0] = f32x16_t{};
-    s[1] = f32x16_t{};
-    {
-      constexpr int kSteps = 2 * C::kKS;   // (ks, kb) pairs, kb fastest
-      auto kfrag = [&](int idx) {
-        const int ks = idx >> 1, kb = idx & 1;
-        return *reinterpret_cast<const bf16x8_t*>(
-            lds_k + swz<C::kChunks, C::kRowBytes>(kb * 32 + r32, 2 * ks + half));
-      };
-      bf16x8_t buf[3];
-      buf[0] = kfrag(0);
-      buf[1] = kfrag(1);
-#pragma unroll
-      for (int idx = 0; idx < kSteps; ++idx) {
-        if (idx + 2 < kSteps) buf[(idx + 2) % 3] = kfrag(idx + 2);
-        s[idx & 1] = mfma32(buf[idx % 3], qf[idx >> 1], s[idx & 1]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-
-    // Element mask on tiles that cross a boundary of some row of the wave.
-    const bool need_mask = j0 < full_lo || j0 + C::kBC > full_hi;
-    if (need_mask) {
-      // visible keys of this row as offsets into the tile, clamped to [-1, 65]
-      const int lo = (int)(my_lo - j0 < -1 ? -1 : (my_lo - j0 > 65 ? 65 : my_lo - j0));
-      const int hi = (int)(my_hi - j0 < -1 ? -1 : (my_hi - j0 > 65 ? 65 : my_hi - j0));
+  // --- vector phase: softmax of tile m's scores into pf -------------------
+  // `issue(k)`, k = 0..3, issues a quarter of the wave's tile copies; the
+  // quarters are spread through the softmax so that the copies, which block
+  // the wave while the address unit is busy, overlap its vector work.
+  auto vector_phase = [&](int m, auto mask_tag, auto issue) __attribute__((always_inline)) {
+    const int jr = m * C::kBC;   // first key of the tile, relative to key0
+    issue(0);
+    // Element mask on tiles that cross a boundary of some row of the wave,
+    // without compares: with lo <= key < hi the visible keys of this row as
+    // offsets into the tile, each score gets clamp(min(key - lo,
+    // hi - 1 - key), -1, 0) * 2^100 added: exactly 0 when visible, and when
+    // not the score becomes exactly -2^100 (the score itself is absorbed).
+    // A masked score can never be a row's maximum while the row sees a key of
+    // the tile, and its probability is exactly 0 then.  If the row sees no
+    // key of the tile, the stand-in maximum -2^100 (times the 24-bit scale,
+    // which is exact in fp32, so the fused exponent argument is exactly 0
+    // and no probability exceeds 1) is replaced, with a rescale by exactly 0,
+    // by the first real score the row meets; every row meets one (its own
+    // position, or its document).
+    if (decltype(mask_tag)::value && (jr < flo || jr + C::kBC > fhi)) {
+      // Offsets clamped to [-1, 65], then shifted by this lane's 4*half so
+      // that every element uses a constant key offset.
+      const float neg_lo = (float)(4 * half - min(max(my_lo - jr, -1), 65));
+      const float hi_m1 = (float)(min(max(my_hi - jr, -1), 65) - 1 - 4 * half);
+      const float big = 0x1p100f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int j = kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-          if (j < lo || j >= hi) s[kb][i] = -INFINITY;
+          const float j = (float)(kb * 32 + 8 * (i >> 2) + (i & 3));   // key offset minus 4*half
+          const float d = __builtin_amdgcn_fmed3f(fminf(j + neg_lo, hi_m1 - j), -1.0f, 0.0f);
+          s[kb][i] = fmaf(d, big, s[kb][i]);
         }
     }
 
@@ -219,7 +294,8 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdParams p) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-    mx = fmaxf(mx, wave_shfl_xor32(mx));
+    mx = fmaxf(mx, wave_xor32_f(mx));
+    issue(1);
     const float mx2 = mx * p.scale_log2;
     const bool raise = mx2 > m_run + 8.0f;
     if (wave_any(raise)) {
@@ -234,48 +310,117 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdParams p) {
     const float mb = m_run == -INFINITY ? 0.f : m_run;
 
     // P = exp2(s * scale*log2e - m), rounded to bf16 as the B operand of PV.
-    bf16x8_t pf[4];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float e = __builtin_amdgcn_exp2f(fmaf(s[kb][i], p.scale_log2, -mb));
         l_run += e;
         pf[2 * kb + (i >> 3)][i & 7] = (__bf16)e;
       }
-
-    // O^T[d][q] += V^T P^T; V^T fragments via the transposing LDS read, two
-    // products ahead of their use, four independent accumulator chains.
-    const int grp = lane >> 4;
-    const int u = lane & 15;
-    {
-      constexpr int kSteps = 4 * C::kDB;   // (ks, db) pairs, db fastest
-      auto vfrag = [&](int idx) {
-        const int ks = idx / C::kDB, db = idx % C::kDB;
-        bf16x4_t part[2];
-#pragma unroll
-        for (int jh = 0; jh < 2; ++jh) {
-          const int row = 16 * ks + 8 * jh + 4 * (grp >> 1) + (u >> 2);
-          const int col = db * 32 + 16 * (grp & 1) + 4 * (u & 3);
-          const int off = swz<C::kChunks, C::kRowBytes>(row, col >> 3) + ((col >> 2) & 1) * 8;
-          part[jh] = lds_read_tr16(lds_v + off);
-        }
-        return __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
-      };
-      bf16x8_t buf[3];
-      buf[0] = vfrag(0);
-      buf[1] = vfrag(1);
-#pragma unroll
-      for (int idx = 0; idx < kSteps; ++idx) {
-        if (idx + 2 < kSteps) buf[(idx + 2) % 3] = vfrag(idx + 2);
-        acc_o[idx % C::kDB] = mfma32(buf[idx % 3], pf[idx / C::kDB], acc_o[idx % C::kDB]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      issue(2 + kb);
     }
-  }
+  };
+
+  // Global phases 2m and 2m+1 form pair m (m = 0 .. n_tiles).  Group 0 runs
+  // the matrix work of pair m in phase 2m and the softmax of tile m in phase
+  // 2m+1; group 1 runs one phase later (its softmax of tile m falls in phase
+  // 2m+2).  The matrix work of pair m reads K of tile m from K buffer m%4
+  // and V of tile m-1 from V buffer (m+3)%4.  In its softmax phase within
+  // pair m every wave copies its share of K of tile m+3 into K buffer
+  // (m+3)%4 and of V of tile m+2 into V buffer (m+2)%4 (both last read in
+  // pair m-1).  At the end of pair m every wave waits for its copies of pair
+  // m-2, so the barrier publishes the tiles that pair m+1 reads while the
+  // copies of two pairs stay in flight.  Copies past the last tile are
+  // clamped to it (the data lands in a buffer nobody reads again).
+  using std::integral_constant;
+  using std::true_type;
+  using std::false_type;
+  constexpr int kPairCopies = 2 * C::kCopiesPerWave;
+  // Copies of pair m, in four parts: k = 0, 1 for K of tile m+3 and k = 2, 3
+  // for V of tile m+2 (with one slice per tensor, parts 1 and 3 are empty).
+  auto copy_part = [&](int m, auto r_tag, int k) __attribute__((always_inline)) {
+    constexpr int r = decltype(r_tag)::value;   // m % 4
+    const int last = n_tiles - 1;
+    const bool is_v = k >= 2;
+    const int c = k & 1;
+    if (c >= C::kCopiesPerWave) return;
+    const int t = is_v ? (m + 2 < last ? m + 2 : last) : (m + 3 < last ? m + 3 : last);
+    char* buf = is_v ? lds_v0 + ((r + 2) & 3) * C::kTileBytes : lds_k0 + ((r + 3) & 3) * C::kTileBytes;
+    copy_slice(is_v ? vbase : kbase, buf, t, c);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto copy_pair = [&](int m, auto r_tag) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) copy_part(m, r_tag, k);
+  };
+
+  // Pair m of the main run (1 <= m < n_tiles): scores of tile m, PV of tile
+  // m-1, softmax of tile m.  Tiles the wave does not see are computed and
+  // masked out entirely (P = 0), which keeps every wave on the same code.
+  auto mid_pair = [&](int m, auto r_tag, auto g_tag) __attribute__((always_inline)) {
+    constexpr int r = decltype(r_tag)::value;
+    constexpr int g = decltype(g_tag)::value;
+    matrix_phase(true_type{}, true_type{}, lds_k0 + r * C::kTileBytes,
+                 lds_v0 + ((r + 3) & 3) * C::kTileBytes);
+    if constexpr (g == 1) wait_vmem_n<2 * kPairCopies>();
+    block_barrier();
+    auto issue = [&](int k) __attribute__((always_inline)) {
+      if constexpr (g == 0) copy_part(m, r_tag, k);
+      else copy_part(m + 1, integral_constant<int, (r + 1) & 3>{}, k);
+    };
+    vector_phase(m, true_type{}, issue);
+    if constexpr (g == 0) wait_vmem_n<2 * kPairCopies>();
+    block_barrier();
+  };
+  auto run = [&](auto g_tag) __attribute__((always_inline)) {
+    constexpr int g = decltype(g_tag)::value;
+    // Prologue: K of tiles 0..2 and V of tiles 0..1.
+    const int last = n_tiles - 1;
+    copy_tile(kbase, lds_k0, 0);
+    copy_tile(kbase, lds_k0 + C::kTileBytes, 1 < last ? 1 : last);
+    copy_tile(kbase, lds_k0 + 2 * C::kTileBytes, 2 < last ? 2 : last);
+    copy_tile(vbase, lds_v0, 0);
+    copy_tile(vbase, lds_v0 + C::kTileBytes, 1 < last ? 1 : last);
+    wait_vmem();
+    block_barrier();
+    if constexpr (g == 1) {   // phase 0: group 1 has no softmax yet, only copies
+      copy_pair(0, integral_constant<int, 0>{});
+      block_barrier();
+    }
+
+    // Pair 0: scores of tile 0 only.
+    matrix_phase(true_type{}, false_type{}, lds_k0, lds_v0);
+    block_barrier();
+    auto issue0 = [&](int k) __attribute__((always_inline)) {
+      if constexpr (g == 0) copy_part(0, integral_constant<int, 0>{}, k);
+      else copy_part(1, integral_constant<int, 1>{}, k);
+    };
+    vector_phase(0, true_type{}, issue0);
+    block_barrier();
+
+    // Pairs 1 .. n_tiles-1, four per iteration so that the buffer rotation
+    // m % 4 is a compile-time constant.
+    for (int m = 1; m < n_tiles; m += 4) {
+      mid_pair(m, integral_constant<int, 1>{}, g_tag);
+      if (m + 1 < n_tiles) mid_pair(m + 1, integral_constant<int, 2>{}, g_tag);
+      if (m + 2 < n_tiles) mid_pair(m + 2, integral_constant<int, 3>{}, g_tag);
+      if (m + 3 < n_tiles) mid_pair(m + 3, integral_constant<int, 0>{}, g_tag);
+    }
+
+    // Pair n_tiles: PV of the last tile only.
+    matrix_phase(false_type{}, true_type{}, lds_k0,
+                 lds_v0 + ((n_tiles + 3) & 3) * C::kTileBytes);
+    wait_vmem();
+    block_barrier();
+    block_barrier();
+    if constexpr (g == 0) block_barrier();   // matches group 1's leading phase
+  };
+  if (group == 0) run(integral_constant<int, 0>{});
+  else run(integral_constant<int, 1>{});
 
   if (qi >= N) return;
-  const float l = l_run + wave_shfl_xor32(l_run);
+  const float l = l_run + wave_xor32_f(l_run);
   const float inv = 1.0f / l;
   __bf16* orow = p.o + (qi * p.bs + b) * (int64_t)p.hq * HD + (int64_t)h * HD;
 #pragma unroll

@@ -46,6 +46,18 @@ __device__ __forceinline__ float wave_shfl_xor32(float x) {
   return __shfl_xor(x, 32, 64);
 }
 
+// Lanes l and l^32 exchange values through v_permlane32_swap (a VALU
+// operation, unlike the LDS-routed shuffle above): with both operands x, the
+// swap leaves x of lanes 0..31 in both halves of one result and x of lanes
+// 32..63 in both halves of the other.
+__device__ __forceinline__ float wave_xor32_f(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const uint32_t lo_half = r[0], hi_half = r[1];   // x of lanes 0..31 and of 32..63
+  const bool upper = (__lane_id() & 32) != 0;
+  return __builtin_bit_cast(float, upper ? lo_half : hi_half);
+}
+
 // Byte offset of 16-byte chunk `ch` of row `row` in an LDS tile of rows of
 // kChunks chunks.  The chunk index is XORed with a per-row value f(row) that
 // takes all 16 values over any 16 consecutive rows (so 16 lanes reading one
@@ -74,6 +86,49 @@ __device__ __forceinline__ void load_lds16(const void* src, void* lds_dst) {
   __builtin_amdgcn_global_load_lds(src, (ULY_LDS void*)lds_dst, 16, 0, 0);
 }
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// The same copy issued from inline assembly, so the compiler does not treat
+// it as a pending write to all of LDS (it would otherwise wait for it before
+// every later LDS read); the caller orders it with wait_vmem / wait_vmem_n
+// and a barrier.  lds_dst must be wave-uniform; M0 carries it.  The
+// compiler's hazard checks do not look inside inline assembly, so the block
+// starts with the 5 wait states that a vector memory instruction needs after
+// a VALU write (v_readfirstlane) of an SGPR it reads, and that also cover the
+// M0 write before an LDS-DMA load.
+__device__ __forceinline__ void copy_lds16_async(const void* src, void* lds_dst) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)((ULY_LDS char*)(lds_dst)));
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0) : "memory");
+}
+
+// The same with a wave-uniform 64-bit base in scalar registers and a 32-bit
+// per-lane byte offset (the saddr form of the instruction).
+__device__ __forceinline__ void copy_lds16_async_sbase(const void* base, uint32_t offset,
+                                                       void* lds_dst) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)((ULY_LDS char*)(lds_dst)));
+  // readfirstlane yields a signed int: widen through uint32_t, never directly.
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  const uint64_t sb = ((uint64_t)hi << 32) | (uint64_t)lo;
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(offset), "s"(sb), "{m0}"(m0)
+               : "memory");
+}
+
+// Waits until at most N vector-memory operations of this wave are pending
+// (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vmem_n() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier for kernels that order their own global-to-LDS copies:
+// waits for this wave's LDS reads, then s_barrier, with no release fence
+// over vector memory (which would also wait for copies still in flight).
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 // A operand of v_mfma_f32_32x32x16_bf16 (rows = head dim, k = 16 sequence
 // positions from row0) read transposed, with ds_read_b64_tr_b16, from a
