@@ -129,14 +129,16 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdParams p) {
   const __bf16* vbase = reinterpret_cast<const __bf16*>(
       wave_uniform(reinterpret_cast<int64_t>(p.v + ((int64_t)b * p.hkv + kh) * HD)));
 
-  // Q fragments (B operand of S^T): lane holds Q[qi][16 ks + 8 half + 0..7].
+  // Q fragments (B operand of S^T): lane holds Q[qi][16 ks + 8 half + 0..7],
+  // multiplied by scale*log2(e) and rounded to bf16 once, so that the
+  // products give scores already in the exp2 domain.
   bf16x8_t qf[C::kKS];
 #pragma unroll
   for (int ks = 0; ks < C::kKS; ++ks) {
-    if (qi < N)
-      qf[ks] = *reinterpret_cast<const bf16x8_t*>(qbase + qi * q_tok + 16 * ks + 8 * half);
-    else
-      qf[ks] = bf16x8_t{};
+    bf16x8_t raw = bf16x8_t{};
+    if (qi < N) raw = *reinterpret_cast<const bf16x8_t*>(qbase + qi * q_tok + 16 * ks + 8 * half);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qf[ks][e] = (__bf16)((float)raw[e] * p.scale_log2);
   }
 
   // Key range of the whole block, and the keys of this wave and lane.  Every
@@ -210,6 +212,9 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdParams p) {
   for (int db = 0; db < C::kDB; ++db) acc_o[db] = f32x16_t{};
   float m_run = -INFINITY;   // reference max, log2 domain
   float l_run = 0.f;         // this lane's share of the row sum
+  // Every score accumulation starts from -m_run (0 while the row has no
+  // maximum yet), so the products give s * scale*log2(e) - m_run directly.
+  f32x16_t sbias = f32x16_t{};
   f32x16_t s[2];             // scores of a tile, from its matrix to its vector phase
   bf16x8_t pf[4];            // bf16 probabilities of a tile, awaiting its PV product
 #pragma unroll
@@ -243,7 +248,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdParams p) {
     for (int idx = 0; idx < NS; ++idx) {
       if (idx + PF < NS) buf[(idx + PF) % (PF + 1)] = frag(idx + PF);
       if (idx < NQ) {
-        const f32x16_t c = idx < 2 ? f32x16_t{} : s[idx & 1];
+        const f32x16_t c = idx < 2 ? sbias : s[idx & 1];
         s[idx & 1] = mfma32(buf[idx % (PF + 1)], qf[idx >> 1], c);
       } else {
         const int i = idx - NQ;
@@ -264,14 +269,8 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdParams p) {
     // without compares: with lo <= key < hi the visible keys of this row as
     // offsets into the tile, each score gets clamp(min(key - lo,
     // hi - 1 - key), -1, 0) * 2^100 added: exactly 0 when visible, and when
-    // not the score becomes exactly -2^100 (the score itself is absorbed).
-    // A masked score can never be a row's maximum while the row sees a key of
-    // the tile, and its probability is exactly 0 then.  If the row sees no
-    // key of the tile, the stand-in maximum -2^100 (times the 24-bit scale,
-    // which is exact in fp32, so the fused exponent argument is exactly 0
-    // and no probability exceeds 1) is replaced, with a rescale by exactly 0,
-    // by the first real score the row meets; every row meets one (its own
-    // position, or its document).
+    // not the score becomes exactly -2^100 (the score itself is absorbed),
+    // whose probability is exactly 0.
     if (decltype(mask_tag)::value && (jr < flo || jr + C::kBC > fhi)) {
       // Offsets clamped to [-1, 65], then shifted by this lane's 4*half so
       // that every element uses a constant key offset.
@@ -288,7 +287,10 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdParams p) {
         }
     }
 
-    // Row max over the tile (this lane's 32 keys, then the partner lane's).
+    // Row max over the tile (this lane's 32 keys, then the partner lane's),
+    // relative to m_run.  A row raises its reference when it has none yet
+    // and sees a key here (max above -2^99), or when its max grew by more
+    // than 8; a row that sees no key here keeps m_run = -inf.
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -296,25 +298,34 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdParams p) {
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
     mx = fmaxf(mx, wave_xor32_f(mx));
     issue(1);
-    const float mx2 = mx * p.scale_log2;
-    const bool raise = mx2 > m_run + 8.0f;
+    const bool raise = mx > (m_run == -INFINITY ? -0x1p99f : 8.0f);
+
     if (wave_any(raise)) {
-      const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - mx2) : 1.0f;
-      if (raise) m_run = mx2;
+      const float mb = m_run == -INFINITY ? 0.f : m_run;
+      const float m_new = raise ? mb + mx : m_run;
+      const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+      m_run = m_new;
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < C::kDB; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc_o[db][i] *= alpha;
+      const float nb = m_run == -INFINITY ? 0.f : -m_run;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sbias[i] = nb;
+      const float shift = raise ? mx : 0.0f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[kb][i] -= shift;
     }
-    const float mb = m_run == -INFINITY ? 0.f : m_run;
 
     // P = exp2(s * scale*log2e - m), rounded to bf16 as the B operand of PV.
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float e = __builtin_amdgcn_exp2f(fmaf(s[kb][i], p.scale_log2, -mb));
+        const float e = __builtin_amdgcn_exp2f(s[kb][i]);
         l_run += e;
         pf[2 * kb + (i >> 3)][i & 7] = (__bf16)e;
       }
