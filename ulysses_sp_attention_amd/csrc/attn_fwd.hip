@@ -215,6 +215,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdParams p) {
   // Every score accumulation starts from -m_run (0 while the row has no
   // maximum yet), so the products give s * scale*log2(e) - m_run directly.
   f32x16_t sbias = f32x16_t{};
+  bool ref_ready = false;    // every row of the wave has a reference max
   f32x16_t s[2];             // scores of a tile, from its matrix to its vector phase
   bf16x8_t pf[4];            // bf16 probabilities of a tile, awaiting its PV product
 #pragma unroll
@@ -287,19 +288,52 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdParams p) {
         }
     }
 
-    // Row max over the tile (this lane's 32 keys, then the partner lane's),
-    // relative to m_run.  A row raises its reference when it has none yet
-    // and sees a key here (max above -2^99), or when its max grew by more
-    // than 8; a row that sees no key here keeps m_run = -inf.
+    issue(1);
+
+    // P = exp2(s * scale*log2e - m_run), rounded to bf16 as the B operand of
+    // PV; returns this lane's share of the tile's row sum.
+    auto exps = [&](auto issue_tag) __attribute__((always_inline)) {
+      float lt = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float e = __builtin_amdgcn_exp2f(s[kb][i]);
+          lt += e;
+          pf[2 * kb + (i >> 3)][i & 7] = (__bf16)e;
+        }
+        if constexpr (decltype(issue_tag)::value) issue(2 + kb);
+      }
+      return lt;
+    };
+
+    // Fast path: every row of the wave has a reference max, and no
+    // probability of the tile exceeds 2^60 (its lane sum stays below that).
+    // The reference may then lag the true running max: probabilities up to
+    // 2^60 keep O and the row sum far inside fp32 range, and rounding to bf16
+    // is relative, so the result is the same as with an exact max.
+    bool issued = false;
+    if (ref_ready) {
+      const float lt = exps(std::true_type{});
+      issued = true;
+      if (!wave_any(!(lt <= 0x1p60f))) {
+        l_run += lt;
+        return;
+      }
+    }
+
+    // Exact path (a row without a reference, or a tile that would overflow):
+    // row max relative to m_run (this lane's 32 keys, then the partner
+    // lane's).  A row takes the tile max as its reference when it has none
+    // yet and sees a key here (max above -2^99), or when its max grew by
+    // more than 8; a row that sees no key here keeps m_run = -inf.
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
     mx = fmaxf(mx, wave_xor32_f(mx));
-    issue(1);
     const bool raise = mx > (m_run == -INFINITY ? -0x1p99f : 8.0f);
-
     if (wave_any(raise)) {
       const float mb = m_run == -INFINITY ? 0.f : m_run;
       const float m_new = raise ? mb + mx : m_run;
@@ -318,19 +352,9 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdParams p) {
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) s[kb][i] -= shift;
+      ref_ready = !wave_any(m_run == -INFINITY);
     }
-
-    // P = exp2(s * scale*log2e - m), rounded to bf16 as the B operand of PV.
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float e = __builtin_amdgcn_exp2f(s[kb][i]);
-        l_run += e;
-        pf[2 * kb + (i >> 3)][i & 7] = (__bf16)e;
-      }
-      issue(2 + kb);
-    }
+    l_run += issued ? exps(std::false_type{}) : exps(std::true_type{});
   };
 
   // Global phases 2m and 2m+1 form pair m (m = 0 .. n_tiles).  Group 0 runs
