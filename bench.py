@@ -38,10 +38,10 @@ WORKLOAD = "llama8b-share-128k"
 # A figure is only reported while the kernel sources hash to what was
 # measured; after any change to them the roofline's traffic is null.
 MEASURED_TRAFFIC = {
-    "attn_bwd": {"bytes": 3.02407e10, "sources": ("attn_bwd.hip", "attn_f32.hip", "device_common.h"),
-                 "sha256_16": "7e3f38a1bda85833"},
-    "attn_fwd": {"bytes": 9.45191e9, "sources": ("attn_fwd.hip", "device_common.h"),
-                 "sha256_16": "d0d6ac6ad090fd3f"},
+    "attn_bwd": {"bytes": 2.99932e10, "sources": ("attn_bwd.hip", "attn_f32.hip", "device_common.h"),
+                 "sha256_16": "226921450229613c"},
+    "attn_fwd": {"bytes": 9.38435e9, "sources": ("attn_fwd.hip", "device_common.h"),
+                 "sha256_16": "682da4780d2e89a2"},
 }
 
 
@@ -65,6 +65,10 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=768,
                     help="query rows of the oracle's timed sample")
+    ap.add_argument("--pack-sets", type=int, default=4,
+                    help="distinct buffer sets the rotated exchange measurement cycles through")
+    ap.add_argument("--pack-reps", type=int, default=24,
+                    help="back-to-back launches per exchange in the rotated measurement")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="before timing, run one plain device-to-device copy of MIB MiB "
                          "(a known-size reference for hardware byte counters)")
@@ -215,6 +219,9 @@ def main():
     breakdown["pack_all"] = {"ms": pack_ms, "GB/s": gbps(pack_bytes, pack_ms),
                              "frac_of_hbm_peak": gbps(pack_bytes, pack_ms) / HBM_PEAK_GBPS}
 
+    rotated = measure_exchanges(w, uly, torch, stream, args.pack_sets, args.pack_reps)
+    breakdown["pack_rotated"] = rotated
+
     # Roofline of the dominant unit of the step, timed with events on the
     # stream its kernels run on.  The attention backward is one entry point
     # (ulysses_attn_bwd) that enqueues three kernels back to back: the D
@@ -268,6 +275,108 @@ def main():
     }
     print(json.dumps(line))
     return 0
+
+
+def measure_exchanges(w, uly, torch, stream, n_sets, reps):
+    """Throughput of the four layout exchanges of a step, each launched
+    `reps` times back to back while cycling through `n_sets` distinct buffer
+    sets (every set is larger than the 256 MB Infinity Cache together with
+    its neighbour, so each launch finds its data in HBM: cold numbers).  The
+    launch arguments are marshalled once per set, so the host stays ahead of
+    the GPU.  A device-to-device copy of the same bytes, rotated the same
+    way, is the practical ceiling."""
+    import ctypes
+
+    import numpy as np
+
+    lib = uly.load_library()
+    N, P, n, r = w.seqlen, w.P, w.n_local, w.rank
+    hl, kl, hd = w.hq_local, w.hkv_local, w.head_dim
+    bf = torch.bfloat16
+    st = stream.cuda_stream
+
+    def seq(heads):
+        return torch.empty((N, 1, heads, hd), dtype=bf, device="cuda")
+
+    def head(heads):
+        return torch.empty((N, 1, heads, hd), dtype=bf, device="cuda")
+
+    def chunks(t):
+        return [t[c * n:(c + 1) * n] for c in range(P)]
+
+    def batch_args(pairs):
+        descs, keep = uly._batch_descs(pairs)
+        return descs, keep
+
+    calls = {"pack_qkv": [], "unpack_o": [], "pack_do": [], "unpack_dqkv": []}
+    keep_alive = []
+    for _ in range(n_sets):
+        sq, sk, sv = seq(w.hq), seq(w.hkv), seq(w.hkv)
+        hq_, hk_, hv_ = head(hl), head(kl), head(kl)
+        so, ho = seq(w.hq), head(hl)
+        sdo, hdo = seq(w.hq), head(hl)
+        sdq, sdk, sdv = seq(w.hq), seq(w.hkv), seq(w.hkv)
+        hdq, hdk, hdv = head(hl), head(kl), head(kl)
+        keep_alive += [sq, sk, sv, hq_, hk_, hv_, so, ho, sdo, hdo, sdq, sdk, sdv, hdq, hdk, hdv]
+        d1, k1 = batch_args([(chunks(sq), hq_), (chunks(sk), hk_), (chunks(sv), hv_)])
+        d4, k4 = batch_args([(chunks(sdq), hdq), (chunks(sdk), hdk), (chunks(sdv), hdv)])
+        co, cdo = uly._ptr_array(chunks(so)), uly._ptr_array(chunks(sdo))
+        keep_alive += [d1, k1, d4, k4, co, cdo]
+        calls["pack_qkv"].append(lambda d=d1: lib.ulysses_seq_to_head_batch(
+            d, 3, P, r, n, 1, hd, uly.BF16, st))
+        calls["unpack_o"].append(lambda c=co, h=ho: lib.ulysses_head_to_seq(
+            h.data_ptr(), P, r, n, 1, w.hq, hd, uly.BF16, c, st))
+        calls["pack_do"].append(lambda c=cdo, h=hdo: lib.ulysses_seq_to_head(
+            c, P, r, n, 1, w.hq, hd, uly.BF16, h.data_ptr(), st))
+        calls["unpack_dqkv"].append(lambda d=d4: lib.ulysses_head_to_seq_batch(
+            d, 3, P, r, n, 1, hd, uly.BF16, st))
+    e = 2
+    nbytes = {"pack_qkv": 2.0 * N * (hl + 2 * kl) * hd * e, "unpack_o": 2.0 * N * hl * hd * e,
+              "pack_do": 2.0 * N * hl * hd * e, "unpack_dqkv": 2.0 * N * (hl + 2 * kl) * hd * e}
+
+    def timed(fns):
+        for f in fns:   # warm-up: one pass over every set
+            f()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(reps):
+            status = fns[i % len(fns)]()
+            if status not in (None, 0):
+                raise RuntimeError(f"exchange launch failed with status {status}")
+        b.record(stream)
+        b.synchronize()
+        return a.elapsed_time(b) / reps
+
+    out = {}
+    tot_ms, tot_b = 0.0, 0.0
+    for name, fns in calls.items():
+        ms = timed(fns)
+        out[name] = {"ms": ms, "GB/s": nbytes[name] / (ms * 1e-3) / 1e9}
+        tot_ms += ms
+        tot_b += nbytes[name]
+    out["all"] = {"ms": tot_ms, "GB/s": tot_b / (tot_ms * 1e-3) / 1e9,
+                  "frac_of_hbm_peak": tot_b / (tot_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+    del keep_alive, calls
+
+    # Practical ceiling: a plain device-to-device copy moving the bytes of the
+    # Q/K/V pack (read + write), rotated over the same number of buffer sets.
+    half = int(nbytes["pack_qkv"] // 2)
+    bufs = [(torch.empty(half, dtype=torch.uint8, device="cuda"),
+             torch.empty(half, dtype=torch.uint8, device="cuda")) for _ in range(n_sets)]
+    def copier(src, dst):
+        def f():
+            dst.copy_(src, non_blocking=True)
+        return f
+
+    copy_ms = timed([copier(s_, d_) for s_, d_ in bufs])
+    out["d2d_copy_same_bytes"] = {"ms": copy_ms, "GB/s": 2.0 * half / (copy_ms * 1e-3) / 1e9}
+    out["method"] = (f"{reps} back-to-back launches per exchange over {n_sets} rotating buffer "
+                     "sets (HBM-cold), one pair of HIP events on the launch stream")
+    del bufs
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(w, n_rows):
