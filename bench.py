@@ -229,7 +229,7 @@ def main():
     # five products of the backward (10 * hd flop per visible pair and head).
     # The forward is one kernel (2 products, 4 * hd flop per pair and head).
     units = {"attn_fwd": (fwd_flop, ["attn_fwd_bf16_kernel"]),
-             "attn_bwd": (bwd_flop, ["row_dot_kernel", "attn_bwd_dq_kernel", "attn_bwd_dkv_kernel"])}
+             "attn_bwd": (bwd_flop, ["bwd_stats_kernel", "attn_bwd_dq_kernel", "attn_bwd_dkv_kernel"])}
     dominant = max(units, key=lambda k_: avg[k_])
     flop, kernels = units[dominant]
     achieved = tflops(flop, avg[dominant])

@@ -176,7 +176,8 @@ ulysses_status_t ulysses_head_to_seq_batch(const ulysses_exchange_tensor_t* tens
  *            accumulation, O rounded to nearest even.  ULYSSES_FP32:
  *            head_dim 32, 64 or 128, fp32 throughout.
  *   seqlen == 0 is a no-op.  n_docs must lie in [1, seqlen] when cu_seqlens
- *   is given.
+ *   is given.  ERR_UNSUPPORTED for seqlen >= 2^30, bs * hq > 65535, or
+ *   (seqlen / 64 + 1) * (hq / hkv) >= 2^31.
  */
 ulysses_status_t ulysses_attn_fwd(const void* q, const void* k, const void* v, int64_t seqlen,
                                   int bs, int hq, int hkv, int head_dim, ulysses_dtype_t dtype,

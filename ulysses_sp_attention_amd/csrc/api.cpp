@@ -74,6 +74,10 @@ ulysses_status_t check_attn(int64_t seqlen, int bs, int hq, int hkv, int head_di
     if (!aligned4(cu)) return ULYSSES_ERR_ALIGNMENT;
   }
   if ((int64_t)bs * hq > 65535) return ULYSSES_ERR_UNSUPPORTED;   // grid.y of the launches
+  // The kernels count positions and 64-row query steps (over the heads of a
+  // GQA group) in 32 bits.
+  if (seqlen >= (int64_t(1) << 30) || (seqlen / 64 + 1) * (hq / hkv) >= (int64_t(1) << 31))
+    return ULYSSES_ERR_UNSUPPORTED;
   s->N = seqlen;
   s->bs = bs;
   s->hq = hq;

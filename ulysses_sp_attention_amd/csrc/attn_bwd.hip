@@ -10,7 +10,8 @@
 //   dV_j  = sum_{h in group} sum_i P_ij dO_i
 // P is recomputed from Q, K and the saved LSE; nothing of size N x N is
 // stored.  Three launches on the caller's stream:
-//   1. D for every query row (row_dot_kernel, in attn_f32.hip);
+//   1. bwd_stats_kernel: -D and -LSE log2(e) for every query row, into the
+//      workspace;
 //   2. dQ: a workgroup owns query rows (as in the forward) and walks the
 //      visible key tiles staged in LDS;
 //   3. dK, dV: a workgroup owns 128 key rows of one key/value head and walks
@@ -30,10 +31,6 @@
 
 namespace ulysses {
 
-template <typename T, int HD>
-hipError_t launch_row_dot(const T* o, const T* dout, float* D, const AttnShape& s,
-                          hipStream_t stream);
-
 namespace {
 
 struct BwdParams {
@@ -41,8 +38,8 @@ struct BwdParams {
   const __bf16* k;
   const __bf16* v;
   const __bf16* dout;
-  const float* lse;
-  const float* D;
+  const float* nlse2;   // -LSE log2(e), [batch][head][position]
+  const float* nD;      // -<dO, O>, same layout
   __bf16* dq;
   __bf16* dk;
   __bf16* dv;
@@ -137,8 +134,8 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_kernel(BwdParams p) {
     }
   }
   const int64_t stat = ((int64_t)b * p.hq + h) * N + qi;
-  const float lse2 = qi < N ? p.lse[stat] * kLog2e : 0.f;
-  const float Di = qi < N ? p.D[stat] : 0.f;
+  const float lse2 = qi < N ? -p.nlse2[stat] : 0.f;
+  const float Di = qi < N ? -p.nD[stat] : 0.f;
 
   const int64_t blk_last = (p0 + C::kBP < N ? p0 + C::kBP : N) - 1;
   const int64_t kv_lo = doc_start_of(p.cu, p.n_docs, p0);
@@ -272,25 +269,34 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_kernel(BwdParams p) {
 // ------------------------------------------------------------------------
 // dK, dV
 // ------------------------------------------------------------------------
-// dK, dV.  A workgroup of 8 waves owns 128 key rows of one key/value head as
-// 4 blocks of 32.  Each block is worked by the two waves that share a SIMD
-// (waves w and w + 4):
-//   the P wave holds the block's K rows and, for every 64-query step,
-//     computes S = Q K^T, P = exp(S - LSE) (handed over through LDS in fp32)
-//     and dV^T += dO^T P;
-//   the dS wave holds the V rows and, in the same phase, finishes the
-//     previous step (dS = P (dP - D), dK^T += Q^T dS) before computing
-//     dP = dO V^T of the current one.
-// Running the dS wave one step behind its partner leaves independent matrix
-// products in every phase for one wave while the other does exponentials or
-// dS arithmetic; one barrier per step hands P over.  Each wave carries one
-// accumulator set, so two waves fit per SIMD.
-// Steps walk the visible queries from the last 64-row tile down, over every
-// query head of the GQA group within a tile, so the GQA sum stays in
-// registers; no atomics, deterministic.  Q and dO tiles arrive by direct
-// global-to-LDS copies one step ahead; Q stays one step longer (the dS wave
-// reads Q^T a phase late), so it rotates through three buffers, and dO, LSE
-// and D through two.
+// A workgroup of 8 waves owns 128 key rows of one key/value head as 4
+// blocks of 32 keys; the two waves that share a SIMD (waves w and w + 4)
+// work block w.  The block walks the 64-query steps its keys see, over every
+// query head of the GQA group within a query tile, so the sum over the
+// group's heads stays in registers (no atomics: results are deterministic).
+// For step n:
+//   the P wave holds K' = K * scale * log2(e) (rounded to bf16 once) and
+//     forms S'_n = Q_n K'^T - LSE log2(e), whose accumulator starts at the
+//     negated statistic, so P_n = exp2(S'_n) needs no further arithmetic;
+//     then dV^T += dO^T P;
+//   the dS wave holds V and forms dP'_n = dO_n V^T - D (likewise seeded),
+//     dS = P dP' and dK^T += Q^T dS.
+// Each step is two phases separated by workgroup barriers.  In every phase
+// one wave of each SIMD issues only matrix products while its partner does
+// only vector work, which the SIMD executes alongside:
+//   phase A(n): P wave  S'_n, dV^T += dO_{n-1}^T P_{n-1}        (matrix)
+//               dS wave dS_{n-1} = P_{n-1} dP'_{n-1}, to bf16  (vector)
+//   phase B(n): P wave  mask, P_n = exp2(S'_n)                  (vector)
+//               dS wave dK^T += Q_{n-1}^T dS_{n-1}, dP'_n       (matrix)
+// P reaches the dS wave through LDS in fp32, one buffer per block.  Q and dO
+// tiles and the per-row statistics arrive by direct global-to-LDS copies
+// two steps ahead, issued in pieces through the vector phases (Q by the dS
+// waves, dO by the P waves).  A Q tile is read until phase B of the next
+// step, so Q rotates through four buffers (a compile-time rotation: the
+// step loop is unrolled four times) and dO through three (a run-time
+// rotation).  Every block computes every step, with an element mask where
+// not all of its keys see the step's queries, so all waves share one
+// schedule.  The statistics are produced by bwd_stats_kernel.
 template <int HD>
 struct DkvCfg {
   static constexpr int kPairs = 4;
@@ -298,339 +304,491 @@ struct DkvCfg {
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int kBK = 32 * kPairs;   // key rows per workgroup
   static constexpr int kBQ = 64;            // query rows per step
-  static constexpr int kSubs = kBQ / 32;
-  static_assert(kSubs == 2, "the interleaved schedules take two 32-row sub-tiles per step");
   static constexpr int kChunks = HD / 8;
   static constexpr int kRowBytes = HD * 2;
   static constexpr int kTileBytes = kBQ * kRowBytes;
-  static constexpr int kQBufs = 3, kDoBufs = 2;
-  static constexpr int kDoOff = kQBufs * kTileBytes;
-  static constexpr int kLseOff = kDoOff + kDoBufs * kTileBytes;
-  static constexpr int kDOff = kLseOff + kDoBufs * kBQ * 4;
-  static constexpr int kPOff = kDOff + kDoBufs * kBQ * 4;
-  static constexpr int kPSub = 16 * 64 * 4;          // a 32 x 32 fp32 P tile
-  static constexpr int kPBytes = kSubs * kPSub;      // one step of one pair
-  static constexpr int kSmem = kPOff + kPairs * 2 * kPBytes;
   static constexpr int kKS = HD / 16;
   static constexpr int kDB = HD / 32;
-  // The dS waves issue the copies of the next step, one 1 KB copy per wave
-  // per tensor and part, in kParts parts spread over their work.
-  static constexpr int kParts = kTileBytes / (16 * 64 * kPairs);
-  static_assert(kParts >= 1 && kParts <= 4 && kTileBytes % (16 * 64 * kPairs) == 0, "tile copies");
-  static_assert(2 * kBQ <= 64 * kPairs, "LSE and D staging");
+  static constexpr int kQBufs = 4, kDoBufs = 3;
+  // LDS: the statistics of the steps in flight, then Q, dO and P.
+  static constexpr int kStatBytes = kBQ * 4;
+  static constexpr int kLseOff = 0;
+  static constexpr int kDOff = kLseOff + kQBufs * kStatBytes;
+  static constexpr int kQOff = 2048;
+  static constexpr int kDoOff = kQOff + kQBufs * kTileBytes;
+  static constexpr int kPOff = kDoOff + kDoBufs * kTileBytes;
+  static constexpr int kPBytes = kBQ * 32 * 4;   // fp32 P of one block and step
+  static constexpr int kSmem = kPOff + kPairs * kPBytes;
+  // A wave-wide direct copy moves 1 KiB.  For each step a group of four
+  // waves copies one tile (kCopies slices per wave) and one 256-byte
+  // statistic (every wave of the group copies the same bytes).
+  static constexpr int kRowsPerCopy = 1024 / kRowBytes;
+  static constexpr int kCopies = kTileBytes / 1024 / kPairs;
+  static constexpr int kPhaseCopies = kCopies + 1;
+  static constexpr int kPrefetch = 4;   // LDS fragments read ahead of their product
+  static_assert(kDOff + kDoBufs * kStatBytes <= kQOff, "statistics region");
+  static_assert(kCopies >= 1 && kTileBytes % (1024 * kPairs) == 0, "tile copies");
+  static_assert(kSmem <= 160 * 1024, "LDS");
 };
 
-template <int HD, int PF>
+template <int HD>
 __global__ __launch_bounds__(512) void attn_bwd_dkv_kernel(BwdParams p) {
   using C = DkvCfg<HD>;
-  __shared__ __attribute__((aligned(16))) char smem[C::kSmem];
+  using std::false_type;
+  using std::integral_constant;
+  using std::true_type;
+  __shared__ __attribute__((aligned(1024))) char smem[C::kSmem];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int pair = wave & (C::kPairs - 1);
+  const int pair = wave & (C::kPairs - 1);   // key block; also the wave's index in its group
   const bool p_wave = wave < C::kPairs;
   const int half = lane >> 5;
   const int r32 = lane & 31;
 
-  const int64_t N = p.N;
+  const int64_t N = wave_uniform(p.N);
   const int kh = blockIdx.y % p.hkv;
   const int b = blockIdx.y / p.hkv;
   const int64_t k0 = (int64_t)blockIdx.x * C::kBK;   // heaviest (smallest keys) first
-  const int64_t kw = k0 + 32 * pair;                // first key row of this pair
-  const int64_t kj = kw + r32;                      // this lane's key row
+  const int64_t kw = k0 + 32 * pair;                // first key of the block
+  const int64_t kj = kw + r32;                      // this lane's key
 
   const int64_t q_tok = (int64_t)p.bs * p.hq * HD;
   const int64_t kv_tok = (int64_t)p.bs * p.hkv * HD;
   const int64_t kvoff = ((int64_t)b * p.hkv + kh) * HD;
 
-  // B operand rows of this lane: K (S = Q K^T) or V (dP = dO V^T).
-  const __bf16* brows = p_wave ? p.k : p.v;
+  // B operand rows of this lane: K' (P wave) or V (dS wave; the multiply by
+  // one leaves it exact).
   bf16x8_t bfrag[C::kKS];
+  {
+    const __bf16* rows = p_wave ? p.k : p.v;
+    const float mul = p_wave ? p.scale_log2 : 1.0f;
 #pragma unroll
-  for (int ks = 0; ks < C::kKS; ++ks)
-    bfrag[ks] = kj < N ? *reinterpret_cast<const bf16x8_t*>(brows + kj * kv_tok + kvoff + 16 * ks + 8 * half)
-                       : bf16x8_t{};
-  // queries that see key kj: [causal ? kj : doc_start(kj), doc_end(kj))
-  const int64_t my_lo = kj < N ? (p.causal ? kj : doc_start_of(p.cu, p.n_docs, kj)) : 0;
-  const int64_t my_hi = kj < N ? doc_end_of(p.cu, p.n_docs, kj, N) : 0;
+    for (int ks = 0; ks < C::kKS; ++ks) {
+      bf16x8_t raw = bf16x8_t{};
+      if (kj < N) raw = *reinterpret_cast<const bf16x8_t*>(rows + kj * kv_tok + kvoff + 16 * ks + 8 * half);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) bfrag[ks][e] = (__bf16)((float)raw[e] * mul);
+    }
+  }
 
-  // Workgroup- and pair-level bounds, held in scalar registers.
+  // Queries seen by the workgroup's keys: [q_lo, q_hi).  Steps walk its
+  // 64-row query tiles from the last one down (concurrent workgroups then
+  // read the same tiles), every head of the group within a tile.
   const int64_t k_last = (k0 + C::kBK < N ? k0 + C::kBK : N) - 1;
-  const int64_t q_lo = wave_uniform(p.causal ? k0 : doc_start_of(p.cu, p.n_docs, k0));
-  const int64_t q_hi = wave_uniform(doc_end_of(p.cu, p.n_docs, k_last, N));
-  const bool pair_active = kw < N;
-  const int64_t w_last = pair_active ? (kw + 31 < N ? kw + 31 : N - 1) : 0;
-  const int64_t w_lo = wave_uniform(pair_active ? (p.causal ? kw : doc_start_of(p.cu, p.n_docs, kw)) : 0);
-  const int64_t w_hi = wave_uniform(pair_active ? doc_end_of(p.cu, p.n_docs, w_last, N) : 0);
-  // Queries seen by every key of the pair: [full_lo, full_hi).
-  const int64_t full_lo =
-      wave_uniform(pair_active ? (p.causal ? w_last : doc_start_of(p.cu, p.n_docs, w_last)) : 0);
-  const int64_t full_hi = wave_uniform(pair_active ? doc_end_of(p.cu, p.n_docs, kw, N) : 0);
+  const int64_t q_lo = p.causal ? k0 : doc_start_of(p.cu, p.n_docs, k0);
+  const int64_t q_hi = doc_end_of(p.cu, p.n_docs, k_last, N);
+  const int qt_lo = (int)wave_uniform(q_lo / C::kBQ);
+  const int qt_hi = (int)wave_uniform((q_hi + C::kBQ - 1) / C::kBQ);
+  const int n_steps = (qt_hi - qt_lo) * p.g;
+  const int t_tail = (int)wave_uniform(N / C::kBQ);   // tiles from here on run past N
+  // Query positions from here on are relative to the first query tile
+  // (32-bit, so that tile-level tests are scalar compares).
+  const int64_t q_base = (int64_t)qt_lo * C::kBQ;
+  // Queries that see key kj: [my_lo, my_hi).
+  const int my_lo = kj < N ? (int)((p.causal ? kj : doc_start_of(p.cu, p.n_docs, kj)) - q_base) : 0;
+  const int my_hi = kj < N ? (int)(doc_end_of(p.cu, p.n_docs, kj, N) - q_base) : 0;
+  // Queries seen by every key of the block: [flo, fhi).
+  const bool blk_active = kw < N;
+  const int64_t w_last = blk_active ? (kw + 31 < N ? kw + 31 : N - 1) : 0;
+  const int flo = blk_active
+      ? (int)wave_uniform((p.causal ? w_last : doc_start_of(p.cu, p.n_docs, w_last)) - q_base) : 0;
+  const int fhi = blk_active ? (int)wave_uniform(doc_end_of(p.cu, p.n_docs, kw, N) - q_base) : 0;
 
-  const int64_t qt_lo = q_lo / C::kBQ;
-  const int64_t qt_hi = (q_hi + C::kBQ - 1) / C::kBQ;
-  const int64_t n_steps = (qt_hi - qt_lo) * p.g;
-
-  // Stages step (query tile t, head kh*g + hh): Q into Q buffer qb and dO
-  // into dO buffer db by direct copies issued by the dS waves (rows past N
-  // repeat row N-1; every pair that reads them is masked), in kParts parts
-  // so that the copies interleave with matrix products instead of queueing
-  // at once; LSE (log2 units) and D through registers of the dS waves,
-  // published by publish_stats once the copies have landed.
-  const int dtid = tid - 64 * C::kPairs;   // thread index among the dS waves
-  // Tile row and source chunk of this lane's 16 bytes in each part, and
-  // their element offset within the step's rows.
-  int part_row[C::kParts];
-  int64_t part_off[C::kParts];
+  // --- direct copies -----------------------------------------------------
+  // Slice c of this wave lands at bytes [1024 cidx, 1024 cidx + 1024) of a
+  // tile buffer, lane l at +16 l, so lane l fetches the source chunk that
+  // the swizzle places there.  Rows past N repeat row N-1 (the tail tile);
+  // those queries are masked for every key, so only finiteness matters.
+  const int64_t row_bytes = q_tok * 2;
+  uint32_t slice_off[C::kCopies];
 #pragma unroll
-  for (int j = 0; j < C::kParts; ++j) {
-    const int piece = (j * C::kPairs + pair) * 64 + lane;
-    part_row[j] = piece / C::kChunks;
-    const int ch = (piece % C::kChunks) ^ swz_f<C::kChunks>(part_row[j]);
-    part_off[j] = part_row[j] * q_tok + ch * 8;
+  for (int c = 0; c < C::kCopies; ++c) {
+    const int cidx = pair * C::kCopies + c;
+    const int row0 = cidx * C::kRowsPerCopy + lane / C::kChunks;
+    const int col = ((lane % C::kChunks) ^ swz_f<C::kChunks>(row0)) * 16;
+    slice_off[c] = (uint32_t)(row0 * row_bytes) + (uint32_t)col;
   }
-  float sst = 0.f;
-  auto issue_part = [&](int j, int64_t t, int hh, int qb, int db) {
-    const int h = kh * p.g + hh;
-    const int64_t qoff = ((int64_t)b * p.hq + h) * HD;
-    const int64_t i0 = t * C::kBQ;
-    const int slot = (j * C::kPairs + pair) * 64;   // first 16-byte slot of this copy
-    int64_t e = i0 * q_tok + qoff + part_off[j];
-    if (i0 + C::kBQ > N && i0 + part_row[j] >= N)   // last tile: repeat row N-1
-      e -= (i0 + part_row[j] - (N - 1)) * q_tok;
-    load_lds16(p.q + e, smem + qb * C::kTileBytes + slot * 16);
-    load_lds16(p.dout + e, smem + C::kDoOff + db * C::kTileBytes + slot * 16);
-    if (j == 0 && dtid >= 0 && dtid < 2 * C::kBQ) {
-      const int64_t qs = i0 + (dtid % C::kBQ);
-      const int64_t idx = ((int64_t)b * p.hq + h) * N + qs;
-      // LSE in log2 units; D negated (it seeds the dP accumulator)
-      sst = qs < N ? (dtid < C::kBQ ? p.lse[idx] * kLog2e : -p.D[idx]) : 0.f;
+  // A step: its query tile t and head index hh within the group.
+  struct Cursor {
+    int t, hh, n;
+  };
+  // Next step, or the same one at the last step (copies past the end repeat
+  // the last step's data into buffers nobody reads again).
+  auto advance = [&](Cursor& c) __attribute__((always_inline)) {
+    if (c.n + 1 < n_steps) {
+      ++c.n;
+      if (++c.hh == p.g) {
+        c.hh = 0;
+        --c.t;
+      }
     }
   };
-  auto publish_stats = [&](int qb, int db) {
-    if (dtid >= 0 && dtid < C::kBQ)
-      reinterpret_cast<float*>(smem + C::kLseOff)[db * C::kBQ + dtid] = sst;
-    else if (dtid >= C::kBQ && dtid < 2 * C::kBQ)
-      reinterpret_cast<float*>(smem + C::kDOff)[db * C::kBQ + dtid - C::kBQ] = sst;
+  // Part k of a group's copies for step c: tile slices k < kCopies of Q (or
+  // dO) into tile buffer `tile`, then at k == kCopies its statistic -LSE
+  // log2(e) (or -D) into `stat`.
+  auto copy_part = [&](auto q_tag, const Cursor& c, int k, char* tile, char* stat)
+      __attribute__((always_inline)) {
+    constexpr bool kQ = decltype(q_tag)::value;
+    const int h = kh * p.g + c.hh;
+    const int64_t i0 = (int64_t)c.t * C::kBQ;
+    if (k < C::kCopies) {
+      const __bf16* src = kQ ? p.q : p.dout;
+      const char* base = reinterpret_cast<const char*>(
+          wave_uniform(reinterpret_cast<int64_t>(src + i0 * q_tok + ((int64_t)b * p.hq + h) * HD)));
+      const int cidx = pair * C::kCopies + k;
+      uint32_t off = slice_off[k];
+      if (c.t >= t_tail) {
+        const int last = (int)(N - 1 - i0);
+        const int row0 = cidx * C::kRowsPerCopy + lane / C::kChunks;
+        const int col = ((lane % C::kChunks) ^ swz_f<C::kChunks>(row0)) * 16;
+        off = (uint32_t)((row0 < last ? row0 : last) * row_bytes) + (uint32_t)col;
+      }
+      copy_lds16_async_sbase(base, off, tile + cidx * 1024);
+    } else if (k == C::kCopies) {
+      const float* src = kQ ? p.nlse2 : p.nD;
+      const char* base = reinterpret_cast<const char*>(
+          wave_uniform(reinterpret_cast<int64_t>(src + ((int64_t)b * p.hq + h) * N + i0)));
+      int row = lane;
+      if (c.t >= t_tail) {
+        const int last = (int)(N - 1 - i0);
+        row = lane < last ? lane : last;
+      }
+      copy_lds4_async_sbase(base, (uint32_t)row * 4u, stat);
+    }
+    __builtin_amdgcn_sched_barrier(0);
   };
+  auto q_tile = [&](int slot) __attribute__((always_inline)) { return smem + C::kQOff + slot * C::kTileBytes; };
+  auto do_tile = [&](int slot) __attribute__((always_inline)) { return smem + C::kDoOff + slot * C::kTileBytes; };
+  auto lse_stat = [&](int slot) __attribute__((always_inline)) { return smem + C::kLseOff + slot * C::kStatBytes; };
+  auto d_stat = [&](int slot) __attribute__((always_inline)) { return smem + C::kDOff + slot * C::kStatBytes; };
 
+  // --- LDS operands --------------------------------------------------------
+  // Row reads (A rows = 32 queries from row0): the swizzle depends on the low
+  // four row bits only, so the 32-row sub-tile adds a constant offset.
+  int roff[C::kKS];
+#pragma unroll
+  for (int ks = 0; ks < C::kKS; ++ks) roff[ks] = swz<C::kChunks, C::kRowBytes>(r32, 2 * ks + half);
   const TrReader<C::kChunks, C::kRowBytes, C::kDB> tr(lane);
-
-  if (n_steps > 0 && !p_wave) {
+  auto row_frag = [&](const char* tile, int idx) __attribute__((always_inline)) {
+    return *reinterpret_cast<const bf16x8_t*>(tile + (idx & 1) * 32 * C::kRowBytes + roff[idx >> 1]);
+  };
+  // Accumulator seed: the statistic of the 16 query rows this lane holds in
+  // sub-tile `sub` (element 4 r4 + e is row 32 sub + 8 r4 + 4 half + e).
+  auto load_seed = [&](const char* stat, int sub) __attribute__((always_inline)) {
+    f32x16_t v;
 #pragma unroll
-    for (int j = 0; j < C::kParts; ++j) issue_part(j, qt_hi - 1, 0, 0, 0);
-    wait_vmem();
-    publish_stats(0, 0);
-  }
-  __syncthreads();
-
-  // The step loop, instantiated once per role so that each role's
-  // accumulators stay in place; both instances pass the same barriers.
-  auto run = [&](auto role) {
-    constexpr bool kP = decltype(role)::value;
-    f32x16_t acc[C::kDB];   // dV^T (P waves) or dK^T (dS waves)
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const f32x4_t x = *reinterpret_cast<const f32x4_t*>(stat + 4 * (32 * sub + 8 * r4 + 4 * half));
 #pragma unroll
-    for (int db = 0; db < C::kDB; ++db) acc[db] = f32x16_t{};
-    f32x16_t dp_prev[C::kSubs];   // dS waves: dP - D of the previous step
-#pragma unroll
-    for (int sub = 0; sub < C::kSubs; ++sub) dp_prev[sub] = f32x16_t{};
-
-    int64_t t = qt_hi - 1;
-    int hh = 0, qb = 0, db = 0;
-    bool prev_vis = false;
-    int prev_qb = 0;
-    for (int64_t n = 0; n <= n_steps; ++n) {
-      const bool cur = n < n_steps;
-      const bool has_next = n + 1 < n_steps;
-      const int nqb = qb == C::kQBufs - 1 ? 0 : qb + 1;
-      const int ndb = db ^ 1;
-      const int64_t nt = hh + 1 < p.g ? t : t - 1;
-      const int nhh = hh + 1 < p.g ? hh + 1 : 0;
-      // dS waves: part i of the next step's copies goes out at point i.
-      auto issue_at = [&](int i) {
-        if (!kP && has_next && i < C::kParts) issue_part(i, nt, nhh, nqb, ndb);
-      };
-      const int64_t i0 = t * C::kBQ;
-      const bool vis = cur && pair_active && i0 < w_hi && i0 + C::kBQ > w_lo;
-      const char* tq = smem + qb * C::kTileBytes;
-      const char* tdo = smem + C::kDoOff + db * C::kTileBytes;
-      char* pbuf = smem + C::kPOff + (2 * pair + (int)(n & 1)) * C::kPBytes;
-
-      if constexpr (kP) {
-        if (vis) {
-          const float* tlse = reinterpret_cast<const float*>(smem + C::kLseOff) + db * C::kBQ;
-          // S = Q K^T for both 32-row sub-tiles: lane holds key kj and 16
-          // query rows of each.
-          f32x16_t s[C::kSubs];
-#pragma unroll
-          for (int sub = 0; sub < C::kSubs; ++sub) s[sub] = f32x16_t{};
-          {
-            // A fragments read PF products ahead, over both sub-tiles.
-            constexpr int kN = C::kSubs * C::kKS;
-            auto afrag = [&](int i) {
-              return *reinterpret_cast<const bf16x8_t*>(
-                  tq + swz<C::kChunks, C::kRowBytes>(32 * (i / C::kKS) + r32, 2 * (i % C::kKS) + half));
-            };
-            bf16x8_t buf[PF + 1];
-#pragma unroll
-            for (int i = 0; i < PF; ++i) buf[i] = afrag(i);
-#pragma unroll
-            for (int i = 0; i < kN; ++i) {
-              if (i + PF < kN) buf[(i + PF) % (PF + 1)] = afrag(i + PF);
-              s[i / C::kKS] = mfma32(buf[i % (PF + 1)], bfrag[i % C::kKS], s[i / C::kKS]);
-              __builtin_amdgcn_sched_barrier(0);
-            }
-          }
-          bf16x8_t pf[C::kSubs][2];
-#pragma unroll
-          for (int sub = 0; sub < C::kSubs; ++sub) {
-            const int64_t s0 = i0 + 32 * sub;
-            // On sub-tiles that cross a boundary (or that this pair does
-            // not see at all), scores of invisible (query, key) pairs become
-            // -inf, so their P is exactly 0.
-            if (s0 < full_lo || s0 + 32 > full_hi) {
-              const int lo = (int)(my_lo - s0 < -1 ? -1 : (my_lo - s0 > 33 ? 33 : my_lo - s0));
-              const int hi = (int)(my_hi - s0 < -1 ? -1 : (my_hi - s0 > 33 ? 33 : my_hi - s0));
-#pragma unroll
-              for (int i = 0; i < 16; ++i) {
-                const int qr = 8 * (i >> 2) + 4 * half + (i & 3);
-                if (qr < lo || qr >= hi) s[sub][i] = -INFINITY;
-              }
-            }
-            float* pt = reinterpret_cast<float*>(pbuf + sub * C::kPSub);
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-              const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(tlse + 32 * sub + 8 * r4 + 4 * half);
-              f32x4_t p4;
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                p4[e] = __builtin_amdgcn_exp2f(fmaf(s[sub][4 * r4 + e], p.scale_log2, -l4[e]));
-                pf[sub][r4 >> 1][4 * (r4 & 1) + e] = (__bf16)p4[e];
-              }
-              *reinterpret_cast<f32x4_t*>(pt + 4 * (64 * r4 + lane)) = p4;
-            }
-            // dV^T += dO^T P over the sub-tile's two 16-row steps, the
-            // transposed A fragments read PF products ahead.
-            {
-              constexpr int kN = 2 * C::kDB;
-              auto tfrag = [&](int i) { return tr.load(tdo, 32 * sub + 16 * (i / C::kDB), i % C::kDB); };
-              bf16x8_t buf[PF + 1];
-#pragma unroll
-              for (int i = 0; i < PF; ++i) buf[i] = tfrag(i);
-#pragma unroll
-              for (int i = 0; i < kN; ++i) {
-                if (i + PF < kN) buf[(i + PF) % (PF + 1)] = tfrag(i + PF);
-                acc[i % C::kDB] = mfma32(buf[i % (PF + 1)], pf[sub][i / C::kDB], acc[i % C::kDB]);
-                __builtin_amdgcn_sched_barrier(0);
-              }
-            }
-          }
-        }
-      } else {
-        // Finish the previous step, one sub-tile at a time:
-        // dS = P (dP - D), dK^T += Q^T dS; the next step's copies go out
-        // between the stages.
-        issue_at(0);
-        const char* pq = smem + prev_qb * C::kTileBytes;
-        const char* ppbuf = smem + C::kPOff + (2 * pair + (int)((n - 1) & 1)) * C::kPBytes;
-#pragma unroll
-        for (int sub = 0; sub < C::kSubs; ++sub) {
-          if (prev_vis) {
-            const float* pt = reinterpret_cast<const float*>(ppbuf + sub * C::kPSub);
-            bf16x8_t dsf[2];
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-              const f32x4_t p4 = *reinterpret_cast<const f32x4_t*>(pt + 4 * (64 * r4 + lane));
-#pragma unroll
-              for (int e = 0; e < 4; ++e)
-                dsf[r4 >> 1][4 * (r4 & 1) + e] = (__bf16)(p4[e] * dp_prev[sub][4 * r4 + e]);
-            }
-            {
-              constexpr int kN = 2 * C::kDB;
-              auto tfrag = [&](int i) { return tr.load(pq, 32 * sub + 16 * (i / C::kDB), i % C::kDB); };
-              bf16x8_t buf[PF + 1];
-#pragma unroll
-              for (int i = 0; i < PF; ++i) buf[i] = tfrag(i);
-#pragma unroll
-              for (int i = 0; i < kN; ++i) {
-                if (i + PF < kN) buf[(i + PF) % (PF + 1)] = tfrag(i + PF);
-                acc[i % C::kDB] = mfma32(buf[i % (PF + 1)], dsf[i / C::kDB], acc[i % C::kDB]);
-                __builtin_amdgcn_sched_barrier(0);
-              }
-            }
-          }
-          issue_at(1 + sub);
-        }
-        issue_at(3);
-        // dP - D = dO V^T - D for both sub-tiles (the accumulators start at
-        // -D), finished in the next phase; A fragments read PF products
-        // ahead.
-        if (vis) {
-          const float* tnd = reinterpret_cast<const float*>(smem + C::kDOff) + db * C::kBQ;
-          constexpr int kN = C::kSubs * C::kKS;
-          auto afrag = [&](int i) {
-            return *reinterpret_cast<const bf16x8_t*>(
-                tdo + swz<C::kChunks, C::kRowBytes>(32 * (i / C::kKS) + r32, 2 * (i % C::kKS) + half));
-          };
-#pragma unroll
-          for (int sub = 0; sub < C::kSubs; ++sub)
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-              const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(tnd + 32 * sub + 8 * r4 + 4 * half);
-#pragma unroll
-              for (int e = 0; e < 4; ++e) dp_prev[sub][4 * r4 + e] = d4[e];
-            }
-          bf16x8_t buf[PF + 1];
-#pragma unroll
-          for (int i = 0; i < PF; ++i) buf[i] = afrag(i);
-#pragma unroll
-          for (int i = 0; i < kN; ++i) {
-            if (i + PF < kN) buf[(i + PF) % (PF + 1)] = afrag(i + PF);
-            dp_prev[i / C::kKS] = mfma32(buf[i % (PF + 1)], bfrag[i % C::kKS], dp_prev[i / C::kKS]);
-            __builtin_amdgcn_sched_barrier(0);
-          }
-        }
-      }
-
-      if (has_next && !kP) {
-        wait_vmem();   // this wave's copies of the next step have landed
-        publish_stats(nqb, ndb);
-      }
-      __syncthreads();
-
-      prev_vis = vis;
-      prev_qb = qb;
-      qb = nqb;
-      db = ndb;
-      if (++hh == p.g) {
-        hh = 0;
-        --t;
-      }
+      for (int e = 0; e < 4; ++e) v[4 * r4 + e] = x[e];
     }
+    return v;
+  };
+  // fp32 P of the block: [sub][r4][lane] x 4 floats (accumulator order).
+  char* const pbuf = smem + C::kPOff + pair * C::kPBytes;
+  auto p_slot = [&](int sub, int r4) __attribute__((always_inline)) {
+    return reinterpret_cast<f32x4_t*>(pbuf + ((sub * 4 + r4) * 64 + lane) * 16);
+  };
 
-    if (kj < N) {
-      __bf16* row = (kP ? p.dv : p.dk) + kj * kv_tok + kvoff;
-      const float mul = kP ? 1.f : p.scale;
+  f32x16_t acc[C::kDB];   // dV^T (P waves) or dK^T (dS waves)
 #pragma unroll
-      for (int d = 0; d < C::kDB; ++d)
+  for (int db = 0; db < C::kDB; ++db) acc[db] = f32x16_t{};
+
+  // ======================= P waves =======================================
+  auto run_p = [&]() __attribute__((always_inline)) {
+    f32x16_t s[2];        // S' of the current step, two 32-query sub-tiles
+    bf16x8_t pf[2][2];    // bf16 P of the previous step, B operand of dV
+    // Matrix phase: S' of a step from Q tile lq seeded from statistic lst
+    // (QK), and dV^T += dO^T P of the previous step from dO tile ldo (PV).
+    auto matrix = [&](auto qk_tag, auto pv_tag, const char* lq, const char* lst, const char* ldo)
+        __attribute__((always_inline)) {
+      constexpr bool kQK = decltype(qk_tag)::value;
+      constexpr bool kPV = decltype(pv_tag)::value;
+      constexpr int NQ = kQK ? 2 * C::kKS : 0;   // (ks, sub), sub fastest
+      constexpr int NP = kPV ? 4 * C::kDB : 0;   // (16-row step, db), db fastest
+      constexpr int NS = NQ + NP;
+      constexpr int PF = C::kPrefetch < NS ? C::kPrefetch : NS;
+      auto frag = [&](int idx) __attribute__((always_inline)) {
+        return idx < NQ ? row_frag(lq, idx) : tr.load(ldo, 16 * ((idx - NQ) / C::kDB), (idx - NQ) % C::kDB);
+      };
+      bf16x8_t buf[PF + 1];
+#pragma unroll
+      for (int i = 0; i < PF; ++i) buf[i] = frag(i);
+      if constexpr (kQK) {
+        s[0] = load_seed(lst, 0);
+        s[1] = load_seed(lst, 1);
+      }
+#pragma unroll
+      for (int idx = 0; idx < NS; ++idx) {
+        if (idx + PF < NS) buf[(idx + PF) % (PF + 1)] = frag(idx + PF);
+        if (idx < NQ) {
+          s[idx & 1] = mfma32(buf[idx % (PF + 1)], bfrag[idx >> 1], s[idx & 1]);
+        } else {
+          const int i = idx - NQ, st = i / C::kDB;
+          acc[i % C::kDB] = mfma32(buf[idx % (PF + 1)], pf[st >> 1][st & 1], acc[i % C::kDB]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    // Vector phase of a step whose first query is i0r: mask, exponentials,
+    // P to LDS; issue(k), k = 0..4, issues part k of the dO copies.
+    auto vector = [&](int i0r, auto issue) __attribute__((always_inline)) {
+      issue(0);
+      // Element mask without compares: with [lo, hi) the visible queries of
+      // this lane's key as offsets into the sub-tile, each score gets
+      // clamp(min(q - lo, hi - 1 - q), -1, 0) * 2^100 added: exactly 0 when
+      // visible; otherwise the score becomes exactly -2^100 (the score itself
+      // is absorbed) and its probability exactly 0.
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        const int s0 = i0r + 32 * sub;
+        if (s0 < flo || s0 + 32 > fhi) {
+          // Offsets clamped to [-1, 33], then shifted by this lane's 4*half
+          // so that every element uses a constant query offset.
+          const float neg_lo = (float)(4 * half - min(max(my_lo - s0, -1), 33));
+          const float hi_m1 = (float)(min(max(my_hi - s0, -1), 33) - 1 - 4 * half);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float j = (float)(8 * (i >> 2) + (i & 3));   // query offset minus 4*half
+            const float d = __builtin_amdgcn_fmed3f(fminf(j + neg_lo, hi_m1 - j), -1.0f, 0.0f);
+            s[sub][i] = fmaf(d, 0x1p100f, s[sub][i]);
+          }
+        }
+      }
+      issue(1);
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
-          bf16x4_t w;
+          f32x4_t p4;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = (__bf16)(acc[d][4 * r4 + e] * mul);
-          *reinterpret_cast<bf16x4_t*>(row + d * 32 + 8 * r4 + 4 * half) = w;
+          for (int e = 0; e < 4; ++e) {
+            p4[e] = __builtin_amdgcn_exp2f(s[sub][4 * r4 + e]);
+            pf[sub][r4 >> 1][4 * (r4 & 1) + e] = (__bf16)p4[e];
+          }
+          *p_slot(sub, r4) = p4;
         }
+        issue(2 + sub);
+      }
+      issue(4);
+    };
+
+    Cursor cur{qt_hi - 1, 0, 0};   // step being computed
+    Cursor cp = cur;               // step whose dO copies go out next
+    auto issue_to = [&](int slot) __attribute__((always_inline)) {
+      return [&, slot](int k) __attribute__((always_inline)) {
+        copy_part(false_type{}, cp, k, do_tile(slot), d_stat(slot));
+      };
+    };
+    // Prologue: dO and D of steps 0 and 1.
+#pragma unroll
+    for (int k = 0; k <= C::kCopies; ++k) copy_part(false_type{}, cp, k, do_tile(0), d_stat(0));
+    advance(cp);
+#pragma unroll
+    for (int k = 0; k <= C::kCopies; ++k) copy_part(false_type{}, cp, k, do_tile(1), d_stat(1));
+    advance(cp);
+    block_barrier();
+    // Step 0: scores only.
+    matrix(true_type{}, false_type{}, q_tile(0), lse_stat(0), do_tile(0));
+    wait_vmem_n<C::kPhaseCopies>();
+    block_barrier();
+    vector((cur.t - qt_lo) * C::kBQ, issue_to(2));
+    advance(cp);
+    block_barrier();
+    advance(cur);
+    int dslot = 1;   // dO buffer of the current step: n % 3
+    auto step = [&](auto r_tag) __attribute__((always_inline)) {
+      constexpr int r = decltype(r_tag)::value;   // n % 4
+      const int prev = dslot == 0 ? 2 : dslot - 1;  // (n - 1) % 3 == (n + 2) % 3
+      matrix(true_type{}, true_type{}, q_tile(r), lse_stat(r), do_tile(prev));
+      wait_vmem_n<C::kPhaseCopies>();
+      block_barrier();
+      vector((cur.t - qt_lo) * C::kBQ, issue_to(prev));
+      advance(cp);
+      block_barrier();
+      advance(cur);
+      dslot = dslot == 2 ? 0 : dslot + 1;
+    };
+    for (int n = 1; n < n_steps; n += 4) {
+      step(integral_constant<int, 1>{});
+      if (n + 1 < n_steps) step(integral_constant<int, 2>{});
+      if (n + 2 < n_steps) step(integral_constant<int, 3>{});
+      if (n + 3 < n_steps) step(integral_constant<int, 0>{});
     }
+    // Phase A after the last step: dV of the last step only.
+    matrix(false_type{}, true_type{}, q_tile(0), lse_stat(0), do_tile(dslot == 0 ? 2 : dslot - 1));
+    block_barrier();
   };
-  if (p_wave)
-    run(std::true_type{});
-  else
-    run(std::false_type{});
+
+  // ======================= dS waves ======================================
+  auto run_ds = [&]() __attribute__((always_inline)) {
+    f32x16_t dp[2];       // dP' of the current step, two 32-query sub-tiles
+    bf16x8_t dsf[2][2];   // bf16 dS of the previous step, B operand of dK
+    // Matrix phase: dK^T += Q^T dS of the previous step from Q tile lq (DK),
+    // and dP' of a step from dO tile ldo seeded from statistic lst (DP).
+    auto matrix = [&](auto dk_tag, auto dp_tag, const char* lq, const char* ldo, const char* lst)
+        __attribute__((always_inline)) {
+      constexpr bool kDK = decltype(dk_tag)::value;
+      constexpr bool kDP = decltype(dp_tag)::value;
+      constexpr int NK = kDK ? 4 * C::kDB : 0;   // (16-row step, db), db fastest
+      constexpr int ND = kDP ? 2 * C::kKS : 0;   // (ks, sub), sub fastest
+      constexpr int NS = NK + ND;
+      constexpr int PF = C::kPrefetch < NS ? C::kPrefetch : NS;
+      auto frag = [&](int idx) __attribute__((always_inline)) {
+        return idx < NK ? tr.load(lq, 16 * (idx / C::kDB), idx % C::kDB) : row_frag(ldo, idx - NK);
+      };
+      bf16x8_t buf[PF + 1];
+#pragma unroll
+      for (int i = 0; i < PF; ++i) buf[i] = frag(i);
+      if constexpr (kDP) {
+        dp[0] = load_seed(lst, 0);
+        dp[1] = load_seed(lst, 1);
+      }
+#pragma unroll
+      for (int idx = 0; idx < NS; ++idx) {
+        if (idx + PF < NS) buf[(idx + PF) % (PF + 1)] = frag(idx + PF);
+        if (idx < NK) {
+          const int st = idx / C::kDB;
+          acc[idx % C::kDB] = mfma32(buf[idx % (PF + 1)], dsf[st >> 1][st & 1], acc[idx % C::kDB]);
+        } else {
+          const int j = idx - NK;
+          dp[j & 1] = mfma32(buf[idx % (PF + 1)], bfrag[j >> 1], dp[j & 1]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    // Vector phase: dS = P dP' of the previous step, to bf16; issue(k),
+    // k = 0..4, issues part k of the Q copies.
+    auto vector = [&](auto issue) __attribute__((always_inline)) {
+      f32x4_t p4[2][4];
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) p4[sub][r4] = *p_slot(sub, r4);
+      issue(0);
+      issue(1);
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            dsf[sub][r4 >> 1][4 * (r4 & 1) + e] = (__bf16)(p4[sub][r4][e] * dp[sub][4 * r4 + e]);
+        issue(2 + sub);
+      }
+      issue(4);
+    };
+
+    Cursor cq{qt_hi - 1, 0, 0};   // step whose Q copies go out next
+    auto issue_to = [&](int slot) __attribute__((always_inline)) {
+      return [&, slot](int k) __attribute__((always_inline)) {
+        copy_part(true_type{}, cq, k, q_tile(slot), lse_stat(slot));
+      };
+    };
+    auto no_issue = [](int) {};
+    // Prologue: Q and LSE of steps 0 and 1; step 0's must land before A(0).
+#pragma unroll
+    for (int k = 0; k <= C::kCopies; ++k) copy_part(true_type{}, cq, k, q_tile(0), lse_stat(0));
+    advance(cq);
+#pragma unroll
+    for (int k = 0; k <= C::kCopies; ++k) copy_part(true_type{}, cq, k, q_tile(1), lse_stat(1));
+    advance(cq);
+    wait_vmem_n<C::kPhaseCopies>();
+    block_barrier();
+    // Step 0: phase A only copies, phase B forms dP'.
+    {
+      auto issue = issue_to(2);
+#pragma unroll
+      for (int k = 0; k <= C::kCopies; ++k) issue(k);
+    }
+    advance(cq);
+    block_barrier();
+    matrix(false_type{}, true_type{}, q_tile(0), do_tile(0), d_stat(0));
+    wait_vmem_n<C::kPhaseCopies>();
+    block_barrier();
+    int dslot = 1;   // dO buffer of the current step: n % 3
+    auto step = [&](auto r_tag) __attribute__((always_inline)) {
+      constexpr int r = decltype(r_tag)::value;   // n % 4
+      vector(issue_to((r + 2) & 3));
+      advance(cq);
+      block_barrier();
+      matrix(true_type{}, true_type{}, q_tile((r + 3) & 3), do_tile(dslot), d_stat(dslot));
+      wait_vmem_n<C::kPhaseCopies>();
+      block_barrier();
+      dslot = dslot == 2 ? 0 : dslot + 1;
+    };
+    for (int n = 1; n < n_steps; n += 4) {
+      step(integral_constant<int, 1>{});
+      if (n + 1 < n_steps) step(integral_constant<int, 2>{});
+      if (n + 2 < n_steps) step(integral_constant<int, 3>{});
+      if (n + 3 < n_steps) step(integral_constant<int, 0>{});
+    }
+    // After the last step: its dS (phase A), then its dK product (phase B).
+    vector(no_issue);
+    block_barrier();
+    matrix(true_type{}, false_type{}, q_tile((n_steps - 1) & 3), do_tile(0), d_stat(0));
+  };
+
+  if (n_steps > 0) {
+    if (p_wave)
+      run_p();
+    else
+      run_ds();
+  }
+  // No copy may still be writing LDS when the workgroup ends.
+  wait_vmem();
+
+  if (kj < N) {
+    __bf16* row = (p_wave ? p.dv : p.dk) + kj * kv_tok + kvoff;
+    const float mul = p_wave ? 1.f : p.scale;
+#pragma unroll
+    for (int d = 0; d < C::kDB; ++d)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        bf16x4_t w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (__bf16)(acc[d][4 * r4 + e] * mul);
+        *reinterpret_cast<bf16x4_t*>(row + d * 32 + 8 * r4 + 4 * half) = w;
+      }
+  }
 }
 
-// LDS fragments read this many products ahead in the dK/dV kernel.
-constexpr int kDkvPrefetch = 3;
+// -D_i = -<dO_i, O_i> and -LSE_i log2(e) of every query row, stored
+// [batch][head][position]: the dQ kernel reads them per row, the dK/dV
+// kernel as 64-row runs.  kLanes lanes reduce one row.
+template <int HD>
+__global__ __launch_bounds__(256) void bwd_stats_kernel(const __bf16* __restrict__ o,
+                                                        const __bf16* __restrict__ dout,
+                                                        const float* __restrict__ lse,
+                                                        float* __restrict__ nD,
+                                                        float* __restrict__ nlse2, int64_t rows,
+                                                        int64_t N, int bs, int hq) {
+  constexpr int kLanes = HD / 8;
+  constexpr int kRowsPerBlock = 256 / kLanes;
+  const int64_t r = (int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / kLanes;
+  const int sub = threadIdx.x % kLanes;
+  float acc = 0.f;
+  if (r < rows) {
+    const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(o + r * HD + sub * 8);
+    const bf16x8_t c = *reinterpret_cast<const bf16x8_t*>(dout + r * HD + sub * 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc += (float)a[e] * (float)c[e];
+  }
+#pragma unroll
+  for (int off = kLanes / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if (r < rows && sub == 0) {
+    // r enumerates (i, b, h) in memory order
+    const int h = (int)(r % hq);
+    const int64_t ib = r / hq;
+    const int b = (int)(ib % bs);
+    const int64_t i = ib / bs;
+    const int64_t idx = ((int64_t)b * hq + h) * N + i;
+    nD[idx] = -acc;
+    nlse2[idx] = -(lse[idx] * kLog2e);
+  }
+}
 
 template <int HD, int GPACK>
 hipError_t launch_dq(BwdParams p, const AttnShape& s, hipStream_t stream) {
@@ -642,9 +800,14 @@ hipError_t launch_dq(BwdParams p, const AttnShape& s, hipStream_t stream) {
 
 }  // namespace
 
-size_t attn_bwd_workspace_bytes(const AttnShape& s, bool /*bf16*/) {
-  const size_t d = (size_t)s.N * s.bs * s.hq * sizeof(float);
-  return (d + 255) / 256 * 256;
+// Workspace: one fp32 array per query row of [bs, hq, N], 256-byte aligned:
+// D for the fp32 path; -D then -LSE log2(e) for the bf16 path.
+static size_t stat_array_bytes(const AttnShape& s) {
+  return ((size_t)s.N * s.bs * s.hq * sizeof(float) + 255) / 256 * 256;
+}
+
+size_t attn_bwd_workspace_bytes(const AttnShape& s, bool bf16) {
+  return (bf16 ? 2 : 1) * stat_array_bytes(s);
 }
 
 hipError_t launch_attn_bwd_bf16(const AttnShape& s, const void* q, const void* k, const void* v,
@@ -656,8 +819,10 @@ hipError_t launch_attn_bwd_bf16(const AttnShape& s, const void* q, const void* k
   p.k = static_cast<const __bf16*>(k);
   p.v = static_cast<const __bf16*>(v);
   p.dout = static_cast<const __bf16*>(dout);
-  p.lse = lse;
-  p.D = static_cast<const float*>(workspace);
+  float* nD = static_cast<float*>(workspace);
+  float* nlse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + stat_array_bytes(s));
+  p.nD = nD;
+  p.nlse2 = nlse2;
   p.dq = static_cast<__bf16*>(dq);
   p.dk = static_cast<__bf16*>(dk);
   p.dv = static_cast<__bf16*>(dv);
@@ -673,10 +838,12 @@ hipError_t launch_attn_bwd_bf16(const AttnShape& s, const void* q, const void* k
   p.n_docs = s.n_docs;
   p.num_blocks = 0;
 
-  float* D = static_cast<float*>(workspace);
   const __bf16* ob = static_cast<const __bf16*>(o);
-  hipError_t e = s.hd == 128 ? launch_row_dot<__bf16, 128>(ob, p.dout, D, s, stream)
-                             : launch_row_dot<__bf16, 64>(ob, p.dout, D, s, stream);
+  const int64_t rows = s.N * s.bs * s.hq;
+  const int64_t stat_blocks = (rows + (s.hd == 128 ? 15 : 31)) / (s.hd == 128 ? 16 : 32);
+  hipError_t e = launch_kernel(s.hd == 128 ? bwd_stats_kernel<128> : bwd_stats_kernel<64>,
+                               dim3((uint32_t)stat_blocks), dim3(256), 0, stream, ob, p.dout, lse,
+                               nD, nlse2, rows, s.N, s.bs, s.hq);
   if (e != hipSuccess) return e;
 
   auto dq_launch = [&](auto hd_tag) -> hipError_t {
@@ -690,7 +857,7 @@ hipError_t launch_attn_bwd_bf16(const AttnShape& s, const void* q, const void* k
     constexpr int HD = decltype(hd_tag)::value;
     using C = DkvCfg<HD>;
     dim3 grid((uint32_t)((s.N + C::kBK - 1) / C::kBK), (uint32_t)(s.bs * s.hkv));
-    return launch_kernel(attn_bwd_dkv_kernel<HD, kDkvPrefetch>, grid, dim3(C::kThreads), 0, stream, p);
+    return launch_kernel(attn_bwd_dkv_kernel<HD>, grid, dim3(C::kThreads), 0, stream, p);
   };
   if (s.hd == 128) {
     if ((e = dq_launch(std::integral_constant<int, 128>{})) != hipSuccess) return e;

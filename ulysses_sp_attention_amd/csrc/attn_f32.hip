@@ -59,10 +59,6 @@ hipError_t launch_row_dot(const T* o, const T* dout, float* D, const AttnShape& 
                        D, rows, s.N, s.bs, s.hq);
 }
 
-template hipError_t launch_row_dot<__bf16, 64>(const __bf16*, const __bf16*, float*,
-                                               const AttnShape&, hipStream_t);
-template hipError_t launch_row_dot<__bf16, 128>(const __bf16*, const __bf16*, float*,
-                                                const AttnShape&, hipStream_t);
 
 namespace {
 

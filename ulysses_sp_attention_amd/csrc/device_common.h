@@ -116,6 +116,20 @@ __device__ __forceinline__ void copy_lds16_async_sbase(const void* base, uint32_
                : "memory");
 }
 
+// The 4-byte form (global_load_lds_dword): lane l's 4 bytes from base +
+// offset land at lds_dst + 4 l, so one wave moves 256 contiguous LDS bytes.
+__device__ __forceinline__ void copy_lds4_async_sbase(const void* base, uint32_t offset,
+                                                      void* lds_dst) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)((ULY_LDS char*)(lds_dst)));
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  const uint64_t sb = ((uint64_t)hi << 32) | (uint64_t)lo;
+  asm volatile("s_nop 4\n\tglobal_load_lds_dword %0, %1" ::"v"(offset), "s"(sb), "{m0}"(m0)
+               : "memory");
+}
+
 // Waits until at most N vector-memory operations of this wave are pending
 // (they complete in issue order).
 template <int N>
