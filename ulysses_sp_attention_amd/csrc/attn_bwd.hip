@@ -325,13 +325,44 @@ struct DkvCfg {
   static constexpr int kRowsPerCopy = 1024 / kRowBytes;
   static constexpr int kCopies = kTileBytes / 1024 / kPairs;
   static constexpr int kPhaseCopies = kCopies + 1;
-  static constexpr int kPrefetch = 4;   // LDS fragments read ahead of their product
   static_assert(kDOff + kDoBufs * kStatBytes <= kQOff, "statistics region");
   static_assert(kCopies >= 1 && kTileBytes % (1024 * kPairs) == 0, "tile copies");
   static_assert(kSmem <= 160 * 1024, "LDS");
 };
 
-template <int HD>
+// Product order within a matrix phase: na products of the kind whose LDS
+// operand is published before the phase (kind a: PV on the P wave, dK on the
+// dS wave) and nb of the other kind (b).  ord 0: a then b; 1: b then a;
+// 2: the first half of a, then b, then the rest of a.  Returns the product
+// at position i, numbered a first.
+__device__ constexpr int phase_order(int na, int nb, int ord, int i) {
+  if (ord == 1) return i < nb ? na + i : i - nb;
+  if (ord == 2) {
+    const int h = na / 2;
+    return i < h ? i : (i < h + nb ? na + (i - h) : i - nb);
+  }
+  return i;
+}
+// Position of the first kind-b product.
+__device__ constexpr int phase_first_b(int na, int nb, int ord) {
+  return ord == 1 ? 0 : (ord == 2 ? na / 2 : na);
+}
+
+// Matrix-phase schedule of the dK/dV kernel: fragments read ahead (PF),
+// product order of the P and dS waves (phase_order), whether a wave reads
+// the first fragments of its next matrix phase at the end of its vector
+// phase (needs the order to start with kind a), and how many positions
+// before the first kind-b product its accumulator seeds are read.
+template <int PF_, int POrd_, int DOrd_, bool PPre_, bool DPre_, int SeedLead_>
+struct DkvSched {
+  static constexpr int PF = PF_, POrd = POrd_, DOrd = DOrd_, SeedLead = SeedLead_;
+  static constexpr bool PPre = PPre_, DPre = DPre_;
+  static_assert(!PPre || POrd != 1, "early reads need kind a first");
+  static_assert(!DPre || DOrd != 1, "early reads need kind a first");
+};
+using DkvSchedDefault = DkvSched<4, 1, 0, false, false, 16>;
+
+template <int HD, class SC = DkvSchedDefault>
 __global__ __launch_bounds__(512) void attn_bwd_dkv_kernel(BwdParams p) {
   using C = DkvCfg<HD>;
   using std::false_type;
@@ -496,38 +527,55 @@ __global__ __launch_bounds__(512) void attn_bwd_dkv_kernel(BwdParams p) {
 #pragma unroll
   for (int db = 0; db < C::kDB; ++db) acc[db] = f32x16_t{};
 
+  constexpr int PF = SC::PF;
+  bf16x8_t fb[PF + 1];   // fragments in flight, slot position % (PF + 1)
+
   // ======================= P waves =======================================
   auto run_p = [&]() __attribute__((always_inline)) {
     f32x16_t s[2];        // S' of the current step, two 32-query sub-tiles
     bf16x8_t pf[2][2];    // bf16 P of the previous step, B operand of dV
-    // Matrix phase: S' of a step from Q tile lq seeded from statistic lst
-    // (QK), and dV^T += dO^T P of the previous step from dO tile ldo (PV).
-    auto matrix = [&](auto qk_tag, auto pv_tag, const char* lq, const char* lst, const char* ldo)
+    // Products of a matrix phase, kind a first: dV^T += dO^T P of the
+    // previous step (PV, dO tile ldo), then S' of the current step (QK, Q
+    // tile lq).  frag(pos) reads the fragment of the product at position pos.
+    auto frag = [&](auto qk_tag, auto pv_tag, int pos, const char* lq, const char* ldo)
         __attribute__((always_inline)) {
+      constexpr int NP = decltype(pv_tag)::value ? 4 * C::kDB : 0;
+      constexpr int NQ = decltype(qk_tag)::value ? 2 * C::kKS : 0;
+      const int idx = phase_order(NP, NQ, SC::POrd, pos);
+      return idx < NP ? tr.load(ldo, 16 * (idx / C::kDB), idx % C::kDB) : row_frag(lq, idx - NP);
+    };
+    auto prefetch = [&](auto qk_tag, auto pv_tag, const char* lq, const char* ldo)
+        __attribute__((always_inline)) {
+      constexpr int NS = (decltype(qk_tag)::value ? 2 * C::kKS : 0) + (decltype(pv_tag)::value ? 4 * C::kDB : 0);
+#pragma unroll
+      for (int i = 0; i < (PF < NS ? PF : NS); ++i) fb[i] = frag(qk_tag, pv_tag, i, lq, ldo);
+    };
+    // QK seeds its accumulators from statistic lst.  With pre_tag false the
+    // phase reads its own first fragments.
+    auto matrix = [&](auto qk_tag, auto pv_tag, auto pre_tag, const char* lq, const char* lst,
+                      const char* ldo) __attribute__((always_inline)) {
       constexpr bool kQK = decltype(qk_tag)::value;
       constexpr bool kPV = decltype(pv_tag)::value;
-      constexpr int NQ = kQK ? 2 * C::kKS : 0;   // (ks, sub), sub fastest
       constexpr int NP = kPV ? 4 * C::kDB : 0;   // (16-row step, db), db fastest
+      constexpr int NQ = kQK ? 2 * C::kKS : 0;   // (ks, sub), sub fastest
       constexpr int NS = NQ + NP;
-      constexpr int PF = C::kPrefetch < NS ? C::kPrefetch : NS;
-      auto frag = [&](int idx) __attribute__((always_inline)) {
-        return idx < NQ ? row_frag(lq, idx) : tr.load(ldo, 16 * ((idx - NQ) / C::kDB), (idx - NQ) % C::kDB);
-      };
-      bf16x8_t buf[PF + 1];
+      constexpr int fb0 = phase_first_b(NP, NQ, SC::POrd);
+      constexpr int seed_pos = fb0 > SC::SeedLead ? fb0 - SC::SeedLead : 0;
+      if constexpr (!decltype(pre_tag)::value) prefetch(qk_tag, pv_tag, lq, ldo);
 #pragma unroll
-      for (int i = 0; i < PF; ++i) buf[i] = frag(i);
-      if constexpr (kQK) {
-        s[0] = load_seed(lst, 0);
-        s[1] = load_seed(lst, 1);
-      }
-#pragma unroll
-      for (int idx = 0; idx < NS; ++idx) {
-        if (idx + PF < NS) buf[(idx + PF) % (PF + 1)] = frag(idx + PF);
-        if (idx < NQ) {
-          s[idx & 1] = mfma32(buf[idx % (PF + 1)], bfrag[idx >> 1], s[idx & 1]);
+      for (int pos = 0; pos < NS; ++pos) {
+        if (pos + PF < NS) fb[(pos + PF) % (PF + 1)] = frag(qk_tag, pv_tag, pos + PF, lq, ldo);
+        if (kQK && pos == seed_pos) {
+          s[0] = load_seed(lst, 0);
+          s[1] = load_seed(lst, 1);
+        }
+        const int idx = phase_order(NP, NQ, SC::POrd, pos);
+        if (idx < NP) {
+          const int st = idx / C::kDB;
+          acc[idx % C::kDB] = mfma32(fb[pos % (PF + 1)], pf[st >> 1][st & 1], acc[idx % C::kDB]);
         } else {
-          const int i = idx - NQ, st = i / C::kDB;
-          acc[i % C::kDB] = mfma32(buf[idx % (PF + 1)], pf[st >> 1][st & 1], acc[i % C::kDB]);
+          const int j = idx - NP;
+          s[j & 1] = mfma32(fb[pos % (PF + 1)], bfrag[j >> 1], s[j & 1]);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -575,6 +623,7 @@ __global__ __launch_bounds__(512) void attn_bwd_dkv_kernel(BwdParams p) {
       issue(4);
     };
 
+    constexpr std::integral_constant<bool, SC::PPre> p_pre{};
     Cursor cur{qt_hi - 1, 0, 0};   // step being computed
     Cursor cp = cur;               // step whose dO copies go out next
     auto issue_to = [&](int slot) __attribute__((always_inline)) {
@@ -591,10 +640,11 @@ __global__ __launch_bounds__(512) void attn_bwd_dkv_kernel(BwdParams p) {
     advance(cp);
     block_barrier();
     // Step 0: scores only.
-    matrix(true_type{}, false_type{}, q_tile(0), lse_stat(0), do_tile(0));
+    matrix(true_type{}, false_type{}, false_type{}, q_tile(0), lse_stat(0), do_tile(0));
     wait_vmem_n<C::kPhaseCopies>();
     block_barrier();
     vector((cur.t - qt_lo) * C::kBQ, issue_to(2));
+    if constexpr (SC::PPre) prefetch(true_type{}, true_type{}, q_tile(0), do_tile(0));   // dO of step 0, for A(1)
     advance(cp);
     block_barrier();
     advance(cur);
@@ -602,10 +652,11 @@ __global__ __launch_bounds__(512) void attn_bwd_dkv_kernel(BwdParams p) {
     auto step = [&](auto r_tag) __attribute__((always_inline)) {
       constexpr int r = decltype(r_tag)::value;   // n % 4
       const int prev = dslot == 0 ? 2 : dslot - 1;  // (n - 1) % 3 == (n + 2) % 3
-      matrix(true_type{}, true_type{}, q_tile(r), lse_stat(r), do_tile(prev));
+      matrix(true_type{}, true_type{}, p_pre, q_tile(r), lse_stat(r), do_tile(prev));
       wait_vmem_n<C::kPhaseCopies>();
       block_barrier();
       vector((cur.t - qt_lo) * C::kBQ, issue_to(prev));
+      if constexpr (SC::PPre) prefetch(true_type{}, true_type{}, q_tile(0), do_tile(dslot));   // dO of step n, for A(n+1)
       advance(cp);
       block_barrier();
       advance(cur);
@@ -617,8 +668,10 @@ __global__ __launch_bounds__(512) void attn_bwd_dkv_kernel(BwdParams p) {
       if (n + 2 < n_steps) step(integral_constant<int, 3>{});
       if (n + 3 < n_steps) step(integral_constant<int, 0>{});
     }
-    // Phase A after the last step: dV of the last step only.
-    matrix(false_type{}, true_type{}, q_tile(0), lse_stat(0), do_tile(dslot == 0 ? 2 : dslot - 1));
+    // Phase A after the last step: dV of the last step only (its first
+    // fragments, from the same dO tile, were read above).
+    matrix(false_type{}, true_type{}, p_pre, q_tile(0), lse_stat(0),
+           do_tile(dslot == 0 ? 2 : dslot - 1));
     block_barrier();
   };
 
@@ -626,35 +679,47 @@ __global__ __launch_bounds__(512) void attn_bwd_dkv_kernel(BwdParams p) {
   auto run_ds = [&]() __attribute__((always_inline)) {
     f32x16_t dp[2];       // dP' of the current step, two 32-query sub-tiles
     bf16x8_t dsf[2][2];   // bf16 dS of the previous step, B operand of dK
-    // Matrix phase: dK^T += Q^T dS of the previous step from Q tile lq (DK),
-    // and dP' of a step from dO tile ldo seeded from statistic lst (DP).
-    auto matrix = [&](auto dk_tag, auto dp_tag, const char* lq, const char* ldo, const char* lst)
+    // Products of a matrix phase, kind a first: dK^T += Q^T dS of the
+    // previous step (DK, Q tile lq), then dP' of the current step (DP, dO
+    // tile ldo).
+    auto frag = [&](auto dk_tag, auto dp_tag, int pos, const char* lq, const char* ldo)
         __attribute__((always_inline)) {
+      constexpr int NK = decltype(dk_tag)::value ? 4 * C::kDB : 0;
+      constexpr int ND = decltype(dp_tag)::value ? 2 * C::kKS : 0;
+      const int idx = phase_order(NK, ND, SC::DOrd, pos);
+      return idx < NK ? tr.load(lq, 16 * (idx / C::kDB), idx % C::kDB) : row_frag(ldo, idx - NK);
+    };
+    auto prefetch = [&](auto dk_tag, auto dp_tag, const char* lq, const char* ldo)
+        __attribute__((always_inline)) {
+      constexpr int NS = (decltype(dk_tag)::value ? 4 * C::kDB : 0) + (decltype(dp_tag)::value ? 2 * C::kKS : 0);
+#pragma unroll
+      for (int i = 0; i < (PF < NS ? PF : NS); ++i) fb[i] = frag(dk_tag, dp_tag, i, lq, ldo);
+    };
+    // DP seeds its accumulators from statistic lst.
+    auto matrix = [&](auto dk_tag, auto dp_tag, auto pre_tag, const char* lq, const char* ldo,
+                      const char* lst) __attribute__((always_inline)) {
       constexpr bool kDK = decltype(dk_tag)::value;
       constexpr bool kDP = decltype(dp_tag)::value;
       constexpr int NK = kDK ? 4 * C::kDB : 0;   // (16-row step, db), db fastest
       constexpr int ND = kDP ? 2 * C::kKS : 0;   // (ks, sub), sub fastest
       constexpr int NS = NK + ND;
-      constexpr int PF = C::kPrefetch < NS ? C::kPrefetch : NS;
-      auto frag = [&](int idx) __attribute__((always_inline)) {
-        return idx < NK ? tr.load(lq, 16 * (idx / C::kDB), idx % C::kDB) : row_frag(ldo, idx - NK);
-      };
-      bf16x8_t buf[PF + 1];
+      constexpr int fb0 = phase_first_b(NK, ND, SC::DOrd);
+      constexpr int seed_pos = fb0 > SC::SeedLead ? fb0 - SC::SeedLead : 0;
+      if constexpr (!decltype(pre_tag)::value) prefetch(dk_tag, dp_tag, lq, ldo);
 #pragma unroll
-      for (int i = 0; i < PF; ++i) buf[i] = frag(i);
-      if constexpr (kDP) {
-        dp[0] = load_seed(lst, 0);
-        dp[1] = load_seed(lst, 1);
-      }
-#pragma unroll
-      for (int idx = 0; idx < NS; ++idx) {
-        if (idx + PF < NS) buf[(idx + PF) % (PF + 1)] = frag(idx + PF);
+      for (int pos = 0; pos < NS; ++pos) {
+        if (pos + PF < NS) fb[(pos + PF) % (PF + 1)] = frag(dk_tag, dp_tag, pos + PF, lq, ldo);
+        if (kDP && pos == seed_pos) {
+          dp[0] = load_seed(lst, 0);
+          dp[1] = load_seed(lst, 1);
+        }
+        const int idx = phase_order(NK, ND, SC::DOrd, pos);
         if (idx < NK) {
           const int st = idx / C::kDB;
-          acc[idx % C::kDB] = mfma32(buf[idx % (PF + 1)], dsf[st >> 1][st & 1], acc[idx % C::kDB]);
+          acc[idx % C::kDB] = mfma32(fb[pos % (PF + 1)], dsf[st >> 1][st & 1], acc[idx % C::kDB]);
         } else {
           const int j = idx - NK;
-          dp[j & 1] = mfma32(buf[idx % (PF + 1)], bfrag[j >> 1], dp[j & 1]);
+          dp[j & 1] = mfma32(fb[pos % (PF + 1)], bfrag[j >> 1], dp[j & 1]);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -681,6 +746,7 @@ __global__ __launch_bounds__(512) void attn_bwd_dkv_kernel(BwdParams p) {
       issue(4);
     };
 
+    constexpr std::integral_constant<bool, SC::DPre> d_pre{};
     Cursor cq{qt_hi - 1, 0, 0};   // step whose Q copies go out next
     auto issue_to = [&](int slot) __attribute__((always_inline)) {
       return [&, slot](int k) __attribute__((always_inline)) {
@@ -705,16 +771,17 @@ __global__ __launch_bounds__(512) void attn_bwd_dkv_kernel(BwdParams p) {
     }
     advance(cq);
     block_barrier();
-    matrix(false_type{}, true_type{}, q_tile(0), do_tile(0), d_stat(0));
+    matrix(false_type{}, true_type{}, false_type{}, q_tile(0), do_tile(0), d_stat(0));
     wait_vmem_n<C::kPhaseCopies>();
     block_barrier();
     int dslot = 1;   // dO buffer of the current step: n % 3
     auto step = [&](auto r_tag) __attribute__((always_inline)) {
       constexpr int r = decltype(r_tag)::value;   // n % 4
       vector(issue_to((r + 2) & 3));
+      if constexpr (SC::DPre) prefetch(true_type{}, true_type{}, q_tile((r + 3) & 3), do_tile(0));   // Q of step n-1
       advance(cq);
       block_barrier();
-      matrix(true_type{}, true_type{}, q_tile((r + 3) & 3), do_tile(dslot), d_stat(dslot));
+      matrix(true_type{}, true_type{}, d_pre, q_tile((r + 3) & 3), do_tile(dslot), d_stat(dslot));
       wait_vmem_n<C::kPhaseCopies>();
       block_barrier();
       dslot = dslot == 2 ? 0 : dslot + 1;
@@ -727,8 +794,10 @@ __global__ __launch_bounds__(512) void attn_bwd_dkv_kernel(BwdParams p) {
     }
     // After the last step: its dS (phase A), then its dK product (phase B).
     vector(no_issue);
+    const char* q_last = q_tile((n_steps - 1) & 3);
+    if constexpr (SC::DPre) prefetch(true_type{}, false_type{}, q_last, do_tile(0));
     block_barrier();
-    matrix(true_type{}, false_type{}, q_tile((n_steps - 1) & 3), do_tile(0), d_stat(0));
+    matrix(true_type{}, false_type{}, d_pre, q_last, do_tile(0), d_stat(0));
   };
 
   if (n_steps > 0) {
