@@ -53,57 +53,65 @@ struct BwdParams {
   int64_t num_blocks;
 };
 
-// A operand (rows = head dim, k = 16 sequence positions starting at row0)
-// read transposed from a row-major swizzled LDS tile: lane l gets the
-// values of column d = 32*db + l%32 at the 8 sequence rows matching the
-// accumulator layout of the other operand.
-template <int kChunks, int kRowBytes>
-__device__ __forceinline__ bf16x8_t load_tr_operand(const char* tile, int row0, int db, int lane) {
-  const int grp = lane >> 4;
-  const int u = lane & 15;
-  bf16x4_t part[2];
-#pragma unroll
-  for (int jh = 0; jh < 2; ++jh) {
-    const int row = row0 + 8 * jh + 4 * (grp >> 1) + (u >> 2);
-    const int col = db * 32 + 16 * (grp & 1) + 4 * (u & 3);
-    const int off = swz<kChunks, kRowBytes>(row, col >> 3) + ((col >> 2) & 1) * 8;
-    part[jh] = lds_read_tr16(tile + off);
-  }
-  return __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
 // ------------------------------------------------------------------------
 // dQ
 // ------------------------------------------------------------------------
+// A workgroup of 8 waves owns a block of query positions for GPACK query
+// heads of one key/value head, as in the forward: each wave owns 32 query
+// rows of one head and keeps Q' = Q * scale * log2(e) (rounded to bf16 once)
+// and dO in registers.  For every 64-key tile t it forms, transposed so
+// that each lane holds one query row,
+//   S'^T = K Q'^T,  P = exp2(S' - LSE log2(e)),  dP^T = V dO^T,
+//   dS = P (dP - D),  dQ^T += K^T dS^T
+// (K^T by transposing LDS reads).  As in the forward, matrix and vector work
+// alternate between the two waves of a SIMD: in every phase one wave issues
+// only matrix products (dQ of tile t-1, then S'^T and dP^T of tile t: 48
+// products) while its partner forms dS of a tile; the second group of waves
+// runs one phase behind the first.  K and V tiles arrive by direct
+// global-to-LDS copies three tiles ahead.  A K tile is read for two tiles
+// (S'^T now, K^T for dQ next), so K rotates through five buffers (a
+// run-time rotation) and V through four (unrolled, compile-time).
 template <int HD, int GPACK>
 struct DqCfg {
   static constexpr int kWaves = 8;
   static constexpr int kThreads = 64 * kWaves;
-  static constexpr int kBP = 32 * kWaves / GPACK;
-  static constexpr int kBC = 64;
+  static constexpr int kBP = 32 * kWaves / GPACK;   // query positions per block
+  static constexpr int kBC = 64;                     // keys per tile
   static constexpr int kChunks = HD / 8;
   static constexpr int kRowBytes = HD * 2;
   static constexpr int kTileBytes = kBC * kRowBytes;
   static constexpr int kKS = HD / 16;
   static constexpr int kDB = HD / 32;
-  static constexpr int kLoads = kBC * kChunks / kThreads;
+  static constexpr int kKBufs = 5, kVBufs = 4;
+  static constexpr int kVOff = kKBufs * kTileBytes;
+  static constexpr int kSmem = kVOff + kVBufs * kTileBytes;
+  // One wave-wide direct copy moves 1 KiB.
+  static constexpr int kRowsPerCopy = 1024 / kRowBytes;
+  static constexpr int kCopiesPerWave = kTileBytes / 1024 / kWaves;   // per tensor and tile
+  static constexpr int kPrefetch = 4;   // LDS fragments read ahead of their product
+  static_assert(kCopiesPerWave >= 1 && kTileBytes % (1024 * kWaves) == 0, "tile copies");
+  static_assert(kSmem <= 160 * 1024, "LDS");
 };
 
 template <int HD, int GPACK>
 __global__ __launch_bounds__(512) void attn_bwd_dq_kernel(BwdParams p) {
   using C = DqCfg<HD, GPACK>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * C::kTileBytes];
-  char* lds_k = smem;
-  char* lds_v = smem + C::kTileBytes;
+  using std::false_type;
+  using std::integral_constant;
+  using std::true_type;
+  __shared__ __attribute__((aligned(1024))) char smem[C::kSmem];
+  char* const lds_k0 = smem;              // K buffers
+  char* const lds_v0 = smem + C::kVOff;   // V buffers
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5;
   const int r32 = lane & 31;
+  const int group = wave >> 2;   // waves w and w+4 share a SIMD
 
-  const int64_t N = p.N;
-  const int64_t pb = p.num_blocks - 1 - (int64_t)blockIdx.x;
+  const int64_t N = wave_uniform(p.N);
+  const int64_t pb = p.num_blocks - 1 - (int64_t)blockIdx.x;   // heaviest first
   const int ngroups = p.g / GPACK;
   int y = blockIdx.y;
   const int hg = y % ngroups;
@@ -119,139 +127,258 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_kernel(BwdParams p) {
   const int64_t q_tok = (int64_t)p.bs * p.hq * HD;
   const int64_t kv_tok = (int64_t)p.bs * p.hkv * HD;
   const int64_t qoff = ((int64_t)b * p.hq + h) * HD;
-  const __bf16* kbase = p.k + ((int64_t)b * p.hkv + kh) * HD;
-  const __bf16* vbase = p.v + ((int64_t)b * p.hkv + kh) * HD;
+  // (Kept in scalar registers: the copies take their base from there.)
+  const __bf16* kbase = reinterpret_cast<const __bf16*>(
+      wave_uniform(reinterpret_cast<int64_t>(p.k + ((int64_t)b * p.hkv + kh) * HD)));
+  const __bf16* vbase = reinterpret_cast<const __bf16*>(
+      wave_uniform(reinterpret_cast<int64_t>(p.v + ((int64_t)b * p.hkv + kh) * HD)));
 
+  // B operands of this lane's query row: Q' (scaled, rounded once) and dO.
   bf16x8_t qf[C::kKS], df[C::kKS];
 #pragma unroll
   for (int ks = 0; ks < C::kKS; ++ks) {
+    bf16x8_t rq = bf16x8_t{}, rd = bf16x8_t{};
     if (qi < N) {
-      qf[ks] = *reinterpret_cast<const bf16x8_t*>(p.q + qi * q_tok + qoff + 16 * ks + 8 * half);
-      df[ks] = *reinterpret_cast<const bf16x8_t*>(p.dout + qi * q_tok + qoff + 16 * ks + 8 * half);
-    } else {
-      qf[ks] = bf16x8_t{};
-      df[ks] = bf16x8_t{};
+      rq = *reinterpret_cast<const bf16x8_t*>(p.q + qi * q_tok + qoff + 16 * ks + 8 * half);
+      rd = *reinterpret_cast<const bf16x8_t*>(p.dout + qi * q_tok + qoff + 16 * ks + 8 * half);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      qf[ks][e] = (__bf16)((float)rq[e] * p.scale_log2);
+      df[ks][e] = (__bf16)((float)rd[e] * 1.0f);
     }
   }
   const int64_t stat = ((int64_t)b * p.hq + h) * N + qi;
-  const float lse2 = qi < N ? -p.nlse2[stat] : 0.f;
-  const float Di = qi < N ? -p.nD[stat] : 0.f;
+  const float nl = qi < N ? p.nlse2[stat] : 0.f;   // -LSE log2(e)
+  const float nd = qi < N ? p.nD[stat] : 0.f;      // -D
 
+  // Key range of the block; every wave walks all its tiles (one schedule for
+  // all waves), tiles a wave does not see being masked out entirely.
   const int64_t blk_last = (p0 + C::kBP < N ? p0 + C::kBP : N) - 1;
   const int64_t kv_lo = doc_start_of(p.cu, p.n_docs, p0);
   const int64_t kv_hi = p.causal ? blk_last + 1 : doc_end_of(p.cu, p.n_docs, blk_last, N);
   const bool wave_active = pw < N;
   const int64_t w_last = wave_active ? (pw + 31 < N ? pw + 31 : N - 1) : 0;
-  const int64_t w_lo = wave_active ? doc_start_of(p.cu, p.n_docs, pw) : 0;
-  const int64_t w_hi = wave_active ? (p.causal ? w_last + 1 : doc_end_of(p.cu, p.n_docs, w_last, N)) : 0;
-  const int64_t full_lo = wave_active ? doc_start_of(p.cu, p.n_docs, w_last) : 0;
-  const int64_t full_hi = wave_active ? (p.causal ? pw + 1 : doc_end_of(p.cu, p.n_docs, pw, N)) : 0;
-  const int64_t my_lo = qi < N ? doc_start_of(p.cu, p.n_docs, qi) : 0;
-  const int64_t my_hi = qi < N ? (p.causal ? qi + 1 : doc_end_of(p.cu, p.n_docs, qi, N)) : 0;
-  const int64_t t_begin = kv_lo / C::kBC;
-  const int64_t t_end = (kv_hi + C::kBC - 1) / C::kBC;
+  // Keys visible to every row of the wave: [full_lo, full_hi).
+  const int64_t full_lo = wave_uniform(wave_active ? doc_start_of(p.cu, p.n_docs, w_last) : 0);
+  const int64_t full_hi = wave_uniform(
+      wave_active ? (p.causal ? pw + 1 : doc_end_of(p.cu, p.n_docs, pw, N)) : 0);
+  // Visible keys of this lane's row, relative to the block's first key.
+  const int64_t key0 = wave_uniform((kv_lo / C::kBC) * C::kBC);
+  const int my_lo = qi < N ? (int)(doc_start_of(p.cu, p.n_docs, qi) - key0) : 0;
+  const int my_hi =
+      qi < N ? (int)((p.causal ? qi + 1 : doc_end_of(p.cu, p.n_docs, qi, N)) - key0) : 0;
+  const int64_t t_begin = wave_uniform(kv_lo / C::kBC);
+  const int n_tiles = (int)wave_uniform((kv_hi + C::kBC - 1) / C::kBC - t_begin);
+  const int keys_left = (int)wave_uniform(N - key0);   // keys from key0 to the end
+  const int m_tail = keys_left / C::kBC;                // first tile running past N
+  const int flo = (int)wave_uniform(full_lo - key0);
+  const int fhi = (int)wave_uniform(full_hi - key0);
 
-  f32x16_t acc[C::kDB];
+  // Direct copies: slice c of this wave lands at bytes [1024 cidx, 1024 cidx
+  // + 1024) of a tile buffer, lane l at +16 l, so lane l fetches the source
+  // chunk that the swizzle places there.  Rows past the sequence end repeat
+  // row N-1 (masked for every query).
+  const int64_t row_bytes = kv_tok * 2;
+  uint32_t slice_off[C::kCopiesPerWave];
+#pragma unroll
+  for (int c = 0; c < C::kCopiesPerWave; ++c) {
+    const int cidx = wave * C::kCopiesPerWave + c;
+    const int row0 = cidx * C::kRowsPerCopy + lane / C::kChunks;
+    const int col_bytes = ((lane % C::kChunks) ^ swz_f<C::kChunks>(row0)) * 16;
+    slice_off[c] = (uint32_t)(row0 * row_bytes) + (uint32_t)col_bytes;
+  }
+  auto copy_slice = [&](const __bf16* base, char* buf, int m, int c) __attribute__((always_inline)) {
+    const int64_t j0 = (t_begin + m) * C::kBC;
+    const char* tile =
+        reinterpret_cast<const char*>(wave_uniform((int64_t)base + j0 * row_bytes));
+    const int cidx = wave * C::kCopiesPerWave + c;
+    uint32_t off = slice_off[c];
+    if (m >= m_tail) {   // the tile runs past the sequence end
+      const int last = keys_left - 1 - m * C::kBC;
+      const int row0 = cidx * C::kRowsPerCopy + lane / C::kChunks;
+      const int col_bytes = ((lane % C::kChunks) ^ swz_f<C::kChunks>(row0)) * 16;
+      const int row = row0 < last ? row0 : last;
+      off = (uint32_t)(row * row_bytes) + (uint32_t)col_bytes;
+    }
+    copy_lds16_async_sbase(tile, off, buf + cidx * 1024);
+  };
+  auto k_buf = [&](int slot) __attribute__((always_inline)) { return lds_k0 + slot * C::kTileBytes; };
+  auto v_buf = [&](int slot) __attribute__((always_inline)) { return lds_v0 + slot * C::kTileBytes; };
+
+  f32x16_t acc[C::kDB];   // dQ^T
 #pragma unroll
   for (int db = 0; db < C::kDB; ++db) acc[db] = f32x16_t{};
+  f32x16_t s[2], dp[2];   // S'^T and dP^T of a tile (two 32-key halves)
+  bf16x8_t dsf[4];        // bf16 dS^T of a tile, B operand of dQ^T
 
-  u32x4_t kst[C::kLoads], vst[C::kLoads];
-  auto load_tile = [&](int64_t t) {
+  // --- matrix phase: dQ^T += K^T dS^T of tile m-1 (DQ, K buffer lkp), then
+  // S'^T and dP^T of tile m (SP, K buffer lk, V buffer lv) --------------------
+  int koff[C::kKS];
 #pragma unroll
-    for (int i = 0; i < C::kLoads; ++i) {
-      const int cid = tid + i * C::kThreads;
-      const int64_t j = t * C::kBC + cid / C::kChunks;
-      const int ch = cid % C::kChunks;
-      if (j < N) {
-        kst[i] = *reinterpret_cast<const u32x4_t*>(kbase + j * kv_tok + ch * 8);
-        vst[i] = *reinterpret_cast<const u32x4_t*>(vbase + j * kv_tok + ch * 8);
+  for (int ks = 0; ks < C::kKS; ++ks) koff[ks] = swz<C::kChunks, C::kRowBytes>(r32, 2 * ks + half);
+  const TrReader<C::kChunks, C::kRowBytes, C::kDB> tr(lane);
+  auto matrix_phase = [&](auto dq_tag, auto sp_tag, const char* lkp, const char* lk, const char* lv)
+      __attribute__((always_inline)) {
+    constexpr bool kDQ = decltype(dq_tag)::value;
+    constexpr bool kSP = decltype(sp_tag)::value;
+    constexpr int NQ = kDQ ? 4 * C::kDB : 0;       // (16-key step, db), db fastest
+    constexpr int NS = kSP ? 4 * C::kKS : 0;       // (ks, kb, K or V), fastest last
+    constexpr int NT = NQ + NS;
+    constexpr int PF = C::kPrefetch < NT ? C::kPrefetch : NT;
+    auto frag = [&](int idx) __attribute__((always_inline)) {
+      if (idx < NQ) return tr.load(lkp, 16 * (idx / C::kDB), idx % C::kDB);
+      const int j = idx - NQ, kb = (j >> 1) & 1, ks = j >> 2;
+      return *reinterpret_cast<const bf16x8_t*>(((j & 1) ? lv : lk) + kb * 32 * C::kRowBytes + koff[ks]);
+    };
+    bf16x8_t buf[PF + 1];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) buf[i] = frag(i);
+#pragma unroll
+    for (int idx = 0; idx < NT; ++idx) {
+      if (idx + PF < NT) buf[(idx + PF) % (PF + 1)] = frag(idx + PF);
+      if (idx < NQ) {
+        acc[idx % C::kDB] = mfma32(buf[idx % (PF + 1)], dsf[idx / C::kDB], acc[idx % C::kDB]);
       } else {
-        kst[i] = u32x4_t{};
-        vst[i] = u32x4_t{};
+        const int j = idx - NQ, kb = (j >> 1) & 1, ks = j >> 2;
+        if (j & 1)
+          dp[kb] = mfma32(buf[idx % (PF + 1)], df[ks], ks == 0 ? f32x16_t{} : dp[kb]);
+        else
+          s[kb] = mfma32(buf[idx % (PF + 1)], qf[ks], ks == 0 ? f32x16_t{} : s[kb]);
       }
-    }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int i = 0; i < C::kLoads; ++i) {
-      const int cid = tid + i * C::kThreads;
-      const int off = swz<C::kChunks, C::kRowBytes>(cid / C::kChunks, cid % C::kChunks);
-      *reinterpret_cast<u32x4_t*>(lds_k + off) = kst[i];
-      *reinterpret_cast<u32x4_t*>(lds_v + off) = vst[i];
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  if (t_begin < t_end) load_tile(t_begin);
-  for (int64_t t = t_begin; t < t_end; ++t) {
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (t + 1 < t_end) load_tile(t + 1);
-    const int64_t j0 = t * C::kBC;
-    if (!wave_active || j0 >= w_hi || j0 + C::kBC <= w_lo) continue;
-    const bool need_mask = j0 < full_lo || j0 + C::kBC > full_hi;
-
+  // --- vector phase: dS of tile m; issue(k), k = 0..3, issues a quarter of
+  // the wave's tile copies -----------------------------------------------------
+  auto vector_phase = [&](int m, auto issue) __attribute__((always_inline)) {
+    const int jr = m * C::kBC;   // first key of the tile, relative to key0
+    issue(0);
+    // Element mask without compares (as in the forward): invisible scores
+    // become exactly -2^100, whose probability is exactly 0.
+    if (jr < flo || jr + C::kBC > fhi) {
+      const float neg_lo = (float)(4 * half - min(max(my_lo - jr, -1), 65));
+      const float hi_m1 = (float)(min(max(my_hi - jr, -1), 65) - 1 - 4 * half);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      // S^T = K Q^T and dP^T = V dO^T for 32 keys; the K and V fragments of
-      // each k-step are read from LDS two steps ahead of their products.
-      f32x16_t s = f32x16_t{}, dp = f32x16_t{};
-      {
-        const int row = kb * 32 + r32;
-        auto frags = [&](int ks, bf16x8_t& kfr, bf16x8_t& vfr) {
-          const int off = swz<C::kChunks, C::kRowBytes>(row, 2 * ks + half);
-          kfr = *reinterpret_cast<const bf16x8_t*>(lds_k + off);
-          vfr = *reinterpret_cast<const bf16x8_t*>(lds_v + off);
-        };
-        bf16x8_t kb3[3], vb3[3];
-        frags(0, kb3[0], vb3[0]);
-        frags(1, kb3[1], vb3[1]);
-#pragma unroll
-        for (int ks = 0; ks < C::kKS; ++ks) {
-          if (ks + 2 < C::kKS) frags(ks + 2, kb3[(ks + 2) % 3], vb3[(ks + 2) % 3]);
-          s = mfma32(kb3[ks % 3], qf[ks], s);
-          dp = mfma32(vb3[ks % 3], df[ks], dp);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-      bf16x8_t dsf[2];
-      if (need_mask) {
-        // visible keys of this row as offsets into the 32-key block, clamped;
-        // invisible scores become -inf so their P and dS are exactly 0
-        const int64_t jb = j0 + kb * 32;
-        const int lo = (int)(my_lo - jb < -1 ? -1 : (my_lo - jb > 33 ? 33 : my_lo - jb));
-        const int hi = (int)(my_hi - jb < -1 ? -1 : (my_hi - jb > 33 ? 33 : my_hi - jb));
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int j = 8 * (i >> 2) + 4 * half + (i & 3);
-          if (j < lo || j >= hi) s[i] = -INFINITY;
+          const float j = (float)(kb * 32 + 8 * (i >> 2) + (i & 3));   // key offset minus 4*half
+          const float d = __builtin_amdgcn_fmed3f(fminf(j + neg_lo, hi_m1 - j), -1.0f, 0.0f);
+          s[kb][i] = fmaf(d, 0x1p100f, s[kb][i]);
         }
-      }
+    }
+    issue(1);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float pv = __builtin_amdgcn_exp2f(fmaf(s[i], p.scale_log2, -lse2));
-        dsf[i >> 3][i & 7] = (__bf16)(pv * (dp[i] - Di));
+        const float pv = __builtin_amdgcn_exp2f(s[kb][i] + nl);
+        dsf[2 * kb + (i >> 3)][i & 7] = (__bf16)(pv * (dp[kb][i] + nd));
       }
-      // dQ^T += K^T dS^T; K^T fragments by transposing LDS reads, two
-      // products ahead, four independent accumulator chains.
-      {
-        constexpr int kSteps = 2 * C::kDB;   // (ks2, db) pairs, db fastest
-        auto ktfrag = [&](int idx) {
-          return load_tr_operand<C::kChunks, C::kRowBytes>(lds_k, kb * 32 + 16 * (idx / C::kDB),
-                                                           idx % C::kDB, lane);
-        };
-        bf16x8_t buf[3];
-        buf[0] = ktfrag(0);
-        buf[1] = ktfrag(1);
-#pragma unroll
-        for (int idx = 0; idx < kSteps; ++idx) {
-          if (idx + 2 < kSteps) buf[(idx + 2) % 3] = ktfrag(idx + 2);
-          acc[idx % C::kDB] = mfma32(buf[idx % 3], dsf[idx / C::kDB], acc[idx % C::kDB]);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
+      issue(2 + kb);
     }
-  }
+  };
+
+  // Global phases 2m and 2m+1 form pair m (m = 0 .. n_tiles).  Group 0 runs
+  // the matrix work of pair m in phase 2m and dS of tile m in phase 2m+1;
+  // group 1 runs one phase later.  In its vector phase of pair m every wave
+  // copies its share of K and V of tile m+3 into K buffer (m+3)%5 and V
+  // buffer (m+3)%4 (K of tile m-2, last read as K^T in pair m-1, and V of
+  // tile m-1, last read in pair m-1); group 1 issues pair m+1's copies, one
+  // pair ahead, so that by global phase both groups issue pair m's copies
+  // before phase 2m+2.  At the end of phase 2m+1 every wave waits for its
+  // copies of pair m-2, so the barrier publishes the tiles of pair m+1 while
+  // two pairs of copies stay in flight.  Copies past the last tile are
+  // clamped to it (the data lands in a buffer nobody reads again).
+  constexpr int kPairCopies = 2 * C::kCopiesPerWave;
+  // Part k of the copies of pair m: k = 0, 1 for K, k = 2, 3 for V (with one
+  // slice per tensor, parts 1 and 3 are empty).  ks5 = (m+3) % 5.
+  auto copy_part = [&](int m, auto r_tag, int ks5, int k) __attribute__((always_inline)) {
+    constexpr int r = decltype(r_tag)::value;   // m % 4
+    const int last = n_tiles - 1;
+    const bool is_v = k >= 2;
+    const int c = k & 1;
+    if (c >= C::kCopiesPerWave) return;
+    const int t = m + 3 < last ? m + 3 : last;
+    char* buf = is_v ? v_buf((r + 3) & 3) : k_buf(ks5);
+    copy_slice(is_v ? vbase : kbase, buf, t, c);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto copy_pair = [&](int m, auto r_tag, int ks5) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) copy_part(m, r_tag, ks5, k);
+  };
+  auto next5 = [](int x) __attribute__((always_inline)) { return x == 4 ? 0 : x + 1; };
+
+  auto run = [&](auto g_tag) __attribute__((always_inline)) {
+    constexpr int g = decltype(g_tag)::value;
+    // K buffer of tile m (k_cur) and of its copy target, tile m+3 (k_cpy).
+    int k_cur = 0, k_cpy = 3;
+    // Pair m of the main run (1 <= m < n_tiles).
+    auto mid_pair = [&](int m, auto r_tag) __attribute__((always_inline)) {
+      constexpr int r = decltype(r_tag)::value;
+      const int k_prev = k_cur == 0 ? 4 : k_cur - 1;
+      matrix_phase(true_type{}, true_type{}, k_buf(k_prev), k_buf(k_cur), v_buf(r));
+      if constexpr (g == 1) wait_vmem_n<2 * kPairCopies>();
+      block_barrier();
+      auto issue = [&](int k) __attribute__((always_inline)) {
+        if constexpr (g == 0) copy_part(m, r_tag, k_cpy, k);
+        else copy_part(m + 1, integral_constant<int, (r + 1) & 3>{}, next5(k_cpy), k);
+      };
+      vector_phase(m, issue);
+      if constexpr (g == 0) wait_vmem_n<2 * kPairCopies>();
+      block_barrier();
+      k_cur = next5(k_cur);
+      k_cpy = next5(k_cpy);
+    };
+    // Prologue: K and V of tiles 0..2.
+    const int last = n_tiles - 1;
+#pragma unroll
+    for (int t = 0; t < 3; ++t)
+#pragma unroll
+      for (int c = 0; c < C::kCopiesPerWave; ++c) {
+        copy_slice(kbase, k_buf(t), t < last ? t : last, c);
+        copy_slice(vbase, v_buf(t), t < last ? t : last, c);
+      }
+    wait_vmem();
+    block_barrier();
+    if constexpr (g == 1) {   // phase 0: group 1 has no vector work yet, only copies
+      copy_pair(0, integral_constant<int, 0>{}, 3);
+      block_barrier();
+    }
+
+    // Pair 0: S'^T and dP^T of tile 0 only.
+    matrix_phase(false_type{}, true_type{}, k_buf(0), k_buf(0), v_buf(0));
+    block_barrier();
+    auto issue0 = [&](int k) __attribute__((always_inline)) {
+      if constexpr (g == 0) copy_part(0, integral_constant<int, 0>{}, 3, k);
+      else copy_part(1, integral_constant<int, 1>{}, 4, k);
+    };
+    vector_phase(0, issue0);
+    block_barrier();
+    k_cur = 1;
+    k_cpy = 4;
+
+    // Pairs 1 .. n_tiles-1, four per iteration so that the V rotation m % 4
+    // is a compile-time constant.
+    for (int m = 1; m < n_tiles; m += 4) {
+      mid_pair(m, integral_constant<int, 1>{});
+      if (m + 1 < n_tiles) mid_pair(m + 1, integral_constant<int, 2>{});
+      if (m + 2 < n_tiles) mid_pair(m + 2, integral_constant<int, 3>{});
+      if (m + 3 < n_tiles) mid_pair(m + 3, integral_constant<int, 0>{});
+    }
+
+    // Pair n_tiles: dQ of the last tile only.
+    matrix_phase(true_type{}, false_type{}, k_buf(k_cur == 0 ? 4 : k_cur - 1), k_buf(0), v_buf(0));
+    wait_vmem();
+    block_barrier();
+    block_barrier();
+    if constexpr (g == 0) block_barrier();   // matches group 1's leading phase
+  };
+  if (group == 0) run(integral_constant<int, 0>{});
+  else run(integral_constant<int, 1>{});
 
   if (qi >= N) return;
   __bf16* orow = p.dq + qi * q_tok + qoff;
