@@ -44,6 +44,8 @@ def _load():
     vp, i64, ci, dbl = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_double
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ci
+    lib.oracle_attn_merge.argtypes = [vp, vp, vp, vp, i64, ci, ci, ci, vp, vp]
+    lib.oracle_attn_merge.restype = ci
     lib.oracle_seq_to_head.argtypes = [vp, ci, ci, i64, ci, ci, ci, ci, vp]
     lib.oracle_seq_to_head.restype = ci
     lib.oracle_head_to_seq.argtypes = [vp, ci, ci, i64, ci, ci, ci, ci, vp]
@@ -171,3 +173,20 @@ def attn_bwd(q, k, v, dout, scale: float, causal: bool = True, cu_seqlens=None,
     if not magnitude:
         return dq, dk, dv
     return dq, dk, dv, dict(zip(("dq", "dk", "dv", "dq_from_D", "dk_from_D"), mags))
+
+
+def attn_merge(o_a, lse_a, o_b, lse_b):
+    """Merge of two partial attention results over disjoint key sets (see
+    oracle.c): returns (O, LSE) with O [N, bs, heads, hd] and LSE [bs, heads, N]."""
+    o_a, o_b, lse_a, lse_b = _f64(o_a), _f64(o_b), _f64(lse_a), _f64(lse_b)
+    N, bs, heads, hd = o_a.shape
+    if o_b.shape != o_a.shape or lse_a.shape != (bs, heads, N) or lse_b.shape != (bs, heads, N):
+        raise ValueError("attn_merge: shape mismatch")
+    o = np.empty_like(o_a)
+    lse = np.empty_like(lse_a)
+    rc = _load().oracle_attn_merge(o_a.ctypes.data, lse_a.ctypes.data, o_b.ctypes.data,
+                                   lse_b.ctypes.data, N, bs, heads, hd, o.ctypes.data,
+                                   lse.ctypes.data)
+    if rc:
+        raise ValueError("oracle_attn_merge: bad arguments")
+    return o, lse

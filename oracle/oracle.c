@@ -425,3 +425,46 @@ int oracle_attn_bwd(const double* q, const double* k, const double* v, const dou
   free(A);
   return 0;
 }
+
+/* ------------------------------------------------------------------------
+ * Merge of two partial attention results over disjoint key sets A and B:
+ * the combination step of ring (blockwise) attention, which the Hugging Face
+ * Ulysses blog compares with Ulysses in "Ulysses vs Ring Attention" (the key/
+ * value blocks travel around a ring and every block's result is folded into
+ * the running one).  Each partial O is its block's sum of exp(s_ij) v_j
+ * divided by its block's exp(LSE), so over A and B together
+ *   LSE = ln(exp(LSE_a) + exp(LSE_b)),
+ *   O   = exp(LSE_a - LSE) O_a + exp(LSE_b - LSE) O_b.
+ * A partial whose LSE is -inf saw no key: it contributes nothing, whatever
+ * its O holds; if both are -inf the row has no key at all: O = 0 and
+ * LSE = -inf.
+ * O tensors are [N, bs, heads, hd], LSE tensors [bs, heads, N].
+ * ---------------------------------------------------------------------- */
+int oracle_attn_merge(const double* o_a, const double* lse_a, const double* o_b,
+                      const double* lse_b, int64_t N, int bs, int heads, int hd, double* o,
+                      double* lse) {
+  if (N < 0 || bs < 1 || heads < 1 || hd < 1 || !o_a || !lse_a || !o_b || !lse_b || !o || !lse)
+    return 1;
+  for (int64_t i = 0; i < N; ++i)
+    for (int b = 0; b < bs; ++b)
+      for (int h = 0; h < heads; ++h) {
+        const size_t r = ((size_t)b * heads + h) * (size_t)N + (size_t)i;
+        const double la = lse_a[r], lb = lse_b[r];
+        const double m = la > lb ? la : lb;
+        double L = -INFINITY, wa = 0.0, wb = 0.0;
+        if (m != -INFINITY) {
+          L = m + log(exp(la - m) + exp(lb - m));
+          wa = exp(la - L);
+          wb = exp(lb - L);
+        }
+        lse[r] = L;
+        const size_t row = (((size_t)i * bs + b) * heads + h) * (size_t)hd;
+        for (int e = 0; e < hd; ++e) {
+          double x = 0.0;
+          if (la != -INFINITY) x += wa * o_a[row + e];
+          if (lb != -INFINITY) x += wb * o_b[row + e];
+          o[row + e] = x;
+        }
+      }
+  return 0;
+}

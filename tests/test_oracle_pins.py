@@ -461,3 +461,69 @@ def test_bwd_with_given_forward_outputs():
         P = np.where(mask, np.exp(s_ - lse[0, h][:, None]), 0.0)
         want_dk[:, 0, 0] += -scale * P.T @ (dD[:, 0, h][:, None] * q[:, 0, h])
     np.testing.assert_allclose(dk2 - base[1], want_dk, rtol=1e-9, atol=1e-12)
+
+
+# --- merge of partial results over disjoint key sets (ring / blockwise) ---
+
+@pytest.mark.parametrize("hkv", [1, 2])
+def test_merge_of_disjoint_key_blocks_equals_attention_over_their_union(hkv):
+    n, bs, hq, hd, scale = 13, 2, 2, 8, 0.4
+    q = rand(n, bs, hq, hd)
+    ka, va, kb, vb = (rand(n, bs, hkv, hd) for _ in range(4))
+    oa, la = oracle.attn_fwd(q, ka, va, scale, causal=False)
+    ob, lb = oracle.attn_fwd(q, kb, vb, scale, causal=False)
+    o, lse = oracle.attn_merge(oa, la, ob, lb)
+    # the same queries against all 2n keys: stack the queries twice and read rows [0, n)
+    full_o, full_l = oracle.attn_fwd(np.concatenate([q, q]), np.concatenate([ka, kb]),
+                                     np.concatenate([va, vb]), scale, causal=False)
+    np.testing.assert_allclose(o, full_o[:n], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(lse, full_l[:, :, :n], rtol=1e-12, atol=1e-12)
+
+
+def test_ring_steps_rebuild_causal_attention_of_the_second_block():
+    # Rows [n, 2n) of causal attention over 2n positions: the first key block
+    # is entirely visible (non-causal), the second is the causal diagonal.
+    n, bs, hq, hkv, hd, scale = 11, 1, 4, 1, 16, 0.3
+    q, k, v = rand(2 * n, bs, hq, hd), rand(2 * n, bs, hkv, hd), rand(2 * n, bs, hkv, hd)
+    o1, l1 = oracle.attn_fwd(q[n:], k[:n], v[:n], scale, causal=False)
+    o2, l2 = oracle.attn_fwd(q[n:], k[n:], v[n:], scale, causal=True)
+    o, lse = oracle.attn_merge(o1, l1, o2, l2)
+    full_o, full_l = oracle.attn_fwd(q, k, v, scale, causal=True)
+    np.testing.assert_allclose(o, full_o[n:], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(lse, full_l[:, :, n:], rtol=1e-12, atol=1e-12)
+
+
+def test_merge_lse_is_numpy_logaddexp_and_weights_sum_to_one():
+    N, bs, heads, hd = 7, 1, 3, 4
+    la, lb = rand(bs, heads, N) * 30, rand(bs, heads, N) * 30
+    oa, ob = rand(N, bs, heads, hd), rand(N, bs, heads, hd)
+    o, lse = oracle.attn_merge(oa, la, ob, lb)
+    np.testing.assert_allclose(lse, np.logaddexp(la, lb), rtol=1e-14, atol=1e-12)
+    # merging O = 1 with O = 1 must give 1 whatever the statistics
+    ones = np.ones_like(oa)
+    o1, _ = oracle.attn_merge(ones, la, ones, lb)
+    np.testing.assert_allclose(o1, 1.0, rtol=1e-14)
+    # a partial with a far smaller LSE leaves the other almost unchanged
+    o2, _ = oracle.attn_merge(oa, np.full_like(la, 10.0), ob, np.full_like(lb, -60.0))
+    np.testing.assert_allclose(o2, oa, rtol=1e-12, atol=1e-25)
+
+
+def test_merge_with_an_empty_partial_returns_the_other_and_empty_pair_is_zero():
+    N, bs, heads, hd = 5, 2, 2, 3
+    oa, la = rand(N, bs, heads, hd), rand(bs, heads, N)
+    garbage = np.full((N, bs, heads, hd), np.nan)
+    ninf = np.full((bs, heads, N), -np.inf)
+    o, lse = oracle.attn_merge(oa, la, garbage, ninf)
+    assert np.array_equal(o, oa) and np.array_equal(lse, la)
+    o, lse = oracle.attn_merge(garbage, ninf, oa, la)
+    assert np.array_equal(o, oa) and np.array_equal(lse, la)
+    o, lse = oracle.attn_merge(garbage, ninf, garbage, ninf)
+    assert np.all(o == 0.0) and np.all(lse == -np.inf)
+
+
+def test_merge_of_a_result_with_itself_keeps_o_and_adds_ln2():
+    N, bs, heads, hd = 6, 1, 2, 5
+    oa, la = rand(N, bs, heads, hd), rand(bs, heads, N)
+    o, lse = oracle.attn_merge(oa, la, oa, la)
+    np.testing.assert_allclose(o, oa, rtol=1e-15, atol=1e-15)
+    np.testing.assert_allclose(lse, la + np.log(2.0), rtol=1e-15, atol=1e-15)
