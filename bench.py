@@ -221,6 +221,7 @@ def main():
 
     rotated = measure_exchanges(w, uly, torch, stream, args.pack_sets, args.pack_reps)
     breakdown["pack_rotated"] = rotated
+    breakdown["attn_merge"] = measure_merge(w, uly, torch, stream, args.pack_sets, args.pack_reps)
 
     # Roofline of the dominant unit of the step, timed with events on the
     # stream its kernels run on.  The attention backward is one entry point
@@ -275,6 +276,59 @@ def main():
     }
     print(json.dumps(line))
     return 0
+
+
+def time_rotated(torch, stream, fns, reps):
+    """Average ms of `reps` launches cycling through `fns` (one per buffer
+    set), after one warm-up pass over every set; one pair of events on the
+    launch stream.  A launch returning a non-zero status raises."""
+    for f in fns:
+        f()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for i in range(reps):
+        status = fns[i % len(fns)]()
+        if status not in (None, 0):
+            raise RuntimeError(f"launch failed with status {status}")
+    b.record(stream)
+    b.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def measure_merge(w, uly, torch, stream, n_sets, reps):
+    """Throughput of the partial-result merge (the combination step of ring /
+    blockwise attention, outside the Ulysses step) at the share's forward
+    shape: two (O, LSE) partials merged into a third buffer, cycling through
+    `n_sets` distinct sets so that every launch reads HBM."""
+    lib = uly.load_library()
+    N, hl, hd = w.seqlen, w.hq_local, w.head_dim
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(20261202)
+    sets = []
+    for _ in range(n_sets):
+        o_a, o_b, o = (torch.randn((N, 1, hl, hd), device="cuda", generator=gen).to(torch.bfloat16)
+                       for _ in range(3))
+        l_a, l_b, l = (8.0 * torch.randn((1, hl, N), device="cuda", generator=gen) for _ in range(3))
+        sets.append((o_a, l_a, o_b, l_b, o, l))
+    st = stream.cuda_stream
+
+    def caller(t):
+        ptrs = [x.data_ptr() for x in t]
+        def f():
+            return lib.ulysses_attn_merge(ptrs[0], ptrs[1], ptrs[2], ptrs[3], N, 1, hl, hd, uly.BF16,
+                                          ptrs[4], ptrs[5], st)
+        return f
+
+    ms = time_rotated(torch, stream, [caller(t) for t in sets], reps)
+    nbytes = 3.0 * (N * hl * hd * 2 + N * hl * 4)   # two partials read, one result written
+    gb = nbytes / (ms * 1e-3) / 1e9
+    del sets
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return {"ms": ms, "GB/s": gb, "frac_of_hbm_peak": gb / HBM_PEAK_GBPS, "bytes": nbytes,
+            "method": f"{reps} back-to-back launches over {n_sets} rotating buffer sets (HBM-cold); "
+                      "not part of the step"}
 
 
 def measure_exchanges(w, uly, torch, stream, n_sets, reps):
@@ -335,18 +389,7 @@ def measure_exchanges(w, uly, torch, stream, n_sets, reps):
               "pack_do": 2.0 * N * hl * hd * e, "unpack_dqkv": 2.0 * N * (hl + 2 * kl) * hd * e}
 
     def timed(fns):
-        for f in fns:   # warm-up: one pass over every set
-            f()
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for i in range(reps):
-            status = fns[i % len(fns)]()
-            if status not in (None, 0):
-                raise RuntimeError(f"exchange launch failed with status {status}")
-        b.record(stream)
-        b.synchronize()
-        return a.elapsed_time(b) / reps
+        return time_rotated(torch, stream, fns, reps)
 
     out = {}
     tot_ms, tot_b = 0.0, 0.0

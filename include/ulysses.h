@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define ULYSSES_ABI_VERSION 2
+#define ULYSSES_ABI_VERSION 3
 
 typedef enum {
   ULYSSES_OK = 0,
@@ -207,6 +207,33 @@ ulysses_status_t ulysses_attn_bwd(const void* q, const void* k, const void* v, c
                                   float softmax_scale, int causal, const int32_t* cu_seqlens,
                                   int n_docs, void* dq, void* dk, void* dv, void* workspace,
                                   size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Merge of two partial attention results over disjoint key sets: the
+ * combination step of ring (blockwise) attention, which the Hugging Face
+ * Ulysses blog compares with Ulysses ("Ulysses vs Ring Attention").  Given
+ * (o_a, lse_a) and (o_b, lse_b) from ulysses_attn_fwd calls for the same
+ * queries against key sets A and B, writes the result over A and B:
+ *   lse = ln(e^lse_a + e^lse_b),
+ *   o   = e^(lse_a - lse) o_a + e^(lse_b - lse) o_b.
+ * A row whose statistic is -inf in one input (no key seen) takes the other
+ * input, whatever the -inf input's O holds; -inf in both gives o = 0 and
+ * lse = -inf.
+ *   o_a, o_b, o       device [seqlen, bs, heads, head_dim] in `dtype`
+ *                     (16-byte aligned)
+ *   lse_a, lse_b, lse device fp32 [bs, heads, seqlen] (4-byte aligned)
+ *   head_dim          32, 64 or 128
+ *   dtype             ULYSSES_BF16 (fp32 arithmetic, o rounded to nearest
+ *                     even) or ULYSSES_FP32
+ * o may be the same buffer as o_a or o_b, and lse the same as lse_a or lse_b
+ * (in-place merge); any other overlap is undefined.  seqlen == 0 is a no-op.
+ * ERR_UNSUPPORTED for seqlen >= 2^30, bs * heads > 65535 or more than 2^34
+ * rows.
+ */
+ulysses_status_t ulysses_attn_merge(const void* o_a, const float* lse_a, const void* o_b,
+                                    const float* lse_b, int64_t seqlen, int bs, int heads,
+                                    int head_dim, ulysses_dtype_t dtype, void* o, float* lse,
+                                    hipStream_t stream);
 
 #ifdef __cplusplus
 }

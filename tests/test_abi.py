@@ -107,9 +107,37 @@ def fwd(lib, **kw):
     (dict(q=MISALIGNED), uly.ERR_ALIGNMENT), (dict(o=MISALIGNED), uly.ERR_ALIGNMENT),
     (dict(lse=FAKE + 2), uly.ERR_ALIGNMENT),
     (dict(N=0), uly.OK),
+    # sizes the kernels count in 32 bits
+    (dict(N=1 << 30), uly.ERR_UNSUPPORTED),
+    (dict(N=1 << 29, hq=1024, hkv=1), uly.ERR_UNSUPPORTED),
+    (dict(bs=256, hq=256, hkv=256), uly.ERR_UNSUPPORTED),
 ])
 def test_attn_fwd_validation(lib, kw, want):
     assert fwd(lib, **kw) == want
+
+
+def merge(lib, **kw):
+    a = dict(oa=FAKE, la=FAKE, ob=FAKE, lb=FAKE, N=128, bs=1, heads=4, hd=128, dt=uly.BF16,
+             o=FAKE, lse=FAKE)
+    a.update(kw)
+    return lib.ulysses_attn_merge(a["oa"], a["la"], a["ob"], a["lb"], a["N"], a["bs"], a["heads"],
+                                  a["hd"], a["dt"], a["o"], a["lse"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(oa=None), uly.ERR_NULL), (dict(lb=None), uly.ERR_NULL), (dict(o=None), uly.ERR_NULL),
+    (dict(lse=None), uly.ERR_NULL),
+    (dict(dt=7), uly.ERR_DTYPE),
+    (dict(hd=96), uly.ERR_SHAPE), (dict(hd=256), uly.ERR_SHAPE), (dict(hd=16), uly.ERR_SHAPE),
+    (dict(N=-1), uly.ERR_SHAPE), (dict(bs=0), uly.ERR_SHAPE), (dict(heads=0), uly.ERR_SHAPE),
+    (dict(N=1 << 30), uly.ERR_UNSUPPORTED), (dict(bs=256, heads=256), uly.ERR_UNSUPPORTED),
+    (dict(oa=MISALIGNED), uly.ERR_ALIGNMENT), (dict(ob=MISALIGNED), uly.ERR_ALIGNMENT),
+    (dict(o=MISALIGNED), uly.ERR_ALIGNMENT), (dict(la=FAKE + 2), uly.ERR_ALIGNMENT),
+    (dict(lse=FAKE + 2), uly.ERR_ALIGNMENT),
+    (dict(N=0), uly.OK), (dict(dt=uly.FP32, hd=32, N=0), uly.OK),
+])
+def test_attn_merge_validation(lib, kw, want):
+    assert merge(lib, **kw) == want
 
 
 def test_attn_bwd_workspace_rules(lib):

@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_PKG, "libulysses.so")
 OK, ERR_NULL, ERR_SHAPE, ERR_DIVISIBILITY, ERR_DTYPE, ERR_ALIGNMENT, ERR_UNSUPPORTED, \
     ERR_WORKSPACE, ERR_HIP = range(9)
 BF16, FP32 = 0, 1
-ABI_VERSION = 2   # ULYSSES_ABI_VERSION this binding is written for
+ABI_VERSION = 3   # ULYSSES_ABI_VERSION this binding is written for
 _INVALID_DTYPE = 99
 
 # Every symbol include/ulysses.h declares.
@@ -29,6 +29,7 @@ EXPORTED_SYMBOLS = (
     "ulysses_abi_version", "ulysses_status_string", "ulysses_seq_to_head", "ulysses_head_to_seq",
     "ulysses_seq_to_head_batch", "ulysses_head_to_seq_batch",
     "ulysses_attn_fwd", "ulysses_attn_bwd_workspace_size", "ulysses_attn_bwd",
+    "ulysses_attn_merge",
 )
 MAX_BATCH = 4   # ULYSSES_MAX_BATCH
 
@@ -82,6 +83,8 @@ def load_library(path: str = LIB_PATH):
     lib.ulysses_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, ci, ci, ci, ci, ci, f32, ci, vp, ci,
                                      vp, vp, vp, vp, sz, vp]
     lib.ulysses_attn_bwd.restype = ci
+    lib.ulysses_attn_merge.argtypes = [vp, vp, vp, vp, i64, ci, ci, ci, ci, vp, vp, vp]
+    lib.ulysses_attn_merge.restype = ci
     _lib = lib
     return lib
 
@@ -218,3 +221,14 @@ def ulysses_attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, softmax_scale
         _dtype_code(q), softmax_scale, int(causal), _ptr(cu_seqlens), n_docs, _ptr(dq), _ptr(dk),
         _ptr(dv), _ptr(workspace), ws_bytes, _stream(stream))
     _check("ulysses_attn_bwd", st)
+
+
+def ulysses_attn_merge(o_a, lse_a, o_b, lse_b, o, lse, stream=None) -> None:
+    """Merge of two partial attention results over disjoint key sets.
+    o_a, o_b, o: [N, bs, heads, hd]; lse_a, lse_b, lse: fp32 [bs, heads, N].
+    o may be o_a or o_b and lse may be lse_a or lse_b (in place)."""
+    N, bs, heads, hd = o_a.shape
+    st = load_library().ulysses_attn_merge(
+        _ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b), N, bs, heads, hd, _dtype_code(o_a),
+        _ptr(o), _ptr(lse), _stream(stream))
+    _check("ulysses_attn_merge", st)

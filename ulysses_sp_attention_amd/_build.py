@@ -11,7 +11,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libulysses.so")
-SOURCES = ["api.cpp", "exchange.hip", "attn_fwd.hip", "attn_f32.hip", "attn_bwd.hip"]
+SOURCES = ["api.cpp", "exchange.hip", "attn_fwd.hip", "attn_f32.hip", "attn_bwd.hip", "attn_merge.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -232,4 +232,25 @@ ulysses_status_t ulysses_attn_bwd(const void* q, const void* k, const void* v, c
       static_cast<float*>(dk), static_cast<float*>(dv), workspace, stream));
 }
 
+ulysses_status_t ulysses_attn_merge(const void* o_a, const float* lse_a, const void* o_b,
+                                    const float* lse_b, int64_t seqlen, int bs, int heads,
+                                    int head_dim, ulysses_dtype_t dtype, void* o, float* lse,
+                                    hipStream_t stream) {
+  if (o_a == nullptr || lse_a == nullptr || o_b == nullptr || lse_b == nullptr || o == nullptr ||
+      lse == nullptr)
+    return ULYSSES_ERR_NULL;
+  if (elem_size(dtype) == 0) return ULYSSES_ERR_DTYPE;
+  if (seqlen < 0 || bs < 1 || heads < 1) return ULYSSES_ERR_SHAPE;
+  if (head_dim != 32 && head_dim != 64 && head_dim != 128) return ULYSSES_ERR_SHAPE;
+  if (seqlen >= (int64_t(1) << 30) || (int64_t)bs * heads > 65535 ||
+      seqlen * bs * heads >= (int64_t(1) << 34))
+    return ULYSSES_ERR_UNSUPPORTED;
+  if (!aligned16(o_a) || !aligned16(o_b) || !aligned16(o) || !aligned4(lse_a) ||
+      !aligned4(lse_b) || !aligned4(lse))
+    return ULYSSES_ERR_ALIGNMENT;
+  if (seqlen == 0) return ULYSSES_OK;
+  return from_hip(ulysses::launch_attn_merge(dtype == ULYSSES_BF16, o_a, lse_a, o_b, lse_b, seqlen,
+                                             bs, heads, head_dim, o, lse, stream));
+}
+
 }  // extern "C"

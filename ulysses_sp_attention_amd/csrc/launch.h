@@ -60,4 +60,10 @@ hipError_t launch_attn_bwd_f32(const AttnShape& s, const float* q, const float* 
                                const float* o, const float* lse, const float* dout, float* dq,
                                float* dk, float* dv, void* workspace, hipStream_t stream);
 
+// Merge of two partial attention results (O, LSE) over disjoint key sets;
+// O is [N, bs, heads, hd] in bf16 or fp32, LSE [bs, heads, N] fp32.
+hipError_t launch_attn_merge(bool bf16, const void* o_a, const float* lse_a, const void* o_b,
+                             const float* lse_b, int64_t N, int bs, int heads, int hd, void* o,
+                             float* lse, hipStream_t stream);
+
 }  // namespace ulysses
