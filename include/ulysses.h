@@ -184,6 +184,35 @@ ulysses_status_t ulysses_attn_fwd(const void* q, const void* k, const void* v, i
                                   float softmax_scale, int causal, const int32_t* cu_seqlens,
                                   int n_docs, void* o, float* lse, hipStream_t stream);
 
+/*
+ * ulysses_attn_fwd with the layout exchange fused into the attention: Q, K
+ * and V are read straight from their sequence chunks and O is written into
+ * this rank's head slots of the O chunks, so neither the head-sharded
+ * tensors nor the exchange launches exist (the first extension the pages'
+ * path allows: the exchange is the step on either side of attention).
+ *   q_chunks, k_chunks, v_chunks, o_chunks
+ *            host arrays of P device pointers; chunk c is [n_local, bs, H,
+ *            head_dim] and holds tokens [c*n_local, (c+1)*n_local) with all H
+ *            heads (H = hq for q and o, hkv for k and v), as for
+ *            ulysses_seq_to_head.  The arrays are read during the call only.
+ *   hq, hkv  global head counts.  This rank attends with q heads
+ *            [rank*hq/P, (rank+1)*hq/P) and the matching key/value heads
+ *            (replicated as in ulysses_seq_to_head when hkv < P); only
+ *            those head slots of the o chunks are written.
+ *   lse      device fp32 [bs, hq/P, P*n_local] (the rank's heads).
+ * The result equals ulysses_seq_to_head of Q, K, V, then ulysses_attn_fwd,
+ * then ulysses_head_to_seq of O, bit for bit.  Other arguments as in
+ * ulysses_attn_fwd.  ERR_UNSUPPORTED unless dtype is ULYSSES_BF16, P <= 16,
+ * n_local is a multiple of 64 and 128 * bs * max(hq, hkv) * head_dim < 2^31;
+ * ERR_DIVISIBILITY for head counts the exchange rejects.
+ */
+ulysses_status_t ulysses_attn_fwd_fused(const void* const* q_chunks, const void* const* k_chunks,
+                                        const void* const* v_chunks, int P, int rank,
+                                        int64_t n_local, int bs, int hq, int hkv, int head_dim,
+                                        ulysses_dtype_t dtype, float softmax_scale, int causal,
+                                        const int32_t* cu_seqlens, int n_docs,
+                                        void* const* o_chunks, float* lse, hipStream_t stream);
+
 /* Bytes of device workspace ulysses_attn_bwd needs for these sizes. */
 size_t ulysses_attn_bwd_workspace_size(int64_t seqlen, int bs, int hq, int hkv, int head_dim,
                                        ulysses_dtype_t dtype);

@@ -201,3 +201,40 @@ def test_batch_exchange_null_table_and_head_to_seq_divisibility(lib):
     descs, keep = batch_descs([("ok8", FAKE, 8), ("ok8", FAKE + 65536, 2)])
     assert lib.ulysses_head_to_seq_batch(descs, 2, 8, 0, 4, 1, 128, uly.BF16, None) == \
         uly.ERR_DIVISIBILITY
+
+
+def fused_fwd(lib, P=4, table=None, o_table=None, **kw):
+    a = dict(rank=1, n=128, bs=1, hq=8, hkv=4, hd=128, dt=uly.BF16, scale=0.1, causal=1, cu=None,
+             n_docs=0, lse=FAKE)
+    a.update(kw)
+    t = chunk_array(table if table is not None else [FAKE + 4096 * i for i in range(P)])
+    ot = chunk_array(o_table if o_table is not None else [FAKE + 4096 * i for i in range(P)])
+    return lib.ulysses_attn_fwd_fused(t, t, t, P, a["rank"], a["n"], a["bs"], a["hq"], a["hkv"],
+                                      a["hd"], a["dt"], a["scale"], a["causal"], a["cu"],
+                                      a["n_docs"], ot, a["lse"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(lse=None), uly.ERR_NULL),
+    (dict(table=[FAKE, None, FAKE, FAKE]), uly.ERR_NULL),
+    (dict(o_table=[FAKE, FAKE, FAKE, None]), uly.ERR_NULL),
+    (dict(table=[FAKE, MISALIGNED, FAKE, FAKE]), uly.ERR_ALIGNMENT),
+    (dict(lse=FAKE + 2), uly.ERR_ALIGNMENT),
+    (dict(rank=4), uly.ERR_SHAPE), (dict(rank=-1), uly.ERR_SHAPE), (dict(n=-64), uly.ERR_SHAPE),
+    (dict(hq=6), uly.ERR_DIVISIBILITY),              # q heads not divisible by P
+    (dict(hkv=3), uly.ERR_DIVISIBILITY),             # kv heads neither multiple nor divisor of P
+    (dict(hd=96), uly.ERR_SHAPE), (dict(dt=9), uly.ERR_DTYPE),
+    (dict(dt=uly.FP32), uly.ERR_UNSUPPORTED),       # bf16 kernels only
+    (dict(n=100), uly.ERR_UNSUPPORTED),             # 64-row tiles must not straddle chunks
+    (dict(bs=128, hq=1024, hkv=4), uly.ERR_UNSUPPORTED),   # 64 rows of all heads beyond 2^31 bytes
+    (dict(n=0), uly.OK),
+    (dict(n=0, hkv=2), uly.OK),                     # replicated kv heads accepted
+])
+def test_attn_fwd_fused_validation(lib, kw, want):
+    assert fused_fwd(lib, **kw) == want
+
+
+def test_attn_fwd_fused_rejects_more_than_16_chunks(lib):
+    table = [FAKE + 4096 * i for i in range(17)]
+    assert fused_fwd(lib, P=17, table=table, o_table=table, hq=34, hkv=17, rank=0) == \
+        uly.ERR_UNSUPPORTED

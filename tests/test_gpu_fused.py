@@ -1,0 +1,105 @@
+"""The exchange fused into attention: the fused forward must equal
+seq_to_head -> attention -> head_to_seq bit for bit (same arithmetic on the
+same values; only where rows are read and written differs), and must leave
+the other ranks' head slots of the output chunks untouched."""
+import numpy as np
+import pytest
+
+import synth
+from helpers import ensure_library, storage_bytes, to_device
+
+pytestmark = pytest.mark.gpu
+
+CANARY = 7.0
+
+
+@pytest.fixture(scope="module", autouse=True)
+def lib():
+    return ensure_library()
+
+
+def split(t, P):
+    n = t.shape[0] // P
+    return [t[c * n:(c + 1) * n] for c in range(P)]
+
+
+def local_heads(heads, P):
+    return heads // P if heads >= P else 1
+
+
+def unfused_fwd(qc, kc, vc, rank, scale, causal, cu_t, o_full):
+    """Reference: the three separate calls."""
+    import torch
+    import ulysses_sp_attention_amd as uly
+    P = len(qc)
+    n, bs, hq, hd = qc[0].shape
+    hkv = kc[0].shape[2]
+    N = P * n
+    qh = torch.empty((N, bs, hq // P, hd), dtype=qc[0].dtype, device="cuda")
+    kh = torch.empty((N, bs, local_heads(hkv, P), hd), dtype=qc[0].dtype, device="cuda")
+    vh = torch.empty_like(kh)
+    uly.ulysses_seq_to_head(qc, rank, qh)
+    uly.ulysses_seq_to_head(kc, rank, kh)
+    uly.ulysses_seq_to_head(vc, rank, vh)
+    o = torch.empty_like(qh)
+    lse = torch.empty((bs, hq // P, N), dtype=torch.float32, device="cuda")
+    uly.ulysses_attn_fwd(qh, kh, vh, o, lse, scale, causal, cu_t)
+    uly.ulysses_head_to_seq(o, rank, split(o_full, P))
+    return lse
+
+
+FWD_CASES = [
+    # P, rank, n_local, bs, hq, hkv, hd, causal, cu
+    (2, 1, 64, 1, 4, 4, 64, True, None),
+    (4, 2, 128, 2, 8, 2, 128, True, None),      # fewer kv heads than ranks: replicated
+    (4, 3, 64, 1, 8, 4, 128, False, None),
+    (8, 3, 128, 1, 32, 8, 128, True, None),     # the Llama-8B head counts
+    (4, 0, 192, 1, 8, 8, 64, True, [0, 100, 101, 400, 768]),
+    (16, 15, 64, 1, 16, 16, 128, True, None),   # the largest P of the fused calls
+    (3, 1, 64, 1, 6, 3, 128, True, [0, 64, 130, 192]),
+]
+
+
+@pytest.mark.parametrize("P,rank,n,bs,hq,hkv,hd,causal,cu", FWD_CASES)
+def test_fused_fwd_equals_exchange_attention_exchange(P, rank, n, bs, hq, hkv, hd, causal, cu):
+    import torch
+    import ulysses_sp_attention_amd as uly
+    N, seed, scale = P * n, 4200 + P * 7 + rank, 1.0 / np.sqrt(hd)
+    q = to_device(synth.normal(seed, synth.STREAM_Q, (N, bs, hq, hd), "bf16"), "bf16")
+    k = to_device(synth.normal(seed, synth.STREAM_K, (N, bs, hkv, hd), "bf16"), "bf16")
+    v = to_device(synth.normal(seed, synth.STREAM_V, (N, bs, hkv, hd), "bf16"), "bf16")
+    cu_t = None if cu is None else torch.tensor(cu, dtype=torch.int32, device="cuda")
+    qc, kc, vc = split(q, P), split(k, P), split(v, P)
+    o_ref = torch.full_like(q, CANARY)
+    lse_ref = unfused_fwd(qc, kc, vc, rank, scale, causal, cu_t, o_ref)
+    o = torch.full_like(q, CANARY)
+    lse = torch.full_like(lse_ref, float("nan"))
+    uly.ulysses_attn_fwd_fused(qc, kc, vc, split(o, P), lse, rank, scale, causal, cu_t)
+    torch.cuda.synchronize()
+    assert storage_bytes(o) == storage_bytes(o_ref)      # other ranks' slots keep the canary
+    assert storage_bytes(lse) == storage_bytes(lse_ref)
+    hl = hq // P
+    untouched = torch.cat([o[:, :, :rank * hl], o[:, :, (rank + 1) * hl:]], dim=2)
+    assert bool(torch.all(untouched == CANARY))
+
+
+def test_fused_fwd_full_size_llama8b_128k():
+    """The benchmark's shape: P = 8 chunks of 16384 tokens, 32 q / 8 kv heads, rank 3."""
+    import torch
+    import ulysses_sp_attention_amd as uly
+    P, rank, n, hq, hkv, hd = 8, 3, 16384, 32, 8, 128
+    N = P * n
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4242)
+    q = (torch.randn((N, 1, hq, hd), device="cuda", generator=gen) / np.sqrt(hd)).to(torch.bfloat16)
+    k = torch.randn((N, 1, hkv, hd), device="cuda", generator=gen).to(torch.bfloat16)
+    v = torch.randn((N, 1, hkv, hd), device="cuda", generator=gen).to(torch.bfloat16)
+    qc, kc, vc = split(q, P), split(k, P), split(v, P)
+    o_ref = torch.full_like(q, CANARY)
+    lse_ref = unfused_fwd(qc, kc, vc, rank, 1.0, True, None, o_ref)
+    o = torch.full_like(q, CANARY)
+    lse = torch.full_like(lse_ref, float("nan"))
+    uly.ulysses_attn_fwd_fused(qc, kc, vc, split(o, P), lse, rank, 1.0, True, None)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16))
+    assert torch.equal(lse.view(torch.int32), lse_ref.view(torch.int32))

@@ -29,7 +29,7 @@ EXPORTED_SYMBOLS = (
     "ulysses_abi_version", "ulysses_status_string", "ulysses_seq_to_head", "ulysses_head_to_seq",
     "ulysses_seq_to_head_batch", "ulysses_head_to_seq_batch",
     "ulysses_attn_fwd", "ulysses_attn_bwd_workspace_size", "ulysses_attn_bwd",
-    "ulysses_attn_merge",
+    "ulysses_attn_merge", "ulysses_attn_fwd_fused",
 )
 MAX_BATCH = 4   # ULYSSES_MAX_BATCH
 
@@ -85,6 +85,9 @@ def load_library(path: str = LIB_PATH):
     lib.ulysses_attn_bwd.restype = ci
     lib.ulysses_attn_merge.argtypes = [vp, vp, vp, vp, i64, ci, ci, ci, ci, vp, vp, vp]
     lib.ulysses_attn_merge.restype = ci
+    lib.ulysses_attn_fwd_fused.argtypes = [vp, vp, vp, ci, ci, i64, ci, ci, ci, ci, ci, f32, ci, vp,
+                                           ci, vp, vp, vp]
+    lib.ulysses_attn_fwd_fused.restype = ci
     _lib = lib
     return lib
 
@@ -232,3 +235,20 @@ def ulysses_attn_merge(o_a, lse_a, o_b, lse_b, o, lse, stream=None) -> None:
         _ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b), N, bs, heads, hd, _dtype_code(o_a),
         _ptr(o), _ptr(lse), _stream(stream))
     _check("ulysses_attn_merge", st)
+
+
+def ulysses_attn_fwd_fused(q_chunks, k_chunks, v_chunks, o_chunks, lse, rank: int,
+                           softmax_scale: float, causal: bool = True, cu_seqlens=None,
+                           stream=None) -> None:
+    """Forward with the exchange fused in: q_chunks, o_chunks are P tensors
+    [n_local, bs, hq, hd] (all heads), k_chunks, v_chunks P tensors
+    [n_local, bs, hkv, hd]; lse: fp32 [bs, hq/P, P*n_local].  Writes only this
+    rank's head slots of o_chunks."""
+    n, bs, hq, hd = q_chunks[0].shape
+    hkv = k_chunks[0].shape[2]
+    n_docs = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
+    st = load_library().ulysses_attn_fwd_fused(
+        _ptr_array(q_chunks), _ptr_array(k_chunks), _ptr_array(v_chunks), len(q_chunks), rank, n,
+        bs, hq, hkv, hd, _dtype_code(q_chunks[0]), softmax_scale, int(causal), _ptr(cu_seqlens),
+        n_docs, _ptr_array(o_chunks), _ptr(lse), _stream(stream))
+    _check("ulysses_attn_fwd_fused", st)

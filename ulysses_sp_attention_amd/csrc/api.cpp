@@ -90,6 +90,55 @@ ulysses_status_t check_attn(int64_t seqlen, int bs, int hq, int hkv, int head_di
   return ULYSSES_OK;
 }
 
+// Checks of the fused (exchange-in-attention) calls shared by forward and
+// backward: the chunk tables, the rank's head slices and the rank's
+// attention shape.  Fills one SeqChunks per global head count.
+ulysses_status_t check_fused(int P, int rank, int64_t n_local, int bs, int hq, int hkv,
+                             int head_dim, ulysses_dtype_t dtype, float scale, int causal,
+                             const int32_t* cu, int n_docs, AttnShape* s, int* q_head0,
+                             int* kv_head0) {
+  if (elem_size(dtype) == 0) return ULYSSES_ERR_DTYPE;
+  if (P < 1 || rank < 0 || rank >= P || n_local < 0 || bs < 1 || hq < 1 || hkv < 1)
+    return ULYSSES_ERR_SHAPE;
+  if (hq % P != 0) return ULYSSES_ERR_DIVISIBILITY;
+  if (hkv >= P ? hkv % P != 0 : P % hkv != 0) return ULYSSES_ERR_DIVISIBILITY;
+  const int hq_l = hq / P;
+  const int hkv_l = hkv >= P ? hkv / P : 1;
+  ulysses_status_t st = check_attn(n_local * P, bs, hq_l, hkv_l, head_dim, dtype, scale, causal,
+                                   cu, n_docs, s);
+  if (st != ULYSSES_OK) return st;
+  // bf16 tensor-core kernels only; 64-row tiles never straddle two chunks;
+  // a tile's row offsets (64 rows of all heads) fit the copies' 32 bits.
+  if (dtype != ULYSSES_BF16 || P > ulysses::kMaxFusedChunks || n_local % 64 != 0 ||
+      64 * (int64_t)bs * (hq > hkv ? hq : hkv) * head_dim * 2 >= (int64_t(1) << 31))
+    return ULYSSES_ERR_UNSUPPORTED;
+  *q_head0 = rank * hq_l;
+  *kv_head0 = hkv >= P ? rank * hkv_l : (int)((int64_t)rank * hkv / P);
+  return ULYSSES_OK;
+}
+
+// Chunk table of one operand for the fused calls (pointers already checked).
+ulysses::SeqChunks seq_chunks(const void* const* chunks, int P, int64_t n_local, int row_heads,
+                              int head0) {
+  ulysses::SeqChunks c{};
+  for (int i = 0; i < P; ++i) c.chunk[i] = reinterpret_cast<uintptr_t>(chunks[i]);
+  c.n = n_local;
+  c.row_heads = row_heads;
+  c.head0 = head0;
+  c.tiles_per_chunk = ulysses::make_fastdiv((uint32_t)(n_local / 64 > 0 ? n_local / 64 : 1));
+  return c;
+}
+
+// NULL or misaligned (16 bytes) entry in a host table of P chunk pointers.
+ulysses_status_t check_table(const void* const* chunks, int P) {
+  if (chunks == nullptr) return ULYSSES_ERR_NULL;
+  for (int i = 0; i < P; ++i)
+    if (chunks[i] == nullptr) return ULYSSES_ERR_NULL;
+  for (int i = 0; i < P; ++i)
+    if (!aligned16(chunks[i])) return ULYSSES_ERR_ALIGNMENT;
+  return ULYSSES_OK;
+}
+
 ulysses_status_t exchange_batch(bool to_head, const ulysses_exchange_tensor_t* tensors, int n,
                                 int P, int rank, int64_t n_local, int bs, int head_dim,
                                 ulysses_dtype_t dtype, hipStream_t stream) {
@@ -251,6 +300,33 @@ ulysses_status_t ulysses_attn_merge(const void* o_a, const float* lse_a, const v
   if (seqlen == 0) return ULYSSES_OK;
   return from_hip(ulysses::launch_attn_merge(dtype == ULYSSES_BF16, o_a, lse_a, o_b, lse_b, seqlen,
                                              bs, heads, head_dim, o, lse, stream));
+}
+
+ulysses_status_t ulysses_attn_fwd_fused(const void* const* q_chunks, const void* const* k_chunks,
+                                        const void* const* v_chunks, int P, int rank,
+                                        int64_t n_local, int bs, int hq, int hkv, int head_dim,
+                                        ulysses_dtype_t dtype, float softmax_scale, int causal,
+                                        const int32_t* cu_seqlens, int n_docs,
+                                        void* const* o_chunks, float* lse, hipStream_t stream) {
+  if (q_chunks == nullptr || k_chunks == nullptr || v_chunks == nullptr || o_chunks == nullptr ||
+      lse == nullptr)
+    return ULYSSES_ERR_NULL;
+  AttnShape s;
+  int q0 = 0, kv0 = 0;
+  ulysses_status_t st = check_fused(P, rank, n_local, bs, hq, hkv, head_dim, dtype, softmax_scale,
+                                    causal, cu_seqlens, n_docs, &s, &q0, &kv0);
+  if (st != ULYSSES_OK) return st;
+  for (const void* const* t : {q_chunks, k_chunks, v_chunks})
+    if ((st = check_table(t, P)) != ULYSSES_OK) return st;
+  if ((st = check_table(const_cast<const void* const*>(o_chunks), P)) != ULYSSES_OK) return st;
+  if (!aligned4(lse)) return ULYSSES_ERR_ALIGNMENT;
+  if (n_local == 0) return ULYSSES_OK;
+  const ulysses::SeqChunks cq = seq_chunks(q_chunks, P, n_local, hq, q0);
+  const ulysses::SeqChunks ck = seq_chunks(k_chunks, P, n_local, hkv, kv0);
+  const ulysses::SeqChunks cv = seq_chunks(v_chunks, P, n_local, hkv, kv0);
+  const ulysses::SeqChunks co =
+      seq_chunks(const_cast<const void* const*>(o_chunks), P, n_local, hq, q0);
+  return from_hip(ulysses::launch_attn_fwd_bf16_fused(s, cq, ck, cv, co, lse, stream));
 }
 
 }  // extern "C"

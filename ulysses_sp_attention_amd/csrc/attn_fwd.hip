@@ -71,7 +71,19 @@ struct FwdParams {
   const int32_t* cu;
   int n_docs;
   int64_t num_pos_blocks;
+  // Fused form only: the operands in their sequence chunks (q, k, v, o
+  // above are unused).
+  SeqChunks cq, ck, cv, co;
 };
+
+// Element offset of row i (batch b, rank head h) from the start of its
+// sequence chunk, and that chunk: see SeqChunks.
+__device__ __forceinline__ int64_t chunk_row_offset(const SeqChunks& c, uint32_t i, int bs, int b,
+                                                    int h, int hd, uint32_t* chunk) {
+  const uint32_t ci = i / (uint32_t)c.n;
+  *chunk = ci;
+  return (((int64_t)(i - ci * (uint32_t)c.n) * bs + b) * c.row_heads + c.head0 + h) * hd;
+}
 
 template <int HD, int GPACK>
 struct FwdCfg {
@@ -92,7 +104,7 @@ struct FwdCfg {
   static_assert(kCopiesPerWave >= 1 && kTileBytes % (1024 * kWaves) == 0, "tile copies");
 };
 
-template <int HD, int GPACK>
+template <int HD, int GPACK, bool kFused>
 __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdParams p) {
   using C = FwdCfg<HD, GPACK>;
   __shared__ __attribute__((aligned(1024))) char smem[2 * C::kBufs * C::kTileBytes];
@@ -123,11 +135,18 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdParams p) {
   const int64_t q_tok = (int64_t)p.bs * p.hq * HD;
   const int64_t kv_tok = (int64_t)p.bs * p.hkv * HD;
   const __bf16* qbase = p.q + ((int64_t)b * p.hq + h) * HD;
-  // (Kept in scalar registers: the copies take their base from there.)
-  const __bf16* kbase = reinterpret_cast<const __bf16*>(
-      wave_uniform(reinterpret_cast<int64_t>(p.k + ((int64_t)b * p.hkv + kh) * HD)));
-  const __bf16* vbase = reinterpret_cast<const __bf16*>(
-      wave_uniform(reinterpret_cast<int64_t>(p.v + ((int64_t)b * p.hkv + kh) * HD)));
+  // (Kept in scalar registers: the copies take their base from there.)  In
+  // the fused form they are the chunk tables' first chunk, replaced per tile.
+  const __bf16* kbase = reinterpret_cast<const __bf16*>(wave_uniform(
+      kFused ? (int64_t)p.ck.chunk[0] : reinterpret_cast<int64_t>(p.k + ((int64_t)b * p.hkv + kh) * HD)));
+  const __bf16* vbase = reinterpret_cast<const __bf16*>(wave_uniform(
+      kFused ? (int64_t)p.cv.chunk[0] : reinterpret_cast<int64_t>(p.v + ((int64_t)b * p.hkv + kh) * HD)));
+  // Address of row i of Q (or O) for this lane's head.
+  auto q_row = [&](const SeqChunks& c, int64_t i) __attribute__((always_inline)) {
+    uint32_t ci;
+    const int64_t off = chunk_row_offset(c, (uint32_t)i, p.bs, b, h, HD, &ci);
+    return reinterpret_cast<__bf16*>(c.chunk[ci]) + off;
+  };
 
   // Q fragments (B operand of S^T): lane holds Q[qi][16 ks + 8 half + 0..7],
   // multiplied by scale*log2(e) and rounded to bf16 once, so that the
@@ -136,7 +155,10 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
   for (int ks = 0; ks < C::kKS; ++ks) {
     bf16x8_t raw = bf16x8_t{};
-    if (qi < N) raw = *reinterpret_cast<const bf16x8_t*>(qbase + qi * q_tok + 16 * ks + 8 * half);
+    if (qi < N) {
+      const __bf16* row = kFused ? q_row(p.cq, qi) : qbase + qi * q_tok;
+      raw = *reinterpret_cast<const bf16x8_t*>(row + 16 * ks + 8 * half);
+    }
 #pragma unroll
     for (int e = 0; e < 8; ++e) qf[ks][e] = (__bf16)((float)raw[e] * p.scale_log2);
   }
@@ -169,7 +191,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdParams p) {
   // buffer, lane l at +16 l, so lane l fetches the source chunk that the
   // swizzle places there.  Rows past the sequence end re-read row N-1: those
   // keys are masked for every query, so only their finiteness matters.
-  const int64_t row_bytes = kv_tok * 2;
+  const int64_t row_bytes = kFused ? (int64_t)p.bs * p.ck.row_heads * HD * 2 : kv_tok * 2;
   // Lane byte offsets of this wave's slices within a tile that lies wholly
   // inside the sequence (the usual case; the last tile of a sequence whose
   // length is not a multiple of kBC clamps its rows instead).
@@ -187,10 +209,19 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdParams p) {
     const int col_bytes = ((lane % C::kChunks) ^ swz_f<C::kChunks>(row0)) * 16;
     slice_off[c] = (uint32_t)(row0 * row_bytes) + (uint32_t)col_bytes;
   }
-  auto copy_slice = [&](const __bf16* base, char* buf, int m, int c) __attribute__((always_inline)) {
+  auto copy_slice = [&](const __bf16* base, const SeqChunks& ch, char* buf, int m, int c)
+      __attribute__((always_inline)) {
     const int64_t j0 = (t_begin + m) * C::kBC;
-    const char* tile =
-        reinterpret_cast<const char*>(wave_uniform((int64_t)base + j0 * row_bytes));
+    const char* tile;
+    if constexpr (kFused) {   // the tile's chunk and its first row within it
+      const uint32_t tt = (uint32_t)(t_begin + m);
+      const uint32_t ci = fast_div(tt, ch.tiles_per_chunk);
+      const int64_t s0 = (int64_t)(tt - ci * ch.tiles_per_chunk.d) * C::kBC;
+      tile = reinterpret_cast<const char*>(wave_uniform(
+          (int64_t)ch.chunk[ci] + ((s0 * p.bs + b) * ch.row_heads + ch.head0 + kh) * HD * 2));
+    } else {
+      tile = reinterpret_cast<const char*>(wave_uniform((int64_t)base + j0 * row_bytes));
+    }
     const int cidx = wave * C::kCopiesPerWave + c;
     uint32_t off = slice_off[c];
     if (m >= m_tail) {   // the tile runs past the sequence end
@@ -202,9 +233,10 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdParams p) {
     }
     copy_lds16_async_sbase(tile, off, buf + cidx * 1024);
   };
-  auto copy_tile = [&](const __bf16* base, char* buf, int m) __attribute__((always_inline)) {
+  auto copy_tile = [&](const __bf16* base, const SeqChunks& ch, char* buf, int m)
+      __attribute__((always_inline)) {
 #pragma unroll
-    for (int c = 0; c < C::kCopiesPerWave; ++c) copy_slice(base, buf, m, c);
+    for (int c = 0; c < C::kCopiesPerWave; ++c) copy_slice(base, ch, buf, m, c);
   };
 
   f32x16_t acc_o[C::kDB];
@@ -382,7 +414,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdParams p) {
     if (c >= C::kCopiesPerWave) return;
     const int t = is_v ? (m + 2 < last ? m + 2 : last) : (m + 3 < last ? m + 3 : last);
     char* buf = is_v ? lds_v0 + ((r + 2) & 3) * C::kTileBytes : lds_k0 + ((r + 3) & 3) * C::kTileBytes;
-    copy_slice(is_v ? vbase : kbase, buf, t, c);
+    copy_slice(is_v ? vbase : kbase, is_v ? p.cv : p.ck, buf, t, c);
     __builtin_amdgcn_sched_barrier(0);
   };
   auto copy_pair = [&](int m, auto r_tag) __attribute__((always_inline)) {
@@ -412,11 +444,11 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdParams p) {
     constexpr int g = decltype(g_tag)::value;
     // Prologue: K of tiles 0..2 and V of tiles 0..1.
     const int last = n_tiles - 1;
-    copy_tile(kbase, lds_k0, 0);
-    copy_tile(kbase, lds_k0 + C::kTileBytes, 1 < last ? 1 : last);
-    copy_tile(kbase, lds_k0 + 2 * C::kTileBytes, 2 < last ? 2 : last);
-    copy_tile(vbase, lds_v0, 0);
-    copy_tile(vbase, lds_v0 + C::kTileBytes, 1 < last ? 1 : last);
+    copy_tile(kbase, p.ck, lds_k0, 0);
+    copy_tile(kbase, p.ck, lds_k0 + C::kTileBytes, 1 < last ? 1 : last);
+    copy_tile(kbase, p.ck, lds_k0 + 2 * C::kTileBytes, 2 < last ? 2 : last);
+    copy_tile(vbase, p.cv, lds_v0, 0);
+    copy_tile(vbase, p.cv, lds_v0 + C::kTileBytes, 1 < last ? 1 : last);
     wait_vmem();
     block_barrier();
     if constexpr (g == 1) {   // phase 0: group 1 has no softmax yet, only copies
@@ -457,7 +489,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdParams p) {
   if (qi >= N) return;
   const float l = l_run + wave_xor32_f(l_run);
   const float inv = 1.0f / l;
-  __bf16* orow = p.o + (qi * p.bs + b) * (int64_t)p.hq * HD + (int64_t)h * HD;
+  __bf16* orow = kFused ? q_row(p.co, qi) : p.o + (qi * p.bs + b) * (int64_t)p.hq * HD + (int64_t)h * HD;
 #pragma unroll
   for (int db = 0; db < C::kDB; ++db)
 #pragma unroll
@@ -470,33 +502,26 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdParams p) {
   if (half == 0) p.lse[((int64_t)b * p.hq + h) * N + qi] = (m_run + __log2f(l)) * kLn2;
 }
 
-template <int HD, int GPACK>
+template <int HD, int GPACK, bool kFused>
 hipError_t launch_fwd(const FwdParams& prm, const AttnShape& s, hipStream_t stream) {
   using C = FwdCfg<HD, GPACK>;
   FwdParams p = prm;
   p.num_pos_blocks = (s.N + C::kBP - 1) / C::kBP;
   dim3 grid((uint32_t)p.num_pos_blocks, (uint32_t)(s.bs * s.hkv * (p.g / GPACK)));
-  return launch_kernel(attn_fwd_bf16_kernel<HD, GPACK>, grid, dim3(C::kThreads), 0, stream, p);
+  return launch_kernel(attn_fwd_bf16_kernel<HD, GPACK, kFused>, grid, dim3(C::kThreads), 0, stream,
+                       p);
 }
 
-template <int HD>
+template <int HD, bool kFused>
 hipError_t launch_fwd_hd(const FwdParams& p, const AttnShape& s, hipStream_t stream) {
-  if (p.g % 8 == 0) return launch_fwd<HD, 8>(p, s, stream);
-  if (p.g % 4 == 0) return launch_fwd<HD, 4>(p, s, stream);
-  if (p.g % 2 == 0) return launch_fwd<HD, 2>(p, s, stream);
-  return launch_fwd<HD, 1>(p, s, stream);
+  if (p.g % 8 == 0) return launch_fwd<HD, 8, kFused>(p, s, stream);
+  if (p.g % 4 == 0) return launch_fwd<HD, 4, kFused>(p, s, stream);
+  if (p.g % 2 == 0) return launch_fwd<HD, 2, kFused>(p, s, stream);
+  return launch_fwd<HD, 1, kFused>(p, s, stream);
 }
 
-}  // namespace
-
-hipError_t launch_attn_fwd_bf16(const AttnShape& s, const void* q, const void* k, const void* v,
-                                void* o, float* lse, hipStream_t stream) {
-  if (s.N == 0) return hipSuccess;
-  FwdParams p;
-  p.q = static_cast<const __bf16*>(q);
-  p.k = static_cast<const __bf16*>(k);
-  p.v = static_cast<const __bf16*>(v);
-  p.o = static_cast<__bf16*>(o);
+FwdParams common_params(const AttnShape& s, float* lse) {
+  FwdParams p{};
   p.lse = lse;
   p.N = s.N;
   p.bs = s.bs;
@@ -508,8 +533,34 @@ hipError_t launch_attn_fwd_bf16(const AttnShape& s, const void* q, const void* k
   p.cu = s.cu;
   p.n_docs = s.n_docs;
   p.num_pos_blocks = 0;
-  if (s.hd == 128) return launch_fwd_hd<128>(p, s, stream);
-  return launch_fwd_hd<64>(p, s, stream);
+  return p;
+}
+
+}  // namespace
+
+hipError_t launch_attn_fwd_bf16_fused(const AttnShape& s, const SeqChunks& q, const SeqChunks& k,
+                                      const SeqChunks& v, const SeqChunks& o, float* lse,
+                                      hipStream_t stream) {
+  if (s.N == 0) return hipSuccess;
+  FwdParams p = common_params(s, lse);
+  p.cq = q;
+  p.ck = k;
+  p.cv = v;
+  p.co = o;
+  if (s.hd == 128) return launch_fwd_hd<128, true>(p, s, stream);
+  return launch_fwd_hd<64, true>(p, s, stream);
+}
+
+hipError_t launch_attn_fwd_bf16(const AttnShape& s, const void* q, const void* k, const void* v,
+                                void* o, float* lse, hipStream_t stream) {
+  if (s.N == 0) return hipSuccess;
+  FwdParams p = common_params(s, lse);
+  p.q = static_cast<const __bf16*>(q);
+  p.k = static_cast<const __bf16*>(k);
+  p.v = static_cast<const __bf16*>(v);
+  p.o = static_cast<__bf16*>(o);
+  if (s.hd == 128) return launch_fwd_hd<128, false>(p, s, stream);
+  return launch_fwd_hd<64, false>(p, s, stream);
 }
 
 }  // namespace ulysses

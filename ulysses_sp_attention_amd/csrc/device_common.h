@@ -174,6 +174,14 @@ struct TrReader {
   }
 };
 
+// n / f.d for the divisor of make_fastdiv (launch.h), exact for every
+// 32-bit n.
+template <typename FD>
+__device__ __forceinline__ uint32_t fast_div(uint32_t n, FD f) {
+  const uint32_t t = __umulhi(n, f.m);
+  return (uint32_t)(((uint64_t)t + n) >> f.l);
+}
+
 // A value the whole wave agrees on, moved to scalar registers so that
 // branches on it stay scalar branches.
 __device__ __forceinline__ int64_t wave_uniform(int64_t x) {

@@ -20,26 +20,6 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kUnroll = 1;
 
-// Unsigned 32-bit division by a run-time invariant divisor with one
-// multiply-high and a shift (Granlund and Montgomery, "Division by invariant
-// integers using multiplication", PLDI 1994; the round-up multiplier
-// m = floor(2^32 (2^l - d) / d) + 1 with l = ceil(log2 d)).
-struct FastDiv {
-  uint32_t d, m, l;
-};
-
-FastDiv make_fastdiv(uint32_t d) {
-  uint32_t l = 0;
-  while ((1ull << l) < d) ++l;
-  const uint64_t m = ((1ull << 32) * ((1ull << l) - d)) / d + 1;
-  return FastDiv{d, (uint32_t)m, l};
-}
-
-__device__ __forceinline__ uint32_t fast_div(uint32_t n, FastDiv f) {
-  const uint32_t t = __umulhi(n, f.m);
-  return (uint32_t)(((uint64_t)t + n) >> f.l);
-}
-
 // Per-tensor launch data: its chunk table is in ExchangeArgs::chunks.
 struct SliceArgs {
   char* head_buf;

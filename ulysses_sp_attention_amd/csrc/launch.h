@@ -38,6 +38,37 @@ hipError_t launch_exchange(bool to_head, const ChunkTable& chunks, int P, char* 
                            int64_t rows_per_chunk, int64_t chunk_row_bytes, int64_t slot_bytes,
                            int64_t head_row_bytes, hipStream_t stream);
 
+// Unsigned 32-bit division by a run-time invariant divisor with one
+// multiply-high and a shift (Granlund and Montgomery, "Division by invariant
+// integers using multiplication", PLDI 1994; the round-up multiplier
+// m = floor(2^32 (2^l - d) / d) + 1 with l = ceil(log2 d)); fast_div in
+// device_common.h applies it.
+struct FastDiv {
+  uint32_t d, m, l;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+  uint32_t l = 0;
+  while ((1ull << l) < d) ++l;
+  const uint64_t m = ((1ull << 32) * ((1ull << l) - d)) / d + 1;
+  return FastDiv{d, (uint32_t)m, l};
+}
+
+// An attention operand still in its P sequence chunks (the layout on either
+// side of the exchange; each chunk [n, bs, row_heads, hd] holds every head):
+// row i, batch b, head h of this rank's slice is at
+//   chunk[i / n] + ((i % n) * bs + b) * row_heads * hd + (head0 + h) * hd
+// elements.  n is a multiple of 64, so a 64-row tile never straddles chunks;
+// tiles_per_chunk divides a tile index by n / 64.
+constexpr int kMaxFusedChunks = 16;
+struct SeqChunks {
+  uintptr_t chunk[kMaxFusedChunks];
+  int64_t n;
+  int row_heads;
+  int head0;
+  FastDiv tiles_per_chunk;
+};
+
 struct AttnShape {
   int64_t N;
   int bs, hq, hkv, hd;
@@ -49,6 +80,11 @@ struct AttnShape {
 
 hipError_t launch_attn_fwd_bf16(const AttnShape& s, const void* q, const void* k, const void* v,
                                 void* o, float* lse, hipStream_t stream);
+// The forward reading Q, K, V from their sequence chunks and writing O into
+// the rank's head slots of the O chunks (s.hq / s.hkv are the rank's heads).
+hipError_t launch_attn_fwd_bf16_fused(const AttnShape& s, const SeqChunks& q, const SeqChunks& k,
+                                      const SeqChunks& v, const SeqChunks& o, float* lse,
+                                      hipStream_t stream);
 hipError_t launch_attn_fwd_f32(const AttnShape& s, const float* q, const float* k, const float* v,
                                float* o, float* lse, hipStream_t stream);
 
