@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define ULYSSES_ABI_VERSION 3
+#define ULYSSES_ABI_VERSION 4
 
 typedef enum {
   ULYSSES_OK = 0,
@@ -236,6 +236,36 @@ ulysses_status_t ulysses_attn_bwd(const void* q, const void* k, const void* v, c
                                   float softmax_scale, int causal, const int32_t* cu_seqlens,
                                   int n_docs, void* dq, void* dk, void* dv, void* workspace,
                                   size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * ulysses_attn_bwd with the layout exchange fused in, the backward of
+ * ulysses_attn_fwd_fused: Q, K, V, O and dO are read straight from their
+ * sequence chunks and dQ, dK, dV are written into this rank's head slots of
+ * their sequence chunks.  The gradients cross the exchange the other way
+ * round from the activations (dO seq -> head, dQ/dK/dV head -> seq; the
+ * exchange itself is the DeepSpeed blog's design section), and here that
+ * crossing is the kernels' addressing.
+ *   q/k/v/o/do/dq/dk/dv_chunks
+ *            host arrays of P device pointers laid out as in
+ *            ulysses_attn_fwd_fused (H = hq for q, o, do, dq; hkv for k, v,
+ *            dk, dv); read during the call only.  Only this rank's head
+ *            slots of dq, dk and dv are written.
+ *   lse      device fp32 [bs, hq/P, P*n_local] from ulysses_attn_fwd_fused.
+ *   workspace  at least ulysses_attn_bwd_workspace_size(P*n_local, bs, hq/P,
+ *            max(hkv/P, 1), head_dim, dtype) bytes, 256-byte aligned.
+ * The result equals ulysses_seq_to_head of Q, K, V, O and dO, then
+ * ulysses_attn_bwd, then ulysses_head_to_seq of dQ, dK and dV, bit for bit.
+ * ERR_DIVISIBILITY also when hkv < P: a key/value head shared by several
+ * ranks would need their partial dK, dV summed, which a write cannot do.
+ * ERR_UNSUPPORTED and the other arguments as in ulysses_attn_fwd_fused.
+ */
+ulysses_status_t ulysses_attn_bwd_fused(
+    const void* const* q_chunks, const void* const* k_chunks, const void* const* v_chunks,
+    const void* const* o_chunks, const float* lse, const void* const* do_chunks, int P, int rank,
+    int64_t n_local, int bs, int hq, int hkv, int head_dim, ulysses_dtype_t dtype,
+    float softmax_scale, int causal, const int32_t* cu_seqlens, int n_docs,
+    void* const* dq_chunks, void* const* dk_chunks, void* const* dv_chunks, void* workspace,
+    size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Merge of two partial attention results over disjoint key sets: the

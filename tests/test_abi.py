@@ -238,3 +238,41 @@ def test_attn_fwd_fused_rejects_more_than_16_chunks(lib):
     table = [FAKE + 4096 * i for i in range(17)]
     assert fused_fwd(lib, P=17, table=table, o_table=table, hq=34, hkv=17, rank=0) == \
         uly.ERR_UNSUPPORTED
+
+
+def fused_bwd(lib, P=4, table=None, out_table=None, ws_bytes=None, **kw):
+    a = dict(rank=1, n=128, bs=1, hq=8, hkv=4, hd=128, dt=uly.BF16, scale=0.1, causal=1, cu=None,
+             n_docs=0, lse=FAKE, ws=FAKE)
+    a.update(kw)
+    t = chunk_array(table if table is not None else [FAKE + 4096 * i for i in range(P)])
+    ot = chunk_array(out_table if out_table is not None else [FAKE + 4096 * i for i in range(P)])
+    if ws_bytes is None:
+        hkv_l = a["hkv"] // P if a["hkv"] >= P else 1
+        ws_bytes = max(lib.ulysses_attn_bwd_workspace_size(P * a["n"], a["bs"], a["hq"] // P,
+                                                           hkv_l, a["hd"], uly.BF16), 1)
+    return lib.ulysses_attn_bwd_fused(t, t, t, t, a["lse"], t, P, a["rank"], a["n"], a["bs"],
+                                      a["hq"], a["hkv"], a["hd"], a["dt"], a["scale"], a["causal"],
+                                      a["cu"], a["n_docs"], ot, ot, ot, a["ws"], ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(lse=None), uly.ERR_NULL),
+    (dict(table=[FAKE, None, FAKE, FAKE]), uly.ERR_NULL),
+    (dict(out_table=[FAKE, FAKE, None, FAKE]), uly.ERR_NULL),
+    (dict(table=[FAKE, FAKE, MISALIGNED, FAKE]), uly.ERR_ALIGNMENT),
+    (dict(out_table=[MISALIGNED, FAKE, FAKE, FAKE]), uly.ERR_ALIGNMENT),
+    (dict(lse=FAKE + 2), uly.ERR_ALIGNMENT),
+    (dict(ws=None), uly.ERR_WORKSPACE),
+    (dict(ws_bytes=8191), uly.ERR_WORKSPACE),         # needs 2 * 512 rows * 2 heads * 4 bytes
+    (dict(ws=FAKE + 8), uly.ERR_ALIGNMENT),
+    (dict(rank=4), uly.ERR_SHAPE), (dict(n=-64), uly.ERR_SHAPE),
+    (dict(hq=6), uly.ERR_DIVISIBILITY),
+    (dict(hkv=2), uly.ERR_DIVISIBILITY),               # replicated kv heads: dK/dV need a sum
+    (dict(hkv=2, n=0), uly.ERR_DIVISIBILITY),
+    (dict(hd=96), uly.ERR_SHAPE), (dict(dt=9), uly.ERR_DTYPE),
+    (dict(dt=uly.FP32), uly.ERR_UNSUPPORTED),
+    (dict(n=100), uly.ERR_UNSUPPORTED),
+    (dict(n=0, ws=None), uly.OK),                      # empty: no workspace needed
+])
+def test_attn_bwd_fused_validation(lib, kw, want):
+    assert fused_bwd(lib, **kw) == want

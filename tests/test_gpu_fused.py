@@ -103,3 +103,95 @@ def test_fused_fwd_full_size_llama8b_128k():
     torch.cuda.synchronize()
     assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16))
     assert torch.equal(lse.view(torch.int32), lse_ref.view(torch.int32))
+
+
+def unfused_bwd(qc, kc, vc, oc, lse, doc, rank, scale, causal, cu_t, dq_full, dk_full, dv_full):
+    """Reference: dO to the head layout, the backward, dQ/dK/dV back."""
+    import torch
+    import ulysses_sp_attention_amd as uly
+    P = len(qc)
+    n, bs, hq, hd = qc[0].shape
+    hkv = kc[0].shape[2]
+    N = P * n
+    heads = lambda h: torch.empty((N, bs, h, hd), dtype=qc[0].dtype, device="cuda")
+    qh, oh, doh = heads(hq // P), heads(hq // P), heads(hq // P)
+    kh, vh = heads(hkv // P), heads(hkv // P)
+    for chunks, h in ((qc, qh), (kc, kh), (vc, vh), (oc, oh), (doc, doh)):
+        uly.ulysses_seq_to_head(chunks, rank, h)
+    dqh, dkh, dvh = torch.empty_like(qh), torch.empty_like(kh), torch.empty_like(vh)
+    ws = workspace(N, bs, hq // P, hkv // P, hd)
+    uly.ulysses_attn_bwd(qh, kh, vh, oh, lse, doh, dqh, dkh, dvh, ws, scale, causal, cu_t)
+    for h, full in ((dqh, dq_full), (dkh, dk_full), (dvh, dv_full)):
+        uly.ulysses_head_to_seq(h, rank, split(full, P))
+
+
+def workspace(N, bs, hq_l, hkv_l, hd):
+    import torch
+    import ulysses_sp_attention_amd as uly
+    nbytes = uly.ulysses_attn_bwd_workspace_size(N, bs, hq_l, hkv_l, hd, uly.BF16)
+    # contents on entry must not matter: start from garbage
+    return torch.full((nbytes // 4,), float("nan"), dtype=torch.float32, device="cuda")
+
+
+def check_bwd(q, k, v, do, P, rank, scale, causal, cu_t):
+    """Forward (fused), then the fused backward against the unfused chain."""
+    import torch
+    import ulysses_sp_attention_amd as uly
+    N, bs, hq, hd = q.shape
+    hkv = k.shape[2]
+    qc, kc, vc, doc = split(q, P), split(k, P), split(v, P), split(do, P)
+    o = torch.full_like(q, CANARY)
+    lse = torch.empty((bs, hq // P, N), dtype=torch.float32, device="cuda")
+    uly.ulysses_attn_fwd_fused(qc, kc, vc, split(o, P), lse, rank, scale, causal, cu_t)
+    oc = split(o, P)
+    ref = [torch.full_like(t, CANARY) for t in (q, k, v)]
+    unfused_bwd(qc, kc, vc, oc, lse, doc, rank, scale, causal, cu_t, *ref)
+    got = [torch.full_like(t, CANARY) for t in (q, k, v)]
+    ws = workspace(N, bs, hq // P, hkv // P, hd)
+    uly.ulysses_attn_bwd_fused(qc, kc, vc, oc, lse, doc, *[split(t, P) for t in got], ws, rank,
+                               scale, causal, cu_t)
+    torch.cuda.synchronize()
+    for name, g, r, heads in zip(("dq", "dk", "dv"), got, ref, (hq, hkv, hkv)):
+        assert torch.equal(g.view(torch.int16), r.view(torch.int16)), name
+        hl = heads // P
+        untouched = torch.cat([g[:, :, :rank * hl], g[:, :, (rank + 1) * hl:]], dim=2)
+        assert bool(torch.all(untouched == CANARY)), name
+
+
+BWD_CASES = [
+    # P, rank, n_local, bs, hq, hkv, hd, causal, cu
+    (2, 1, 64, 1, 4, 4, 64, True, None),
+    (4, 2, 128, 2, 8, 4, 128, True, None),
+    (4, 3, 64, 1, 8, 4, 128, False, None),
+    (8, 3, 128, 1, 32, 8, 128, True, None),     # the Llama-8B head counts
+    (4, 0, 192, 1, 8, 8, 64, True, [0, 100, 101, 400, 768]),
+    (16, 15, 64, 1, 16, 16, 128, True, None),   # the largest P of the fused calls
+    (3, 1, 64, 1, 6, 3, 128, True, [0, 64, 130, 192]),
+    (2, 0, 320, 1, 16, 2, 128, True, [0, 1, 2, 333, 640]),   # group of 8 q heads per kv head
+]
+
+
+@pytest.mark.parametrize("P,rank,n,bs,hq,hkv,hd,causal,cu", BWD_CASES)
+def test_fused_bwd_equals_exchange_backward_exchange(P, rank, n, bs, hq, hkv, hd, causal, cu):
+    import torch
+    N, seed, scale = P * n, 5200 + P * 7 + rank, 1.0 / np.sqrt(hd)
+    q = to_device(synth.normal(seed, synth.STREAM_Q, (N, bs, hq, hd), "bf16"), "bf16")
+    k = to_device(synth.normal(seed, synth.STREAM_K, (N, bs, hkv, hd), "bf16"), "bf16")
+    v = to_device(synth.normal(seed, synth.STREAM_V, (N, bs, hkv, hd), "bf16"), "bf16")
+    do = to_device(synth.normal(seed, synth.STREAM_DO, (N, bs, hq, hd), "bf16"), "bf16")
+    cu_t = None if cu is None else torch.tensor(cu, dtype=torch.int32, device="cuda")
+    check_bwd(q, k, v, do, P, rank, scale, causal, cu_t)
+
+
+def test_fused_bwd_full_size_llama8b_128k():
+    """The benchmark's shape: P = 8 chunks of 16384 tokens, 32 q / 8 kv heads, rank 3."""
+    import torch
+    P, rank, n, hq, hkv, hd = 8, 3, 16384, 32, 8, 128
+    N = P * n
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(5252)
+    q = (torch.randn((N, 1, hq, hd), device="cuda", generator=gen) / np.sqrt(hd)).to(torch.bfloat16)
+    k = torch.randn((N, 1, hkv, hd), device="cuda", generator=gen).to(torch.bfloat16)
+    v = torch.randn((N, 1, hkv, hd), device="cuda", generator=gen).to(torch.bfloat16)
+    do = torch.randn((N, 1, hq, hd), device="cuda", generator=gen).to(torch.bfloat16)
+    check_bwd(q, k, v, do, P, rank, 1.0, True, None)

@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_PKG, "libulysses.so")
 OK, ERR_NULL, ERR_SHAPE, ERR_DIVISIBILITY, ERR_DTYPE, ERR_ALIGNMENT, ERR_UNSUPPORTED, \
     ERR_WORKSPACE, ERR_HIP = range(9)
 BF16, FP32 = 0, 1
-ABI_VERSION = 3   # ULYSSES_ABI_VERSION this binding is written for
+ABI_VERSION = 4   # ULYSSES_ABI_VERSION this binding is written for
 _INVALID_DTYPE = 99
 
 # Every symbol include/ulysses.h declares.
@@ -29,7 +29,7 @@ EXPORTED_SYMBOLS = (
     "ulysses_abi_version", "ulysses_status_string", "ulysses_seq_to_head", "ulysses_head_to_seq",
     "ulysses_seq_to_head_batch", "ulysses_head_to_seq_batch",
     "ulysses_attn_fwd", "ulysses_attn_bwd_workspace_size", "ulysses_attn_bwd",
-    "ulysses_attn_merge", "ulysses_attn_fwd_fused",
+    "ulysses_attn_merge", "ulysses_attn_fwd_fused", "ulysses_attn_bwd_fused",
 )
 MAX_BATCH = 4   # ULYSSES_MAX_BATCH
 
@@ -88,6 +88,9 @@ def load_library(path: str = LIB_PATH):
     lib.ulysses_attn_fwd_fused.argtypes = [vp, vp, vp, ci, ci, i64, ci, ci, ci, ci, ci, f32, ci, vp,
                                            ci, vp, vp, vp]
     lib.ulysses_attn_fwd_fused.restype = ci
+    lib.ulysses_attn_bwd_fused.argtypes = [vp, vp, vp, vp, vp, vp, ci, ci, i64, ci, ci, ci, ci, ci,
+                                           f32, ci, vp, ci, vp, vp, vp, vp, sz, vp]
+    lib.ulysses_attn_bwd_fused.restype = ci
     _lib = lib
     return lib
 
@@ -252,3 +255,24 @@ def ulysses_attn_fwd_fused(q_chunks, k_chunks, v_chunks, o_chunks, lse, rank: in
         bs, hq, hkv, hd, _dtype_code(q_chunks[0]), softmax_scale, int(causal), _ptr(cu_seqlens),
         n_docs, _ptr_array(o_chunks), _ptr(lse), _stream(stream))
     _check("ulysses_attn_fwd_fused", st)
+
+
+def ulysses_attn_bwd_fused(q_chunks, k_chunks, v_chunks, o_chunks, lse, do_chunks, dq_chunks,
+                           dk_chunks, dv_chunks, workspace, rank: int, softmax_scale: float,
+                           causal: bool = True, cu_seqlens=None, stream=None) -> None:
+    """Backward with the exchange fused in: every *_chunks argument is P
+    tensors [n_local, bs, H, hd] (H = hq for q, o, do, dq; hkv for k, v, dk,
+    dv); lse: fp32 [bs, hq/P, P*n_local] from ulysses_attn_fwd_fused;
+    workspace as for ulysses_attn_bwd at the rank's head counts.  Writes only
+    this rank's head slots of dq_chunks, dk_chunks and dv_chunks."""
+    n, bs, hq, hd = q_chunks[0].shape
+    hkv = k_chunks[0].shape[2]
+    n_docs = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load_library().ulysses_attn_bwd_fused(
+        _ptr_array(q_chunks), _ptr_array(k_chunks), _ptr_array(v_chunks), _ptr_array(o_chunks),
+        _ptr(lse), _ptr_array(do_chunks), len(q_chunks), rank, n, bs, hq, hkv, hd,
+        _dtype_code(q_chunks[0]), softmax_scale, int(causal), _ptr(cu_seqlens), n_docs,
+        _ptr_array(dq_chunks), _ptr_array(dk_chunks), _ptr_array(dv_chunks), _ptr(workspace),
+        ws_bytes, _stream(stream))
+    _check("ulysses_attn_bwd_fused", st)

@@ -329,4 +329,44 @@ ulysses_status_t ulysses_attn_fwd_fused(const void* const* q_chunks, const void*
   return from_hip(ulysses::launch_attn_fwd_bf16_fused(s, cq, ck, cv, co, lse, stream));
 }
 
+ulysses_status_t ulysses_attn_bwd_fused(
+    const void* const* q_chunks, const void* const* k_chunks, const void* const* v_chunks,
+    const void* const* o_chunks, const float* lse, const void* const* do_chunks, int P, int rank,
+    int64_t n_local, int bs, int hq, int hkv, int head_dim, ulysses_dtype_t dtype,
+    float softmax_scale, int causal, const int32_t* cu_seqlens, int n_docs,
+    void* const* dq_chunks, void* const* dk_chunks, void* const* dv_chunks, void* workspace,
+    size_t workspace_bytes, hipStream_t stream) {
+  if (q_chunks == nullptr || k_chunks == nullptr || v_chunks == nullptr || o_chunks == nullptr ||
+      lse == nullptr || do_chunks == nullptr || dq_chunks == nullptr || dk_chunks == nullptr ||
+      dv_chunks == nullptr)
+    return ULYSSES_ERR_NULL;
+  AttnShape s;
+  int q0 = 0, kv0 = 0;
+  ulysses_status_t st = check_fused(P, rank, n_local, bs, hq, hkv, head_dim, dtype, softmax_scale,
+                                    causal, cu_seqlens, n_docs, &s, &q0, &kv0);
+  if (st != ULYSSES_OK) return st;
+  // A replicated KV head (hkv < P) would need its ranks' partial dK/dV summed
+  // before it lands in the sequence chunks: not a plain write.
+  if (hkv < P) return ULYSSES_ERR_DIVISIBILITY;
+  for (const void* const* t : {q_chunks, k_chunks, v_chunks, o_chunks, do_chunks})
+    if ((st = check_table(t, P)) != ULYSSES_OK) return st;
+  for (void* const* t : {dq_chunks, dk_chunks, dv_chunks})
+    if ((st = check_table(const_cast<const void* const*>(t), P)) != ULYSSES_OK) return st;
+  if (!aligned4(lse)) return ULYSSES_ERR_ALIGNMENT;
+  const size_t need = ulysses::attn_bwd_workspace_bytes(s, true);
+  if (n_local > 0 && (workspace == nullptr || workspace_bytes < need)) return ULYSSES_ERR_WORKSPACE;
+  if (n_local > 0 && !aligned16(workspace)) return ULYSSES_ERR_ALIGNMENT;
+  if (n_local == 0) return ULYSSES_OK;
+  auto table = [&](const void* const* t, int heads, int head0) {
+    return seq_chunks(t, P, n_local, heads, head0);
+  };
+  auto out_table = [&](void* const* t, int heads, int head0) {
+    return seq_chunks(const_cast<const void* const*>(t), P, n_local, heads, head0);
+  };
+  return from_hip(ulysses::launch_attn_bwd_bf16_fused(
+      s, table(q_chunks, hq, q0), table(k_chunks, hkv, kv0), table(v_chunks, hkv, kv0),
+      table(o_chunks, hq, q0), lse, table(do_chunks, hq, q0), out_table(dq_chunks, hq, q0),
+      out_table(dk_chunks, hkv, kv0), out_table(dv_chunks, hkv, kv0), workspace, stream));
+}
+
 }  // extern "C"

@@ -33,6 +33,12 @@ namespace ulysses {
 
 namespace {
 
+// Workspace: one fp32 array per query row of [bs, hq, N], 256-byte aligned:
+// D for the fp32 path; -D then -LSE log2(e) for the bf16 path.
+size_t stat_array_bytes(const AttnShape& s) {
+  return ((size_t)s.N * s.bs * s.hq * sizeof(float) + 255) / 256 * 256;
+}
+
 struct BwdParams {
   const __bf16* q;
   const __bf16* k;
@@ -51,6 +57,9 @@ struct BwdParams {
   const int32_t* cu;
   int n_docs;
   int64_t num_blocks;
+  // Fused form only: the operands in their sequence chunks (the pointers
+  // above, except the statistics, are unused).
+  SeqChunks cq, ck, cv, cdo, cdq, cdk, cdv;
 };
 
 // ------------------------------------------------------------------------
@@ -93,7 +102,7 @@ struct DqCfg {
   static_assert(kSmem <= 160 * 1024, "LDS");
 };
 
-template <int HD, int GPACK>
+template <int HD, int GPACK, bool kFused>
 __global__ __launch_bounds__(512) void attn_bwd_dq_kernel(BwdParams p) {
   using C = DqCfg<HD, GPACK>;
   using std::false_type;
@@ -128,10 +137,10 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_kernel(BwdParams p) {
   const int64_t kv_tok = (int64_t)p.bs * p.hkv * HD;
   const int64_t qoff = ((int64_t)b * p.hq + h) * HD;
   // (Kept in scalar registers: the copies take their base from there.)
-  const __bf16* kbase = reinterpret_cast<const __bf16*>(
-      wave_uniform(reinterpret_cast<int64_t>(p.k + ((int64_t)b * p.hkv + kh) * HD)));
-  const __bf16* vbase = reinterpret_cast<const __bf16*>(
-      wave_uniform(reinterpret_cast<int64_t>(p.v + ((int64_t)b * p.hkv + kh) * HD)));
+  const __bf16* kbase = reinterpret_cast<const __bf16*>(wave_uniform(
+      kFused ? (int64_t)p.ck.chunk[0] : reinterpret_cast<int64_t>(p.k + ((int64_t)b * p.hkv + kh) * HD)));
+  const __bf16* vbase = reinterpret_cast<const __bf16*>(wave_uniform(
+      kFused ? (int64_t)p.cv.chunk[0] : reinterpret_cast<int64_t>(p.v + ((int64_t)b * p.hkv + kh) * HD)));
 
   // B operands of this lane's query row: Q' (scaled, rounded once) and dO.
   bf16x8_t qf[C::kKS], df[C::kKS];
@@ -139,8 +148,10 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_kernel(BwdParams p) {
   for (int ks = 0; ks < C::kKS; ++ks) {
     bf16x8_t rq = bf16x8_t{}, rd = bf16x8_t{};
     if (qi < N) {
-      rq = *reinterpret_cast<const bf16x8_t*>(p.q + qi * q_tok + qoff + 16 * ks + 8 * half);
-      rd = *reinterpret_cast<const bf16x8_t*>(p.dout + qi * q_tok + qoff + 16 * ks + 8 * half);
+      const __bf16* qrow = kFused ? chunk_row(p.cq, (uint32_t)qi, p.bs, b, h, HD) : p.q + qi * q_tok + qoff;
+      const __bf16* drow = kFused ? chunk_row(p.cdo, (uint32_t)qi, p.bs, b, h, HD) : p.dout + qi * q_tok + qoff;
+      rq = *reinterpret_cast<const bf16x8_t*>(qrow + 16 * ks + 8 * half);
+      rd = *reinterpret_cast<const bf16x8_t*>(drow + 16 * ks + 8 * half);
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -179,7 +190,7 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_kernel(BwdParams p) {
   // + 1024) of a tile buffer, lane l at +16 l, so lane l fetches the source
   // chunk that the swizzle places there.  Rows past the sequence end repeat
   // row N-1 (masked for every query).
-  const int64_t row_bytes = kv_tok * 2;
+  const int64_t row_bytes = kFused ? (int64_t)p.bs * p.ck.row_heads * HD * 2 : kv_tok * 2;
   uint32_t slice_off[C::kCopiesPerWave];
 #pragma unroll
   for (int c = 0; c < C::kCopiesPerWave; ++c) {
@@ -188,10 +199,15 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_kernel(BwdParams p) {
     const int col_bytes = ((lane % C::kChunks) ^ swz_f<C::kChunks>(row0)) * 16;
     slice_off[c] = (uint32_t)(row0 * row_bytes) + (uint32_t)col_bytes;
   }
-  auto copy_slice = [&](const __bf16* base, char* buf, int m, int c) __attribute__((always_inline)) {
+  auto copy_slice = [&](const __bf16* base, const SeqChunks& ch, char* buf, int m, int c)
+      __attribute__((always_inline)) {
     const int64_t j0 = (t_begin + m) * C::kBC;
-    const char* tile =
-        reinterpret_cast<const char*>(wave_uniform((int64_t)base + j0 * row_bytes));
+    const char* tile;
+    if constexpr (kFused)
+      tile = reinterpret_cast<const char*>(
+          wave_uniform(chunk_tile_base(ch, (uint32_t)(t_begin + m), p.bs, b, kh, HD)));
+    else
+      tile = reinterpret_cast<const char*>(wave_uniform((int64_t)base + j0 * row_bytes));
     const int cidx = wave * C::kCopiesPerWave + c;
     uint32_t off = slice_off[c];
     if (m >= m_tail) {   // the tile runs past the sequence end
@@ -303,7 +319,7 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_kernel(BwdParams p) {
     if (c >= C::kCopiesPerWave) return;
     const int t = m + 3 < last ? m + 3 : last;
     char* buf = is_v ? v_buf((r + 3) & 3) : k_buf(ks5);
-    copy_slice(is_v ? vbase : kbase, buf, t, c);
+    copy_slice(is_v ? vbase : kbase, is_v ? p.cv : p.ck, buf, t, c);
     __builtin_amdgcn_sched_barrier(0);
   };
   auto copy_pair = [&](int m, auto r_tag, int ks5) __attribute__((always_inline)) {
@@ -339,8 +355,8 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_kernel(BwdParams p) {
     for (int t = 0; t < 3; ++t)
 #pragma unroll
       for (int c = 0; c < C::kCopiesPerWave; ++c) {
-        copy_slice(kbase, k_buf(t), t < last ? t : last, c);
-        copy_slice(vbase, v_buf(t), t < last ? t : last, c);
+        copy_slice(kbase, p.ck, k_buf(t), t < last ? t : last, c);
+        copy_slice(vbase, p.cv, v_buf(t), t < last ? t : last, c);
       }
     wait_vmem();
     block_barrier();
@@ -381,7 +397,7 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_kernel(BwdParams p) {
   else run(integral_constant<int, 1>{});
 
   if (qi >= N) return;
-  __bf16* orow = p.dq + qi * q_tok + qoff;
+  __bf16* orow = kFused ? chunk_row(p.cdq, (uint32_t)qi, p.bs, b, h, HD) : p.dq + qi * q_tok + qoff;
 #pragma unroll
   for (int db = 0; db < C::kDB; ++db)
 #pragma unroll
@@ -490,7 +506,7 @@ struct DkvSched {
 };
 using DkvSchedDefault = DkvSched<3, 1, 0, false, false, 16>;
 
-template <int HD, class SC = DkvSchedDefault>
+template <int HD, bool kFused, class SC = DkvSchedDefault>
 __global__ __launch_bounds__(512) void attn_bwd_dkv_kernel(BwdParams p) {
   using C = DkvCfg<HD>;
   using std::false_type;
@@ -523,10 +539,14 @@ __global__ __launch_bounds__(512) void attn_bwd_dkv_kernel(BwdParams p) {
   {
     const __bf16* rows = p_wave ? p.k : p.v;
     const float mul = p_wave ? p.scale_log2 : 1.0f;
+    const __bf16* krow = nullptr;
+    if (kj < N)
+      krow = kFused ? chunk_row(p_wave ? p.ck : p.cv, (uint32_t)kj, p.bs, b, kh, HD)
+                    : rows + kj * kv_tok + kvoff;
 #pragma unroll
     for (int ks = 0; ks < C::kKS; ++ks) {
       bf16x8_t raw = bf16x8_t{};
-      if (kj < N) raw = *reinterpret_cast<const bf16x8_t*>(rows + kj * kv_tok + kvoff + 16 * ks + 8 * half);
+      if (kj < N) raw = *reinterpret_cast<const bf16x8_t*>(krow + 16 * ks + 8 * half);
 #pragma unroll
       for (int e = 0; e < 8; ++e) bfrag[ks][e] = (__bf16)((float)raw[e] * mul);
     }
@@ -560,7 +580,7 @@ __global__ __launch_bounds__(512) void attn_bwd_dkv_kernel(BwdParams p) {
   // tile buffer, lane l at +16 l, so lane l fetches the source chunk that
   // the swizzle places there.  Rows past N repeat row N-1 (the tail tile);
   // those queries are masked for every key, so only finiteness matters.
-  const int64_t row_bytes = q_tok * 2;
+  const int64_t row_bytes = kFused ? (int64_t)p.bs * p.cq.row_heads * HD * 2 : q_tok * 2;
   uint32_t slice_off[C::kCopies];
 #pragma unroll
   for (int c = 0; c < C::kCopies; ++c) {
@@ -594,8 +614,13 @@ __global__ __launch_bounds__(512) void attn_bwd_dkv_kernel(BwdParams p) {
     const int64_t i0 = (int64_t)c.t * C::kBQ;
     if (k < C::kCopies) {
       const __bf16* src = kQ ? p.q : p.dout;
-      const char* base = reinterpret_cast<const char*>(
-          wave_uniform(reinterpret_cast<int64_t>(src + i0 * q_tok + ((int64_t)b * p.hq + h) * HD)));
+      const char* base;
+      if constexpr (kFused)
+        base = reinterpret_cast<const char*>(
+            wave_uniform(chunk_tile_base(kQ ? p.cq : p.cdo, (uint32_t)c.t, p.bs, b, h, HD)));
+      else
+        base = reinterpret_cast<const char*>(
+            wave_uniform(reinterpret_cast<int64_t>(src + i0 * q_tok + ((int64_t)b * p.hq + h) * HD)));
       const int cidx = pair * C::kCopies + k;
       uint32_t off = slice_off[k];
       if (c.t >= t_tail) {
@@ -932,7 +957,8 @@ __global__ __launch_bounds__(512) void attn_bwd_dkv_kernel(BwdParams p) {
   wait_vmem();
 
   if (kj < N) {
-    __bf16* row = (p_wave ? p.dv : p.dk) + kj * kv_tok + kvoff;
+    __bf16* row = kFused ? chunk_row(p_wave ? p.cdv : p.cdk, (uint32_t)kj, p.bs, b, kh, HD)
+                         : (p_wave ? p.dv : p.dk) + kj * kv_tok + kvoff;
     const float mul = p_wave ? 1.f : p.scale;
 #pragma unroll
     for (int d = 0; d < C::kDB; ++d)
@@ -948,75 +974,61 @@ __global__ __launch_bounds__(512) void attn_bwd_dkv_kernel(BwdParams p) {
 
 // -D_i = -<dO_i, O_i> and -LSE_i log2(e) of every query row, stored
 // [batch][head][position]: the dQ kernel reads them per row, the dK/dV
-// kernel as 64-row runs.  kLanes lanes reduce one row.
-template <int HD>
+// kernel as 64-row runs.  kLanes lanes reduce one row.  In the fused form O
+// and dO are read from their sequence chunks (co, cdo).
+template <int HD, bool kFused>
 __global__ __launch_bounds__(256) void bwd_stats_kernel(const __bf16* __restrict__ o,
                                                         const __bf16* __restrict__ dout,
                                                         const float* __restrict__ lse,
                                                         float* __restrict__ nD,
                                                         float* __restrict__ nlse2, int64_t rows,
-                                                        int64_t N, int bs, int hq) {
+                                                        int64_t N, int bs, int hq, SeqChunks co,
+                                                        SeqChunks cdo) {
   constexpr int kLanes = HD / 8;
   constexpr int kRowsPerBlock = 256 / kLanes;
   const int64_t r = (int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / kLanes;
   const int sub = threadIdx.x % kLanes;
+  // r enumerates (i, b, h) in the memory order of a head-sharded tensor
+  const int h = (int)(r % hq);
+  const int64_t ib = r / hq;
+  const int b = (int)(ib % bs);
+  const int64_t i = ib / bs;
   float acc = 0.f;
   if (r < rows) {
-    const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(o + r * HD + sub * 8);
-    const bf16x8_t c = *reinterpret_cast<const bf16x8_t*>(dout + r * HD + sub * 8);
+    const __bf16* orow = kFused ? chunk_row(co, (uint32_t)i, bs, b, h, HD) : o + r * HD;
+    const __bf16* drow = kFused ? chunk_row(cdo, (uint32_t)i, bs, b, h, HD) : dout + r * HD;
+    const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(orow + sub * 8);
+    const bf16x8_t c = *reinterpret_cast<const bf16x8_t*>(drow + sub * 8);
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc += (float)a[e] * (float)c[e];
   }
 #pragma unroll
   for (int off = kLanes / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
   if (r < rows && sub == 0) {
-    // r enumerates (i, b, h) in memory order
-    const int h = (int)(r % hq);
-    const int64_t ib = r / hq;
-    const int b = (int)(ib % bs);
-    const int64_t i = ib / bs;
     const int64_t idx = ((int64_t)b * hq + h) * N + i;
     nD[idx] = -acc;
     nlse2[idx] = -(lse[idx] * kLog2e);
   }
 }
 
-template <int HD, int GPACK>
+template <int HD, int GPACK, bool kFused>
 hipError_t launch_dq(BwdParams p, const AttnShape& s, hipStream_t stream) {
   using C = DqCfg<HD, GPACK>;
   p.num_blocks = (s.N + C::kBP - 1) / C::kBP;
   dim3 grid((uint32_t)p.num_blocks, (uint32_t)(s.bs * s.hkv * (p.g / GPACK)));
-  return launch_kernel(attn_bwd_dq_kernel<HD, GPACK>, grid, dim3(C::kThreads), 0, stream, p);
+  return launch_kernel(attn_bwd_dq_kernel<HD, GPACK, kFused>, grid, dim3(C::kThreads), 0, stream, p);
 }
 
-}  // namespace
-
-// Workspace: one fp32 array per query row of [bs, hq, N], 256-byte aligned:
-// D for the fp32 path; -D then -LSE log2(e) for the bf16 path.
-static size_t stat_array_bytes(const AttnShape& s) {
-  return ((size_t)s.N * s.bs * s.hq * sizeof(float) + 255) / 256 * 256;
-}
-
-size_t attn_bwd_workspace_bytes(const AttnShape& s, bool bf16) {
-  return (bf16 ? 2 : 1) * stat_array_bytes(s);
-}
-
-hipError_t launch_attn_bwd_bf16(const AttnShape& s, const void* q, const void* k, const void* v,
-                                const void* o, const float* lse, const void* dout, void* dq,
-                                void* dk, void* dv, void* workspace, hipStream_t stream) {
-  if (s.N == 0) return hipSuccess;
-  BwdParams p;
-  p.q = static_cast<const __bf16*>(q);
-  p.k = static_cast<const __bf16*>(k);
-  p.v = static_cast<const __bf16*>(v);
-  p.dout = static_cast<const __bf16*>(dout);
+// The three launches of the backward (statistics, dQ, dK/dV) for parameters
+// p; o and dout (single-buffer form) or co and cdo (fused form) feed the
+// statistics.
+template <bool kFused>
+hipError_t launch_bwd(BwdParams& p, const AttnShape& s, const __bf16* o, const SeqChunks& co,
+                      const float* lse, void* workspace, hipStream_t stream) {
   float* nD = static_cast<float*>(workspace);
   float* nlse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + stat_array_bytes(s));
   p.nD = nD;
   p.nlse2 = nlse2;
-  p.dq = static_cast<__bf16*>(dq);
-  p.dk = static_cast<__bf16*>(dk);
-  p.dv = static_cast<__bf16*>(dv);
   p.N = s.N;
   p.bs = s.bs;
   p.hq = s.hq;
@@ -1029,26 +1041,25 @@ hipError_t launch_attn_bwd_bf16(const AttnShape& s, const void* q, const void* k
   p.n_docs = s.n_docs;
   p.num_blocks = 0;
 
-  const __bf16* ob = static_cast<const __bf16*>(o);
   const int64_t rows = s.N * s.bs * s.hq;
   const int64_t stat_blocks = (rows + (s.hd == 128 ? 15 : 31)) / (s.hd == 128 ? 16 : 32);
-  hipError_t e = launch_kernel(s.hd == 128 ? bwd_stats_kernel<128> : bwd_stats_kernel<64>,
-                               dim3((uint32_t)stat_blocks), dim3(256), 0, stream, ob, p.dout, lse,
-                               nD, nlse2, rows, s.N, s.bs, s.hq);
+  hipError_t e = launch_kernel(s.hd == 128 ? bwd_stats_kernel<128, kFused> : bwd_stats_kernel<64, kFused>,
+                               dim3((uint32_t)stat_blocks), dim3(256), 0, stream, o, p.dout, lse,
+                               nD, nlse2, rows, s.N, s.bs, s.hq, co, p.cdo);
   if (e != hipSuccess) return e;
 
   auto dq_launch = [&](auto hd_tag) -> hipError_t {
     constexpr int HD = decltype(hd_tag)::value;
-    if (p.g % 8 == 0) return launch_dq<HD, 8>(p, s, stream);
-    if (p.g % 4 == 0) return launch_dq<HD, 4>(p, s, stream);
-    if (p.g % 2 == 0) return launch_dq<HD, 2>(p, s, stream);
-    return launch_dq<HD, 1>(p, s, stream);
+    if (p.g % 8 == 0) return launch_dq<HD, 8, kFused>(p, s, stream);
+    if (p.g % 4 == 0) return launch_dq<HD, 4, kFused>(p, s, stream);
+    if (p.g % 2 == 0) return launch_dq<HD, 2, kFused>(p, s, stream);
+    return launch_dq<HD, 1, kFused>(p, s, stream);
   };
   auto dkv_launch = [&](auto hd_tag) -> hipError_t {
     constexpr int HD = decltype(hd_tag)::value;
     using C = DkvCfg<HD>;
     dim3 grid((uint32_t)((s.N + C::kBK - 1) / C::kBK), (uint32_t)(s.bs * s.hkv));
-    return launch_kernel(attn_bwd_dkv_kernel<HD>, grid, dim3(C::kThreads), 0, stream, p);
+    return launch_kernel(attn_bwd_dkv_kernel<HD, kFused>, grid, dim3(C::kThreads), 0, stream, p);
   };
   if (s.hd == 128) {
     if ((e = dq_launch(std::integral_constant<int, 128>{})) != hipSuccess) return e;
@@ -1056,6 +1067,45 @@ hipError_t launch_attn_bwd_bf16(const AttnShape& s, const void* q, const void* k
   }
   if ((e = dq_launch(std::integral_constant<int, 64>{})) != hipSuccess) return e;
   return dkv_launch(std::integral_constant<int, 64>{});
+}
+
+}  // namespace
+
+
+size_t attn_bwd_workspace_bytes(const AttnShape& s, bool bf16) {
+  return (bf16 ? 2 : 1) * stat_array_bytes(s);
+}
+
+hipError_t launch_attn_bwd_bf16(const AttnShape& s, const void* q, const void* k, const void* v,
+                                const void* o, const float* lse, const void* dout, void* dq,
+                                void* dk, void* dv, void* workspace, hipStream_t stream) {
+  if (s.N == 0) return hipSuccess;
+  BwdParams p{};
+  p.q = static_cast<const __bf16*>(q);
+  p.k = static_cast<const __bf16*>(k);
+  p.v = static_cast<const __bf16*>(v);
+  p.dout = static_cast<const __bf16*>(dout);
+  p.dq = static_cast<__bf16*>(dq);
+  p.dk = static_cast<__bf16*>(dk);
+  p.dv = static_cast<__bf16*>(dv);
+  return launch_bwd<false>(p, s, static_cast<const __bf16*>(o), p.cq, lse, workspace, stream);
+}
+
+hipError_t launch_attn_bwd_bf16_fused(const AttnShape& s, const SeqChunks& q, const SeqChunks& k,
+                                      const SeqChunks& v, const SeqChunks& o, const float* lse,
+                                      const SeqChunks& dout, const SeqChunks& dq,
+                                      const SeqChunks& dk, const SeqChunks& dv, void* workspace,
+                                      hipStream_t stream) {
+  if (s.N == 0) return hipSuccess;
+  BwdParams p{};
+  p.cq = q;
+  p.ck = k;
+  p.cv = v;
+  p.cdo = dout;
+  p.cdq = dq;
+  p.cdk = dk;
+  p.cdv = dv;
+  return launch_bwd<true>(p, s, nullptr, o, lse, workspace, stream);
 }
 
 }  // namespace ulysses

@@ -76,14 +76,6 @@ struct FwdParams {
   SeqChunks cq, ck, cv, co;
 };
 
-// Element offset of row i (batch b, rank head h) from the start of its
-// sequence chunk, and that chunk: see SeqChunks.
-__device__ __forceinline__ int64_t chunk_row_offset(const SeqChunks& c, uint32_t i, int bs, int b,
-                                                    int h, int hd, uint32_t* chunk) {
-  const uint32_t ci = i / (uint32_t)c.n;
-  *chunk = ci;
-  return (((int64_t)(i - ci * (uint32_t)c.n) * bs + b) * c.row_heads + c.head0 + h) * hd;
-}
 
 template <int HD, int GPACK>
 struct FwdCfg {
@@ -143,9 +135,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdParams p) {
       kFused ? (int64_t)p.cv.chunk[0] : reinterpret_cast<int64_t>(p.v + ((int64_t)b * p.hkv + kh) * HD)));
   // Address of row i of Q (or O) for this lane's head.
   auto q_row = [&](const SeqChunks& c, int64_t i) __attribute__((always_inline)) {
-    uint32_t ci;
-    const int64_t off = chunk_row_offset(c, (uint32_t)i, p.bs, b, h, HD, &ci);
-    return reinterpret_cast<__bf16*>(c.chunk[ci]) + off;
+    return chunk_row(c, (uint32_t)i, p.bs, b, h, HD);
   };
 
   // Q fragments (B operand of S^T): lane holds Q[qi][16 ks + 8 half + 0..7],
@@ -213,12 +203,9 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdParams p) {
       __attribute__((always_inline)) {
     const int64_t j0 = (t_begin + m) * C::kBC;
     const char* tile;
-    if constexpr (kFused) {   // the tile's chunk and its first row within it
-      const uint32_t tt = (uint32_t)(t_begin + m);
-      const uint32_t ci = fast_div(tt, ch.tiles_per_chunk);
-      const int64_t s0 = (int64_t)(tt - ci * ch.tiles_per_chunk.d) * C::kBC;
-      tile = reinterpret_cast<const char*>(wave_uniform(
-          (int64_t)ch.chunk[ci] + ((s0 * p.bs + b) * ch.row_heads + ch.head0 + kh) * HD * 2));
+    if constexpr (kFused) {
+      tile = reinterpret_cast<const char*>(
+          wave_uniform(chunk_tile_base(ch, (uint32_t)(t_begin + m), p.bs, b, kh, HD)));
     } else {
       tile = reinterpret_cast<const char*>(wave_uniform((int64_t)base + j0 * row_bytes));
     }

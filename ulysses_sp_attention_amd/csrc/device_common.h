@@ -182,6 +182,33 @@ __device__ __forceinline__ uint32_t fast_div(uint32_t n, FD f) {
   return (uint32_t)(((uint64_t)t + n) >> f.l);
 }
 
+// Addresses in an operand held as sequence chunks (SeqChunks in launch.h):
+// the element offset of row i (batch b, head h of the rank's slice) from the
+// start of its chunk, whose index goes to *chunk ...
+template <typename SC>
+__device__ __forceinline__ int64_t chunk_row_offset(const SC& c, uint32_t i, int bs, int b, int h,
+                                                    int hd, uint32_t* chunk) {
+  const uint32_t ci = i / (uint32_t)c.n;
+  *chunk = ci;
+  return (((int64_t)(i - ci * (uint32_t)c.n) * bs + b) * c.row_heads + c.head0 + h) * hd;
+}
+// ... the address of that row ...
+template <typename SC>
+__device__ __forceinline__ __bf16* chunk_row(const SC& c, uint32_t i, int bs, int b, int h, int hd) {
+  uint32_t ci;
+  const int64_t off = chunk_row_offset(c, i, bs, b, h, hd, &ci);
+  return reinterpret_cast<__bf16*>(c.chunk[ci]) + off;
+}
+// ... and the byte address of the first row of 64-row tile `tile` (tiles
+// never straddle chunks).
+template <typename SC>
+__device__ __forceinline__ int64_t chunk_tile_base(const SC& c, uint32_t tile, int bs, int b, int h,
+                                                   int hd) {
+  const uint32_t ci = fast_div(tile, c.tiles_per_chunk);
+  const int64_t s0 = (int64_t)(tile - ci * c.tiles_per_chunk.d) * 64;
+  return (int64_t)c.chunk[ci] + ((s0 * bs + b) * c.row_heads + c.head0 + h) * hd * 2;
+}
+
 // A value the whole wave agrees on, moved to scalar registers so that
 // branches on it stay scalar branches.
 __device__ __forceinline__ int64_t wave_uniform(int64_t x) {

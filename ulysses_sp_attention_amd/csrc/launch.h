@@ -92,6 +92,13 @@ size_t attn_bwd_workspace_bytes(const AttnShape& s, bool bf16);
 hipError_t launch_attn_bwd_bf16(const AttnShape& s, const void* q, const void* k, const void* v,
                                 const void* o, const float* lse, const void* dout, void* dq,
                                 void* dk, void* dv, void* workspace, hipStream_t stream);
+// The backward with every operand in its sequence chunks (dq, dk, dv written
+// into the rank's head slots).
+hipError_t launch_attn_bwd_bf16_fused(const AttnShape& s, const SeqChunks& q, const SeqChunks& k,
+                                      const SeqChunks& v, const SeqChunks& o, const float* lse,
+                                      const SeqChunks& dout, const SeqChunks& dq,
+                                      const SeqChunks& dk, const SeqChunks& dv, void* workspace,
+                                      hipStream_t stream);
 hipError_t launch_attn_bwd_f32(const AttnShape& s, const float* q, const float* k, const float* v,
                                const float* o, const float* lse, const float* dout, float* dq,
                                float* dk, float* dv, void* workspace, hipStream_t stream);
