@@ -219,6 +219,10 @@ def main():
     breakdown["pack_all"] = {"ms": pack_ms, "GB/s": gbps(pack_bytes, pack_ms),
                              "frac_of_hbm_peak": gbps(pack_bytes, pack_ms) / HBM_PEAK_GBPS}
 
+    breakdown["fused_step"] = measure_fused(uly, torch, np, stream, args, r, scale, lse, ws,
+                                            (cq, ck, cv, co, cdo, cdq, cdk, cdv),
+                                            fwd_flop, bwd_flop, ms_step)
+
     rotated = measure_exchanges(w, uly, torch, stream, args.pack_sets, args.pack_reps)
     breakdown["pack_rotated"] = rotated
     breakdown["attn_merge"] = measure_merge(w, uly, torch, stream, args.pack_sets, args.pack_reps)
@@ -276,6 +280,42 @@ def main():
     }
     print(json.dumps(line))
     return 0
+
+
+def measure_fused(uly, torch, np, stream, args, rank, scale, lse, ws, tables, fwd_flop,
+                  bwd_flop, unfused_ms):
+    """The same step with the exchange fused into the attention kernels
+    (ulysses_attn_fwd_fused + ulysses_attn_bwd_fused: no head-sharded copies,
+    no exchange launches), timed like the main step."""
+    cq, ck, cv, co, cdo, cdq, cdk, cdv = tables
+
+    def fstep(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        uly.ulysses_attn_fwd_fused(cq, ck, cv, co, lse, rank, scale, True)
+        if ev is not None:
+            ev[1].record(stream)
+        uly.ulysses_attn_bwd_fused(cq, ck, cv, co, lse, cdo, cdq, cdk, cdv, ws, rank, scale, True)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        fstep()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for s_ in range(args.steps):
+        fstep(events[s_])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    fwd_ms = float(np.mean([ev[0].elapsed_time(ev[1]) for ev in events]))
+    bwd_ms = float(np.mean([ev[1].elapsed_time(ev[2]) for ev in events]))
+    tf = (fwd_flop + bwd_flop) / (ms * 1e-3) / 1e12
+    return {"ms_per_step": ms, "TFLOP/s": tf, "speedup_vs_unfused_step": unfused_ms / ms,
+            "attn_fwd_fused": {"ms": fwd_ms, "TFLOP/s": fwd_flop / (fwd_ms * 1e-3) / 1e12},
+            "attn_bwd_fused": {"ms": bwd_ms, "TFLOP/s": bwd_flop / (bwd_ms * 1e-3) / 1e12},
+            "method": "ulysses_attn_fwd_fused + ulysses_attn_bwd_fused on the sequence chunks, "
+                      "same inputs, steps and warmup as the main step"}
 
 
 def time_rotated(torch, stream, fns, reps):

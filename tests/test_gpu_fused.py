@@ -1,7 +1,10 @@
-"""The exchange fused into attention: the fused forward must equal
-seq_to_head -> attention -> head_to_seq bit for bit (same arithmetic on the
-same values; only where rows are read and written differs), and must leave
-the other ranks' head slots of the output chunks untouched."""
+"""The exchange fused into attention: the fused forward and backward must
+equal seq_to_head -> attention -> head_to_seq bit for bit (same arithmetic on
+the same values; only where rows are read and written differs), and must
+leave the other ranks' head slots of the output chunks untouched.  Every case
+runs with the chunks as consecutive slices of one tensor (the strided-view
+kernels) and as separate buffers at descending addresses (the chunk-table
+kernels)."""
 import numpy as np
 import pytest
 
@@ -21,6 +24,28 @@ def lib():
 def split(t, P):
     n = t.shape[0] // P
     return [t[c * n:(c + 1) * n] for c in range(P)]
+
+
+LAYOUTS = ["contiguous", "scattered"]
+
+
+def place(t, P, layout):
+    """P chunks holding t's sequence slices: views of t itself, or copies in
+    one buffer in reverse order with a gap (no chunk follows its predecessor)."""
+    if layout == "contiguous":
+        return split(t, P)
+    import torch
+    n = t.shape[0] // P
+    buf = torch.empty(((P + 1) * n,) + tuple(t.shape[1:]), dtype=t.dtype, device=t.device)
+    chunks = [buf[(P - c) * n:(P - c + 1) * n] for c in range(P)]
+    for c in range(P):
+        chunks[c].copy_(t[c * n:(c + 1) * n])
+    return chunks
+
+
+def gather(chunks):
+    import torch
+    return torch.cat(list(chunks), dim=0)
 
 
 def local_heads(heads, P):
@@ -60,22 +85,31 @@ FWD_CASES = [
 ]
 
 
+@pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("P,rank,n,bs,hq,hkv,hd,causal,cu", FWD_CASES)
-def test_fused_fwd_equals_exchange_attention_exchange(P, rank, n, bs, hq, hkv, hd, causal, cu):
+def test_fused_fwd_equals_exchange_attention_exchange(P, rank, n, bs, hq, hkv, hd, causal, cu,
+                                                      layout):
     import torch
-    import ulysses_sp_attention_amd as uly
     N, seed, scale = P * n, 4200 + P * 7 + rank, 1.0 / np.sqrt(hd)
     q = to_device(synth.normal(seed, synth.STREAM_Q, (N, bs, hq, hd), "bf16"), "bf16")
     k = to_device(synth.normal(seed, synth.STREAM_K, (N, bs, hkv, hd), "bf16"), "bf16")
     v = to_device(synth.normal(seed, synth.STREAM_V, (N, bs, hkv, hd), "bf16"), "bf16")
     cu_t = None if cu is None else torch.tensor(cu, dtype=torch.int32, device="cuda")
-    qc, kc, vc = split(q, P), split(k, P), split(v, P)
+    check_fwd(q, k, v, P, rank, scale, causal, cu_t, layout)
+
+
+def check_fwd(q, k, v, P, rank, scale, causal, cu_t, layout):
+    import torch
+    import ulysses_sp_attention_amd as uly
+    hq = q.shape[2]
     o_ref = torch.full_like(q, CANARY)
-    lse_ref = unfused_fwd(qc, kc, vc, rank, scale, causal, cu_t, o_ref)
-    o = torch.full_like(q, CANARY)
+    lse_ref = unfused_fwd(split(q, P), split(k, P), split(v, P), rank, scale, causal, cu_t, o_ref)
+    oc = place(torch.full_like(q, CANARY), P, layout)
     lse = torch.full_like(lse_ref, float("nan"))
-    uly.ulysses_attn_fwd_fused(qc, kc, vc, split(o, P), lse, rank, scale, causal, cu_t)
+    uly.ulysses_attn_fwd_fused(place(q, P, layout), place(k, P, layout), place(v, P, layout), oc,
+                               lse, rank, scale, causal, cu_t)
     torch.cuda.synchronize()
+    o = gather(oc)
     assert storage_bytes(o) == storage_bytes(o_ref)      # other ranks' slots keep the canary
     assert storage_bytes(lse) == storage_bytes(lse_ref)
     hl = hq // P
@@ -83,10 +117,10 @@ def test_fused_fwd_equals_exchange_attention_exchange(P, rank, n, bs, hq, hkv, h
     assert bool(torch.all(untouched == CANARY))
 
 
-def test_fused_fwd_full_size_llama8b_128k():
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_fused_fwd_full_size_llama8b_128k(layout):
     """The benchmark's shape: P = 8 chunks of 16384 tokens, 32 q / 8 kv heads, rank 3."""
     import torch
-    import ulysses_sp_attention_amd as uly
     P, rank, n, hq, hkv, hd = 8, 3, 16384, 32, 8, 128
     N = P * n
     gen = torch.Generator(device="cuda")
@@ -94,15 +128,7 @@ def test_fused_fwd_full_size_llama8b_128k():
     q = (torch.randn((N, 1, hq, hd), device="cuda", generator=gen) / np.sqrt(hd)).to(torch.bfloat16)
     k = torch.randn((N, 1, hkv, hd), device="cuda", generator=gen).to(torch.bfloat16)
     v = torch.randn((N, 1, hkv, hd), device="cuda", generator=gen).to(torch.bfloat16)
-    qc, kc, vc = split(q, P), split(k, P), split(v, P)
-    o_ref = torch.full_like(q, CANARY)
-    lse_ref = unfused_fwd(qc, kc, vc, rank, 1.0, True, None, o_ref)
-    o = torch.full_like(q, CANARY)
-    lse = torch.full_like(lse_ref, float("nan"))
-    uly.ulysses_attn_fwd_fused(qc, kc, vc, split(o, P), lse, rank, 1.0, True, None)
-    torch.cuda.synchronize()
-    assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16))
-    assert torch.equal(lse.view(torch.int32), lse_ref.view(torch.int32))
+    check_fwd(q, k, v, P, rank, 1.0, True, None, layout)
 
 
 def unfused_bwd(qc, kc, vc, oc, lse, doc, rank, scale, causal, cu_t, dq_full, dk_full, dv_full):
@@ -133,25 +159,26 @@ def workspace(N, bs, hq_l, hkv_l, hd):
     return torch.full((nbytes // 4,), float("nan"), dtype=torch.float32, device="cuda")
 
 
-def check_bwd(q, k, v, do, P, rank, scale, causal, cu_t):
+def check_bwd(q, k, v, do, P, rank, scale, causal, cu_t, layout):
     """Forward (fused), then the fused backward against the unfused chain."""
     import torch
     import ulysses_sp_attention_amd as uly
     N, bs, hq, hd = q.shape
     hkv = k.shape[2]
-    qc, kc, vc, doc = split(q, P), split(k, P), split(v, P), split(do, P)
     o = torch.full_like(q, CANARY)
     lse = torch.empty((bs, hq // P, N), dtype=torch.float32, device="cuda")
-    uly.ulysses_attn_fwd_fused(qc, kc, vc, split(o, P), lse, rank, scale, causal, cu_t)
-    oc = split(o, P)
-    ref = [torch.full_like(t, CANARY) for t in (q, k, v)]
-    unfused_bwd(qc, kc, vc, oc, lse, doc, rank, scale, causal, cu_t, *ref)
-    got = [torch.full_like(t, CANARY) for t in (q, k, v)]
-    ws = workspace(N, bs, hq // P, hkv // P, hd)
-    uly.ulysses_attn_bwd_fused(qc, kc, vc, oc, lse, doc, *[split(t, P) for t in got], ws, rank,
+    uly.ulysses_attn_fwd_fused(split(q, P), split(k, P), split(v, P), split(o, P), lse, rank,
                                scale, causal, cu_t)
+    ref = [torch.full_like(t, CANARY) for t in (q, k, v)]
+    unfused_bwd(split(q, P), split(k, P), split(v, P), split(o, P), lse, split(do, P), rank, scale,
+                causal, cu_t, *ref)
+    outs = [place(torch.full_like(t, CANARY), P, layout) for t in (q, k, v)]
+    ws = workspace(N, bs, hq // P, hkv // P, hd)
+    uly.ulysses_attn_bwd_fused(*[place(t, P, layout) for t in (q, k, v, o)], lse,
+                               place(do, P, layout), *outs, ws, rank, scale, causal, cu_t)
     torch.cuda.synchronize()
-    for name, g, r, heads in zip(("dq", "dk", "dv"), got, ref, (hq, hkv, hkv)):
+    for name, oc, r, heads in zip(("dq", "dk", "dv"), outs, ref, (hq, hkv, hkv)):
+        g = gather(oc)
         assert torch.equal(g.view(torch.int16), r.view(torch.int16)), name
         hl = heads // P
         untouched = torch.cat([g[:, :, :rank * hl], g[:, :, (rank + 1) * hl:]], dim=2)
@@ -171,8 +198,10 @@ BWD_CASES = [
 ]
 
 
+@pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("P,rank,n,bs,hq,hkv,hd,causal,cu", BWD_CASES)
-def test_fused_bwd_equals_exchange_backward_exchange(P, rank, n, bs, hq, hkv, hd, causal, cu):
+def test_fused_bwd_equals_exchange_backward_exchange(P, rank, n, bs, hq, hkv, hd, causal, cu,
+                                                     layout):
     import torch
     N, seed, scale = P * n, 5200 + P * 7 + rank, 1.0 / np.sqrt(hd)
     q = to_device(synth.normal(seed, synth.STREAM_Q, (N, bs, hq, hd), "bf16"), "bf16")
@@ -180,10 +209,11 @@ def test_fused_bwd_equals_exchange_backward_exchange(P, rank, n, bs, hq, hkv, hd
     v = to_device(synth.normal(seed, synth.STREAM_V, (N, bs, hkv, hd), "bf16"), "bf16")
     do = to_device(synth.normal(seed, synth.STREAM_DO, (N, bs, hq, hd), "bf16"), "bf16")
     cu_t = None if cu is None else torch.tensor(cu, dtype=torch.int32, device="cuda")
-    check_bwd(q, k, v, do, P, rank, scale, causal, cu_t)
+    check_bwd(q, k, v, do, P, rank, scale, causal, cu_t, layout)
 
 
-def test_fused_bwd_full_size_llama8b_128k():
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_fused_bwd_full_size_llama8b_128k(layout):
     """The benchmark's shape: P = 8 chunks of 16384 tokens, 32 q / 8 kv heads, rank 3."""
     import torch
     P, rank, n, hq, hkv, hd = 8, 3, 16384, 32, 8, 128
@@ -194,4 +224,4 @@ def test_fused_bwd_full_size_llama8b_128k():
     k = torch.randn((N, 1, hkv, hd), device="cuda", generator=gen).to(torch.bfloat16)
     v = torch.randn((N, 1, hkv, hd), device="cuda", generator=gen).to(torch.bfloat16)
     do = torch.randn((N, 1, hq, hd), device="cuda", generator=gen).to(torch.bfloat16)
-    check_bwd(q, k, v, do, P, rank, 1.0, True, None)
+    check_bwd(q, k, v, do, P, rank, 1.0, True, None, layout)

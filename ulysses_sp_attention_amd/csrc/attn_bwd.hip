@@ -51,6 +51,10 @@ struct BwdParams {
   __bf16* dv;
   int64_t N;
   int bs, hq, hkv, g;
+  // Heads per token row in memory of q/o/dout/dq and of k/v/dk/dv: hq and
+  // hkv for head-sharded tensors, the global counts for strided views of
+  // the sequence chunks (the pointers then point at the rank's first head).
+  int q_row_heads, kv_row_heads;
   float scale;
   float scale_log2;
   int causal;
@@ -133,14 +137,14 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_kernel(BwdParams p) {
   const int64_t pw = p0 + (int64_t)(wave / GPACK) * 32;
   const int64_t qi = pw + r32;
 
-  const int64_t q_tok = (int64_t)p.bs * p.hq * HD;
-  const int64_t kv_tok = (int64_t)p.bs * p.hkv * HD;
-  const int64_t qoff = ((int64_t)b * p.hq + h) * HD;
+  const int64_t q_tok = (int64_t)p.bs * p.q_row_heads * HD;
+  const int64_t kv_tok = (int64_t)p.bs * p.kv_row_heads * HD;
+  const int64_t qoff = ((int64_t)b * p.q_row_heads + h) * HD;
   // (Kept in scalar registers: the copies take their base from there.)
   const __bf16* kbase = reinterpret_cast<const __bf16*>(wave_uniform(
-      kFused ? (int64_t)p.ck.chunk[0] : reinterpret_cast<int64_t>(p.k + ((int64_t)b * p.hkv + kh) * HD)));
+      kFused ? (int64_t)p.ck.chunk[0] : reinterpret_cast<int64_t>(p.k + ((int64_t)b * p.kv_row_heads + kh) * HD)));
   const __bf16* vbase = reinterpret_cast<const __bf16*>(wave_uniform(
-      kFused ? (int64_t)p.cv.chunk[0] : reinterpret_cast<int64_t>(p.v + ((int64_t)b * p.hkv + kh) * HD)));
+      kFused ? (int64_t)p.cv.chunk[0] : reinterpret_cast<int64_t>(p.v + ((int64_t)b * p.kv_row_heads + kh) * HD)));
 
   // B operands of this lane's query row: Q' (scaled, rounded once) and dO.
   bf16x8_t qf[C::kKS], df[C::kKS];
@@ -529,9 +533,9 @@ __global__ __launch_bounds__(512) void attn_bwd_dkv_kernel(BwdParams p) {
   const int64_t kw = k0 + 32 * pair;                // first key of the block
   const int64_t kj = kw + r32;                      // this lane's key
 
-  const int64_t q_tok = (int64_t)p.bs * p.hq * HD;
-  const int64_t kv_tok = (int64_t)p.bs * p.hkv * HD;
-  const int64_t kvoff = ((int64_t)b * p.hkv + kh) * HD;
+  const int64_t q_tok = (int64_t)p.bs * p.q_row_heads * HD;
+  const int64_t kv_tok = (int64_t)p.bs * p.kv_row_heads * HD;
+  const int64_t kvoff = ((int64_t)b * p.kv_row_heads + kh) * HD;
 
   // B operand rows of this lane: K' (P wave) or V (dS wave; the multiply by
   // one leaves it exact).
@@ -620,7 +624,7 @@ __global__ __launch_bounds__(512) void attn_bwd_dkv_kernel(BwdParams p) {
             wave_uniform(chunk_tile_base(kQ ? p.cq : p.cdo, (uint32_t)c.t, p.bs, b, h, HD)));
       else
         base = reinterpret_cast<const char*>(
-            wave_uniform(reinterpret_cast<int64_t>(src + i0 * q_tok + ((int64_t)b * p.hq + h) * HD)));
+            wave_uniform(reinterpret_cast<int64_t>(src + i0 * q_tok + ((int64_t)b * p.q_row_heads + h) * HD)));
       const int cidx = pair * C::kCopies + k;
       uint32_t off = slice_off[k];
       if (c.t >= t_tail) {
@@ -1020,9 +1024,9 @@ hipError_t launch_dq(BwdParams p, const AttnShape& s, hipStream_t stream) {
 }
 
 // The three launches of the backward (statistics, dQ, dK/dV) for parameters
-// p; o and dout (single-buffer form) or co and cdo (fused form) feed the
-// statistics.
-template <bool kFused>
+// p; o and p.dout (single-buffer statistics) or co and p.cdo (chunked
+// statistics) feed the statistics.
+template <bool kFused, bool kStatsFused = kFused>
 hipError_t launch_bwd(BwdParams& p, const AttnShape& s, const __bf16* o, const SeqChunks& co,
                       const float* lse, void* workspace, hipStream_t stream) {
   float* nD = static_cast<float*>(workspace);
@@ -1034,6 +1038,8 @@ hipError_t launch_bwd(BwdParams& p, const AttnShape& s, const __bf16* o, const S
   p.hq = s.hq;
   p.hkv = s.hkv;
   p.g = s.hq / s.hkv;
+  if (!p.q_row_heads) p.q_row_heads = s.hq;
+  if (!p.kv_row_heads) p.kv_row_heads = s.hkv;
   p.scale = s.scale;
   p.scale_log2 = s.scale * kLog2e;
   p.causal = s.causal;
@@ -1043,7 +1049,8 @@ hipError_t launch_bwd(BwdParams& p, const AttnShape& s, const __bf16* o, const S
 
   const int64_t rows = s.N * s.bs * s.hq;
   const int64_t stat_blocks = (rows + (s.hd == 128 ? 15 : 31)) / (s.hd == 128 ? 16 : 32);
-  hipError_t e = launch_kernel(s.hd == 128 ? bwd_stats_kernel<128, kFused> : bwd_stats_kernel<64, kFused>,
+  hipError_t e = launch_kernel(s.hd == 128 ? bwd_stats_kernel<128, kStatsFused>
+                                            : bwd_stats_kernel<64, kStatsFused>,
                                dim3((uint32_t)stat_blocks), dim3(256), 0, stream, o, p.dout, lse,
                                nD, nlse2, rows, s.N, s.bs, s.hq, co, p.cdo);
   if (e != hipSuccess) return e;
@@ -1098,6 +1105,28 @@ hipError_t launch_attn_bwd_bf16_fused(const AttnShape& s, const SeqChunks& q, co
                                       hipStream_t stream) {
   if (s.N == 0) return hipSuccess;
   BwdParams p{};
+  p.cdo = dout;   // the statistics read O and dO from their chunks either way
+  const uintptr_t base[7] = {
+      contiguous_base(q, s.N, s.bs, s.hd),  contiguous_base(k, s.N, s.bs, s.hd),
+      contiguous_base(v, s.N, s.bs, s.hd),  contiguous_base(dout, s.N, s.bs, s.hd),
+      contiguous_base(dq, s.N, s.bs, s.hd), contiguous_base(dk, s.N, s.bs, s.hd),
+      contiguous_base(dv, s.N, s.bs, s.hd)};
+  bool strided = true;
+  for (uintptr_t b : base) strided = strided && b != 0;
+  if (strided) {
+    // Every gradient-kernel table is a strided view of one tensor: the
+    // single-buffer kernels with the global head counts as row strides.
+    p.q = reinterpret_cast<const __bf16*>(base[0]);
+    p.k = reinterpret_cast<const __bf16*>(base[1]);
+    p.v = reinterpret_cast<const __bf16*>(base[2]);
+    p.dout = reinterpret_cast<const __bf16*>(base[3]);
+    p.dq = reinterpret_cast<__bf16*>(base[4]);
+    p.dk = reinterpret_cast<__bf16*>(base[5]);
+    p.dv = reinterpret_cast<__bf16*>(base[6]);
+    p.q_row_heads = q.row_heads;
+    p.kv_row_heads = k.row_heads;
+    return launch_bwd<false, true>(p, s, nullptr, o, lse, workspace, stream);
+  }
   p.cq = q;
   p.ck = k;
   p.cv = v;

@@ -66,6 +66,10 @@ struct FwdParams {
   float* lse;
   int64_t N;
   int bs, hq, hkv, g;
+  // Heads per token row in memory of q/o and of k/v: hq and hkv for
+  // head-sharded tensors, the global counts for strided views of the
+  // sequence chunks (q, k, v, o then point at the rank's first head).
+  int q_row_heads, kv_row_heads;
   float scale_log2;   // softmax scale * log2(e)
   int causal;
   const int32_t* cu;
@@ -124,15 +128,15 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdParams p) {
   const int64_t pw = p0 + (int64_t)(wave / GPACK) * 32;
   const int64_t qi = pw + r32;
 
-  const int64_t q_tok = (int64_t)p.bs * p.hq * HD;
-  const int64_t kv_tok = (int64_t)p.bs * p.hkv * HD;
-  const __bf16* qbase = p.q + ((int64_t)b * p.hq + h) * HD;
+  const int64_t q_tok = (int64_t)p.bs * p.q_row_heads * HD;
+  const int64_t kv_tok = (int64_t)p.bs * p.kv_row_heads * HD;
+  const __bf16* qbase = p.q + ((int64_t)b * p.q_row_heads + h) * HD;
   // (Kept in scalar registers: the copies take their base from there.)  In
   // the fused form they are the chunk tables' first chunk, replaced per tile.
   const __bf16* kbase = reinterpret_cast<const __bf16*>(wave_uniform(
-      kFused ? (int64_t)p.ck.chunk[0] : reinterpret_cast<int64_t>(p.k + ((int64_t)b * p.hkv + kh) * HD)));
+      kFused ? (int64_t)p.ck.chunk[0] : reinterpret_cast<int64_t>(p.k + ((int64_t)b * p.kv_row_heads + kh) * HD)));
   const __bf16* vbase = reinterpret_cast<const __bf16*>(wave_uniform(
-      kFused ? (int64_t)p.cv.chunk[0] : reinterpret_cast<int64_t>(p.v + ((int64_t)b * p.hkv + kh) * HD)));
+      kFused ? (int64_t)p.cv.chunk[0] : reinterpret_cast<int64_t>(p.v + ((int64_t)b * p.kv_row_heads + kh) * HD)));
   // Address of row i of Q (or O) for this lane's head.
   auto q_row = [&](const SeqChunks& c, int64_t i) __attribute__((always_inline)) {
     return chunk_row(c, (uint32_t)i, p.bs, b, h, HD);
@@ -476,7 +480,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdParams p) {
   if (qi >= N) return;
   const float l = l_run + wave_xor32_f(l_run);
   const float inv = 1.0f / l;
-  __bf16* orow = kFused ? q_row(p.co, qi) : p.o + (qi * p.bs + b) * (int64_t)p.hq * HD + (int64_t)h * HD;
+  __bf16* orow = kFused ? q_row(p.co, qi) : p.o + (qi * p.bs + b) * (int64_t)p.q_row_heads * HD + (int64_t)h * HD;
 #pragma unroll
   for (int db = 0; db < C::kDB; ++db)
 #pragma unroll
@@ -515,6 +519,8 @@ FwdParams common_params(const AttnShape& s, float* lse) {
   p.hq = s.hq;
   p.hkv = s.hkv;
   p.g = s.hq / s.hkv;
+  p.q_row_heads = s.hq;
+  p.kv_row_heads = s.hkv;
   p.scale_log2 = s.scale * kLog2e;
   p.causal = s.causal;
   p.cu = s.cu;
@@ -530,6 +536,20 @@ hipError_t launch_attn_fwd_bf16_fused(const AttnShape& s, const SeqChunks& q, co
                                       hipStream_t stream) {
   if (s.N == 0) return hipSuccess;
   FwdParams p = common_params(s, lse);
+  const uintptr_t qb = contiguous_base(q, s.N, s.bs, s.hd), kb = contiguous_base(k, s.N, s.bs, s.hd),
+                  vb = contiguous_base(v, s.N, s.bs, s.hd), ob = contiguous_base(o, s.N, s.bs, s.hd);
+  if (qb && kb && vb && ob) {
+    // Every table is a strided view of one tensor: the single-buffer kernel
+    // with the global head counts as row strides.
+    p.q = reinterpret_cast<const __bf16*>(qb);
+    p.k = reinterpret_cast<const __bf16*>(kb);
+    p.v = reinterpret_cast<const __bf16*>(vb);
+    p.o = reinterpret_cast<__bf16*>(ob);
+    p.q_row_heads = q.row_heads;
+    p.kv_row_heads = k.row_heads;
+    if (s.hd == 128) return launch_fwd_hd<128, false>(p, s, stream);
+    return launch_fwd_hd<64, false>(p, s, stream);
+  }
   p.cq = q;
   p.ck = k;
   p.cv = v;

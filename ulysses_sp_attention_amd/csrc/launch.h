@@ -69,6 +69,18 @@ struct SeqChunks {
   FastDiv tiles_per_chunk;
 };
 
+// Base address of this table's first head slot when its chunks are one
+// buffer's consecutive slices (chunk c at chunk[0] + c * n rows of bs *
+// row_heads * hd bf16 values), 0 otherwise.  Such a table is a strided view
+// of one [N, bs, row_heads, hd] tensor.
+inline uintptr_t contiguous_base(const SeqChunks& c, int64_t N, int bs, int hd) {
+  const int64_t P = c.n > 0 ? N / c.n : 0;
+  const uintptr_t step = (uintptr_t)c.n * bs * c.row_heads * hd * 2;
+  for (int64_t i = 1; i < P; ++i)
+    if (c.chunk[i] != c.chunk[0] + (uintptr_t)i * step) return 0;
+  return c.chunk[0] + (uintptr_t)c.head0 * hd * 2;
+}
+
 struct AttnShape {
   int64_t N;
   int bs, hq, hkv, hd;
