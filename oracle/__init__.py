@@ -45,6 +45,9 @@ def _load():
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ci
     lib.oracle_attn_merge.argtypes = [vp, vp, vp, vp, i64, ci, ci, ci, vp, vp]
+    lib.oracle_logits_loss.argtypes = [vp, vp, vp, i64, i64, i64, i64, dbl, vp, vp, vp, vp, vp, vp,
+                                       vp, vp]
+    lib.oracle_logits_loss.restype = ci
     lib.oracle_attn_merge.restype = ci
     lib.oracle_seq_to_head.argtypes = [vp, ci, ci, i64, ci, ci, ci, ci, vp]
     lib.oracle_seq_to_head.restype = ci
@@ -190,3 +193,37 @@ def attn_merge(o_a, lse_a, o_b, lse_b):
     if rc:
         raise ValueError("oracle_attn_merge: bad arguments")
     return o, lse
+
+
+IGNORE_INDEX = -100
+
+
+def logits_loss(h, w, labels, grad_scale: float = 1.0, ignore_index: int = IGNORE_INDEX,
+                magnitude: bool = False):
+    """Cross-entropy of the lm_head logits h W^T against (already shifted)
+    labels and its gradients (see oracle.c).  h [T, d], w [V, d], labels [T].
+    Returns (loss_rows [T], loss_sum, n_good, dh [T, d], dw [V, d]); with
+    magnitude=True also a dict of rounding-bound magnitudes (zmag [T],
+    dh [T, d], dw [V, d])."""
+    h, w = _f64(h), _f64(w)
+    labels = np.ascontiguousarray(labels, dtype=np.int64)
+    T, d = h.shape
+    V = w.shape[0]
+    if w.shape != (V, d) or labels.shape != (T,):
+        raise ValueError("logits_loss: shape mismatch")
+    loss_rows = np.empty(T)
+    loss_sum = np.empty(1)
+    n_good = np.empty(1, dtype=np.int64)
+    dh = np.empty((T, d))
+    dw = np.empty((V, d))
+    mags = [np.empty(T), np.empty((T, d)), np.empty((V, d))] if magnitude else [None] * 3
+    ptr = lambda a: None if a is None else a.ctypes.data
+    rc = _load().oracle_logits_loss(ptr(h), ptr(w), ptr(labels), T, d, V, ignore_index,
+                                    grad_scale, ptr(loss_rows), ptr(loss_sum), ptr(n_good),
+                                    ptr(dh), ptr(dw), *[ptr(m) for m in mags])
+    if rc:
+        raise ValueError(f"oracle_logits_loss: bad arguments ({rc})")
+    out = (loss_rows, float(loss_sum[0]), int(n_good[0]), dh, dw)
+    if magnitude:
+        return out + (dict(zip(("zmag", "dh", "dw"), mags)),)
+    return out

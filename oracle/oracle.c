@@ -468,3 +468,99 @@ int oracle_attn_merge(const double* o_a, const double* lse_a, const double* o_b,
       }
   return 0;
 }
+
+/* ----------------------------------------------------------------------
+ * Language-model loss over the hidden states and its gradients: the
+ * computation that the integration guide's tiled fused logits loss
+ * (section on tiled loss computation) shards over the sequence so that
+ * the [tokens, vocab] logits never exist in full.  Sharding does not change
+ * the result, so the oracle states it whole, by definition:
+ *   z_iv   = <h_i, w_v>                       (lm_head, no bias)
+ *   lse_i  = ln sum_v exp(z_iv)
+ *   loss_i = lse_i - z_i,y_i   for a token whose label y_i is not the
+ *            ignore index (labels arrive already shifted, so label i is
+ *            the target of position i); 0 for an ignored token
+ *   loss_sum = sum_i loss_i,  n_good = number of tokens not ignored
+ *   G_iv   = s (softmax(z_i)_v - [v == y_i]) for a kept token, 0 otherwise,
+ *            the gradient of s * loss_sum with respect to z_iv
+ *   dh = G W   ([T, d]),   dW = G^T H   ([V, d]).
+ * The caller picks s: 1 / (total good tokens over all ranks) gives the
+ * gradient of the guide's loss aggregation (sum of per-rank losses
+ * weighted by good tokens, divided by the total good tokens).
+ * Optional magnitude outputs (any may be NULL) bound the rounding of a
+ * low-precision implementation: zmag_i = max_v sum_k |h_ik w_vk|,
+ * dh_mag = |G| |W|, dw_mag = |G|^T |H|.
+ * h is [T, d], w is [V, d], labels [T]; every output is row-major.
+ * ---------------------------------------------------------------------- */
+int oracle_logits_loss(const double* h, const double* w, const int64_t* labels, int64_t T,
+                       int64_t d, int64_t V, int64_t ignore_index, double s, double* loss_rows,
+                       double* loss_sum, int64_t* n_good, double* dh, double* dw, double* zmag,
+                       double* dh_mag, double* dw_mag) {
+  if (T < 0 || d < 1 || V < 1 || !h || !w || !labels || !loss_rows || !loss_sum || !n_good ||
+      !dh || !dw)
+    return 1;
+  for (int64_t i = 0; i < T; ++i)
+    if (labels[i] != ignore_index && (labels[i] < 0 || labels[i] >= V)) return 2;
+  double* G = (double*)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1) * (size_t)V);
+  if (!G) return 3;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t i = 0; i < T; ++i) {
+    double* z = G + (size_t)i * (size_t)V;
+    double zm = 0.0;
+    for (int64_t v = 0; v < V; ++v) {
+      double acc = 0.0, mag = 0.0;
+      for (int64_t k = 0; k < d; ++k) {
+        acc += h[i * d + k] * w[v * d + k];
+        mag += fabs(h[i * d + k] * w[v * d + k]);
+      }
+      z[v] = acc;
+      if (mag > zm) zm = mag;
+    }
+    if (zmag) zmag[i] = zm;
+    if (labels[i] == ignore_index) {
+      loss_rows[i] = 0.0;
+      for (int64_t v = 0; v < V; ++v) z[v] = 0.0;
+      continue;
+    }
+    double m = z[0];
+    for (int64_t v = 1; v < V; ++v)
+      if (z[v] > m) m = z[v];
+    double sum = 0.0;
+    for (int64_t v = 0; v < V; ++v) sum += exp(z[v] - m);
+    const double lse = m + log(sum);
+    loss_rows[i] = lse - z[labels[i]];
+    for (int64_t v = 0; v < V; ++v) z[v] = s * (exp(z[v] - lse) - (v == labels[i] ? 1.0 : 0.0));
+  }
+  double total = 0.0;
+  int64_t good = 0;
+  for (int64_t i = 0; i < T; ++i) {
+    total += loss_rows[i];
+    if (labels[i] != ignore_index) ++good;
+  }
+  *loss_sum = total;
+  *n_good = good;
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < T; ++i)
+    for (int64_t k = 0; k < d; ++k) {
+      double acc = 0.0, mag = 0.0;
+      for (int64_t v = 0; v < V; ++v) {
+        acc += G[(size_t)i * V + v] * w[v * d + k];
+        mag += fabs(G[(size_t)i * V + v] * w[v * d + k]);
+      }
+      dh[i * d + k] = acc;
+      if (dh_mag) dh_mag[i * d + k] = mag;
+    }
+#pragma omp parallel for schedule(static)
+  for (int64_t v = 0; v < V; ++v)
+    for (int64_t k = 0; k < d; ++k) {
+      double acc = 0.0, mag = 0.0;
+      for (int64_t i = 0; i < T; ++i) {
+        acc += G[(size_t)i * V + v] * h[i * d + k];
+        mag += fabs(G[(size_t)i * V + v] * h[i * d + k]);
+      }
+      dw[v * d + k] = acc;
+      if (dw_mag) dw_mag[v * d + k] = mag;
+    }
+  free(G);
+  return 0;
+}

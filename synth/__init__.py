@@ -24,6 +24,20 @@ _lib = None
 
 # Stream ids of the seeded inputs.
 STREAM_Q, STREAM_K, STREAM_V, STREAM_DO, STREAM_DOCS = 1, 2, 3, 4, 5
+# Streams of the language-model loss inputs: hidden states, lm_head weight,
+# labels and the choice of ignored tokens.
+STREAM_HIDDEN, STREAM_LM_HEAD, STREAM_LABELS, STREAM_IGNORE = 6, 7, 8, 9
+IGNORE_INDEX = -100
+
+
+def lm_labels(seed: int, T: int, vocab: int, ignore_percent: int = 10) -> np.ndarray:
+    """Seeded int64 labels in [0, vocab); about ignore_percent% of them are
+    IGNORE_INDEX (token i is ignored when draw i of STREAM_IGNORE in
+    [0, 100) falls below ignore_percent)."""
+    labels = uniform_int(seed, STREAM_LABELS, T, 0, vocab - 1)
+    drop = uniform_int(seed, STREAM_IGNORE, T, 0, 99) < ignore_percent
+    labels[drop] = IGNORE_INDEX
+    return labels
 
 
 def build_lib() -> str:

@@ -527,3 +527,111 @@ def test_merge_of_a_result_with_itself_keeps_o_and_adds_ln2():
     o, lse = oracle.attn_merge(oa, la, oa, la)
     np.testing.assert_allclose(o, oa, rtol=1e-15, atol=1e-15)
     np.testing.assert_allclose(lse, la + np.log(2.0), rtol=1e-15, atol=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# Language-model loss (lm_head + cross-entropy with ignored labels) and its
+# gradients: the computation the integration guide's tiled fused logits loss
+# shards over the sequence.
+# ---------------------------------------------------------------------------
+
+def lm_inputs(T, d, V, seed, ignore_every=4):
+    rng = np.random.default_rng(seed)
+    h = rng.standard_normal((T, d))
+    w = rng.standard_normal((V, d)) / np.sqrt(d)
+    labels = rng.integers(0, V, size=T)
+    labels[::ignore_every] = oracle.IGNORE_INDEX
+    return h, w, labels
+
+
+@pytest.mark.parametrize("T,d,V,s", [(7, 5, 11, 1.0), (16, 8, 33, 0.25), (3, 16, 2, 1.0 / 3)])
+def test_logits_loss_matches_torch_cross_entropy_and_autograd(T, d, V, s):
+    """torch's own cross-entropy (sum over kept tokens, ignore_index) and its
+    autograd gradients, in fp64 on the CPU."""
+    h, w, labels = lm_inputs(T, d, V, seed=T * 100 + V)
+    loss_rows, loss_sum, n_good, dh, dw = oracle.logits_loss(h, w, labels, s)
+    ht = torch.tensor(h, requires_grad=True)
+    wt = torch.tensor(w, requires_grad=True)
+    lt = torch.tensor(labels)
+    rows = torch.nn.functional.cross_entropy(ht @ wt.T, lt, ignore_index=oracle.IGNORE_INDEX,
+                                             reduction="none")
+    (s * rows.sum()).backward()
+    np.testing.assert_allclose(loss_rows, rows.detach().numpy(), rtol=1e-12, atol=1e-12)
+    assert loss_sum == pytest.approx(float(rows.sum()), rel=1e-12, abs=1e-12)
+    assert n_good == int((labels != oracle.IGNORE_INDEX).sum())
+    np.testing.assert_allclose(dh, ht.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dw, wt.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_logits_loss_zero_weights_closed_form():
+    """W = 0: every logit is 0, so a kept token's loss is ln V, dh = 0, and
+    dW_v = s * sum_i (1/V - [y_i = v]) h_i over kept tokens."""
+    T, d, V, s = 9, 4, 6, 0.5
+    h, _, labels = lm_inputs(T, d, V, seed=5)
+    w = np.zeros((V, d))
+    loss_rows, loss_sum, n_good, dh, dw = oracle.logits_loss(h, w, labels, s)
+    kept = labels != oracle.IGNORE_INDEX
+    np.testing.assert_allclose(loss_rows[kept], np.log(V), rtol=1e-14)
+    assert np.all(loss_rows[~kept] == 0.0)
+    assert loss_sum == pytest.approx(kept.sum() * np.log(V), rel=1e-14)
+    assert np.all(dh == 0.0)
+    expect = np.zeros((V, d))
+    for i in np.nonzero(kept)[0]:
+        expect += h[i] / V
+        expect[labels[i]] -= h[i]
+    np.testing.assert_allclose(dw, s * expect, rtol=1e-12, atol=1e-14)
+
+
+def test_logits_loss_two_classes_is_logistic_loss():
+    """V = 2: the loss is log(1 + e^(z_other - z_label)) (binary logistic)."""
+    T, d = 12, 6
+    h, w, _ = lm_inputs(T, d, 2, seed=8)
+    labels = np.arange(T) % 2                       # every token kept
+    loss_rows, *_ = oracle.logits_loss(h, w, labels)
+    z = h @ w.T
+    margin = z[np.arange(T), 1 - labels] - z[np.arange(T), labels]
+    np.testing.assert_allclose(loss_rows, np.log1p(np.exp(margin)), rtol=1e-12)
+
+
+def test_logits_loss_gradients_match_finite_differences():
+    T, d, V, s = 4, 3, 5, 0.7
+    h, w, labels = lm_inputs(T, d, V, seed=11)
+    _, _, _, dh, dw = oracle.logits_loss(h, w, labels, s)
+    eps = 1e-6
+
+    def loss(hh, ww):
+        return s * oracle.logits_loss(hh, ww, labels)[1]
+
+    for (i, k) in [(0, 0), (1, 2), (3, 1)]:
+        hp, hm = h.copy(), h.copy()
+        hp[i, k] += eps
+        hm[i, k] -= eps
+        assert dh[i, k] == pytest.approx((loss(hp, w) - loss(hm, w)) / (2 * eps), abs=1e-7)
+    for (v, k) in [(0, 0), (2, 1), (4, 2)]:
+        wp, wm = w.copy(), w.copy()
+        wp[v, k] += eps
+        wm[v, k] -= eps
+        assert dw[v, k] == pytest.approx((loss(h, wp) - loss(h, wm)) / (2 * eps), abs=1e-7)
+
+
+def test_logits_loss_invariants():
+    """Shifting every w_v by one vector shifts a row's logits equally: the
+    losses stay.  The rows of G sum to zero, so sum_v dW_v = 0."""
+    T, d, V = 10, 7, 13
+    h, w, labels = lm_inputs(T, d, V, seed=21)
+    rows, _, _, _, dw = oracle.logits_loss(h, w, labels)
+    shifted, *_ = oracle.logits_loss(h, w + np.random.default_rng(2).standard_normal(d), labels)
+    np.testing.assert_allclose(shifted, rows, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dw.sum(axis=0), 0.0, atol=1e-12)
+
+
+def test_logits_loss_all_ignored_and_bad_labels():
+    h, w, _ = lm_inputs(4, 3, 5, seed=1)
+    labels = np.full(4, oracle.IGNORE_INDEX)
+    rows, total, n_good, dh, dw = oracle.logits_loss(h, w, labels)
+    assert total == 0.0 and n_good == 0
+    assert not rows.any() and not dh.any() and not dw.any()
+    with pytest.raises(ValueError):
+        oracle.logits_loss(h, w, np.array([0, 1, 5, 2]))        # label == V
+    with pytest.raises(ValueError):
+        oracle.logits_loss(h, w, np.array([0, -1, 2, 2]))       # negative, not the ignore index
