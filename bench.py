@@ -63,6 +63,8 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-logits-loss", action="store_true",
+                    help="skip the language-model loss record (outside the attention step)")
     ap.add_argument("--cpu-rows", type=int, default=768,
                     help="query rows of the oracle's timed sample")
     ap.add_argument("--pack-sets", type=int, default=4,
@@ -226,6 +228,8 @@ def main():
     rotated = measure_exchanges(w, uly, torch, stream, args.pack_sets, args.pack_reps)
     breakdown["pack_rotated"] = rotated
     breakdown["attn_merge"] = measure_merge(w, uly, torch, stream, args.pack_sets, args.pack_reps)
+    if not args.no_logits_loss:
+        breakdown["logits_loss"] = measure_logits_loss(uly, torch, np, stream, args)
 
     # Roofline of the dominant unit of the step, timed with events on the
     # stream its kernels run on.  The attention backward is one entry point
@@ -316,6 +320,53 @@ def measure_fused(uly, torch, np, stream, args, rank, scale, lse, ws, tables, fw
             "attn_bwd_fused": {"ms": bwd_ms, "TFLOP/s": bwd_flop / (bwd_ms * 1e-3) / 1e12},
             "method": "ulysses_attn_fwd_fused + ulysses_attn_bwd_fused on the sequence chunks, "
                       "same inputs, steps and warmup as the main step"}
+
+
+def measure_logits_loss(uly, torch, np, stream, args):
+    """The language-model loss of one rank's tokens at the Llama-8B lm_head
+    (d = 4096, vocab = 128256) over the 128K share's 16384 tokens, 4096 rows
+    of logits at a time: three GEMMs per shard (6 T V d flop in all) and the
+    row kernel.  Outside the attention step; timed with HIP events on the
+    launch stream around each call."""
+    import synth
+    T, d, V, shard = 16384, 4096, 128256, 4096
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(99)
+    h = torch.randn((T, d), device="cuda", generator=gen).to(torch.bfloat16)
+    w = (torch.randn((V, d), device="cuda", generator=gen) * (2.0 / d ** 0.5)).to(torch.bfloat16)
+    labels = torch.tensor(synth.lm_labels(99, T, V, 10), device="cuda")
+    rows = torch.empty(T, dtype=torch.float32, device="cuda")
+    total = torch.empty(1, dtype=torch.float32, device="cuda")
+    good = torch.empty(1, dtype=torch.int64, device="cuda")
+    dh = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
+    dw = torch.empty((V, d), dtype=torch.float32, device="cuda")
+    ws = torch.empty(uly.ulysses_logits_loss_workspace_size(shard, V), dtype=torch.uint8,
+                     device="cuda")
+
+    def call():
+        uly.ulysses_logits_loss(h, w, labels, rows, total, good, dh, dw, ws, 1.0 / T, shard)
+
+    for _ in range(2):
+        call()
+    torch.cuda.synchronize()
+    reps = max(args.steps, 3)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    for i in range(reps):
+        ev[i].record(stream)
+        call()
+    ev[reps].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]))
+    flop = 6.0 * T * V * d
+    tf = flop / (ms * 1e-3) / 1e12
+    out = {"ms": ms, "TFLOP/s": tf, "frac_of_mfma_peak": tf / MFMA_BF16_PEAK_TFLOPS,
+           "flop": flop, "tokens": T, "hidden": d, "vocab": V, "shard_rows": shard,
+           "loss_sum_finite": bool(torch.isfinite(total).item()),
+           "method": f"{reps} calls back to back after 2 warm-up calls, HIP events on the "
+                     "launch stream; GEMMs by rocBLAS, the row kernel and loss sum by libulysses"}
+    del h, w, dh, dw, ws
+    torch.cuda.empty_cache()
+    return out
 
 
 def time_rotated(torch, stream, fns, reps):

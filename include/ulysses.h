@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define ULYSSES_ABI_VERSION 4
+#define ULYSSES_ABI_VERSION 5
 
 typedef enum {
   ULYSSES_OK = 0,
@@ -293,6 +293,53 @@ ulysses_status_t ulysses_attn_merge(const void* o_a, const float* lse_a, const v
                                     const float* lse_b, int64_t seqlen, int bs, int heads,
                                     int head_dim, ulysses_dtype_t dtype, void* o, float* lse,
                                     hipStream_t stream);
+
+/* Bytes of device workspace ulysses_logits_loss needs for shard_rows rows of
+ * logits over a vocabulary of `vocab` (0 for sizes it rejects). */
+size_t ulysses_logits_loss_workspace_size(int64_t shard_rows, int64_t vocab);
+
+/*
+ * Language-model loss of the rank's T tokens and its gradients, with the
+ * logits formed shard_rows rows at a time so that the [T, vocab] logits
+ * never exist in full (the integration guide's tiled fused logits loss,
+ * section on tiled loss computation: the backward runs inside the forward,
+ * shard by shard).  For token i with label y_i (labels arrive already
+ * shifted: y_i is the target of position i):
+ *   z_iv = <h_i, w_v>,  lse_i = ln sum_v exp(z_iv),
+ *   loss_rows[i] = lse_i - z_i,y_i,  or 0 when y_i == ignore_index;
+ *   loss_sum = sum_i loss_rows[i],  n_good = number of kept tokens;
+ *   G_iv = grad_scale (softmax(z_i)_v - [v == y_i]) (0 for ignored rows);
+ *   dh = G W,  dw = G^T H  (the gradients of grad_scale * loss_sum).
+ * grad_scale = 1 / (kept tokens over all ranks) gives the gradient of the
+ * guide's token-weighted loss aggregation.
+ *   h          device bf16 [T, d] (16-byte aligned)
+ *   w          device bf16 [vocab, d] (16-byte aligned)
+ *   labels     device int64 [T] (8-byte aligned)
+ *   dtype      ULYSSES_BF16 (inputs and dh; fp32 logits and accumulation;
+ *              G rounded to bf16 before the two gradient products)
+ *   loss_rows  device fp32 [T]; loss_sum device fp32 [1]; n_good device
+ *              int64 [1] (8-byte aligned)
+ *   dh         device bf16 [T, d]; dw device fp32 [vocab, d]: fully
+ *              overwritten (T == 0: dw = 0, loss_sum = 0, n_good = 0)
+ *   workspace  device memory of at least
+ *              ulysses_logits_loss_workspace_size(min(shard_rows, T), vocab)
+ *              bytes, 16-byte aligned, contents irrelevant (fp32 logits
+ *              and bf16 G of one shard)
+ * A label outside [0, vocab) other than ignore_index gives a NaN loss row
+ * and a NaN gradient row, without an out-of-bounds access.  The three
+ * products per shard are rocBLAS GEMMs (split-K atomics off, so results are
+ * reproducible) on a rocBLAS handle that the library makes per host thread
+ * and device on first use and keeps.  ERR_SHAPE for T < 0, d < 1,
+ * vocab < 1, shard_rows < 1 or a non-finite grad_scale; ERR_UNSUPPORTED for
+ * a dtype other than bf16 or a size >= 2^31; ERR_HIP also when a rocBLAS
+ * call fails.
+ */
+ulysses_status_t ulysses_logits_loss(const void* h, const void* w, const int64_t* labels,
+                                     int64_t T, int64_t d, int64_t vocab, ulysses_dtype_t dtype,
+                                     int64_t ignore_index, float grad_scale, int64_t shard_rows,
+                                     float* loss_rows, float* loss_sum, int64_t* n_good, void* dh,
+                                     float* dw, void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -276,3 +276,44 @@ def fused_bwd(lib, P=4, table=None, out_table=None, ws_bytes=None, **kw):
 ])
 def test_attn_bwd_fused_validation(lib, kw, want):
     assert fused_bwd(lib, **kw) == want
+
+
+def logits_loss_call(lib, **kw):
+    a = dict(h=FAKE, w=FAKE, labels=FAKE, T=64, d=128, V=1000, dt=uly.BF16, ignore=-100,
+             s=1.0, shard=32, rows=FAKE, total=FAKE, good=FAKE, dh=FAKE, dw=FAKE, ws=FAKE,
+             ws_bytes=None)
+    a.update(kw)
+    if a["ws_bytes"] is None:
+        a["ws_bytes"] = max(lib.ulysses_logits_loss_workspace_size(min(a["shard"], max(a["T"], 1)),
+                                                                   a["V"]), 1)
+    return lib.ulysses_logits_loss(a["h"], a["w"], a["labels"], a["T"], a["d"], a["V"], a["dt"],
+                                   a["ignore"], a["s"], a["shard"], a["rows"], a["total"],
+                                   a["good"], a["dh"], a["dw"], a["ws"], a["ws_bytes"], None)
+
+
+def test_logits_loss_workspace_size(lib):
+    # fp32 logits and bf16 G of one shard, each rounded up to 256 bytes
+    assert lib.ulysses_logits_loss_workspace_size(32, 1000) == 128000 + 64000
+    assert lib.ulysses_logits_loss_workspace_size(3, 5) == 256 + 256
+    assert lib.ulysses_logits_loss_workspace_size(0, 5) == 0
+    assert lib.ulysses_logits_loss_workspace_size(4, 1 << 31) == 0
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(w=None), uly.ERR_NULL), (dict(h=None), uly.ERR_NULL), (dict(labels=None), uly.ERR_NULL),
+    (dict(dw=None), uly.ERR_NULL), (dict(total=None), uly.ERR_NULL), (dict(dh=None), uly.ERR_NULL),
+    (dict(dt=9), uly.ERR_DTYPE),
+    (dict(dt=uly.FP32), uly.ERR_UNSUPPORTED),
+    (dict(T=-1), uly.ERR_SHAPE), (dict(d=0), uly.ERR_SHAPE), (dict(V=0), uly.ERR_SHAPE),
+    (dict(shard=0), uly.ERR_SHAPE), (dict(s=float("nan")), uly.ERR_SHAPE),
+    (dict(s=float("inf")), uly.ERR_SHAPE),
+    (dict(V=1 << 31), uly.ERR_UNSUPPORTED), (dict(d=1 << 31), uly.ERR_UNSUPPORTED),
+    (dict(h=MISALIGNED), uly.ERR_ALIGNMENT), (dict(dw=MISALIGNED), uly.ERR_ALIGNMENT),
+    (dict(labels=FAKE + 4), uly.ERR_ALIGNMENT), (dict(good=FAKE + 4), uly.ERR_ALIGNMENT),
+    (dict(rows=FAKE + 2), uly.ERR_ALIGNMENT),
+    (dict(ws=None), uly.ERR_WORKSPACE),
+    (dict(ws_bytes=32 * 1000 * 6 - 1), uly.ERR_WORKSPACE),
+    (dict(ws=FAKE + 8), uly.ERR_ALIGNMENT),
+])
+def test_logits_loss_validation(lib, kw, want):
+    assert logits_loss_call(lib, **kw) == want

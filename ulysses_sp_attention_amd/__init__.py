@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_PKG, "libulysses.so")
 OK, ERR_NULL, ERR_SHAPE, ERR_DIVISIBILITY, ERR_DTYPE, ERR_ALIGNMENT, ERR_UNSUPPORTED, \
     ERR_WORKSPACE, ERR_HIP = range(9)
 BF16, FP32 = 0, 1
-ABI_VERSION = 4   # ULYSSES_ABI_VERSION this binding is written for
+ABI_VERSION = 5   # ULYSSES_ABI_VERSION this binding is written for
 _INVALID_DTYPE = 99
 
 # Every symbol include/ulysses.h declares.
@@ -30,6 +30,7 @@ EXPORTED_SYMBOLS = (
     "ulysses_seq_to_head_batch", "ulysses_head_to_seq_batch",
     "ulysses_attn_fwd", "ulysses_attn_bwd_workspace_size", "ulysses_attn_bwd",
     "ulysses_attn_merge", "ulysses_attn_fwd_fused", "ulysses_attn_bwd_fused",
+    "ulysses_logits_loss_workspace_size", "ulysses_logits_loss",
 )
 MAX_BATCH = 4   # ULYSSES_MAX_BATCH
 
@@ -91,6 +92,11 @@ def load_library(path: str = LIB_PATH):
     lib.ulysses_attn_bwd_fused.argtypes = [vp, vp, vp, vp, vp, vp, ci, ci, i64, ci, ci, ci, ci, ci,
                                            f32, ci, vp, ci, vp, vp, vp, vp, sz, vp]
     lib.ulysses_attn_bwd_fused.restype = ci
+    lib.ulysses_logits_loss_workspace_size.argtypes = [i64, i64]
+    lib.ulysses_logits_loss_workspace_size.restype = sz
+    lib.ulysses_logits_loss.argtypes = [vp, vp, vp, i64, i64, i64, ci, i64, f32, i64, vp, vp, vp, vp,
+                                        vp, vp, sz, vp]
+    lib.ulysses_logits_loss.restype = ci
     _lib = lib
     return lib
 
@@ -276,3 +282,27 @@ def ulysses_attn_bwd_fused(q_chunks, k_chunks, v_chunks, o_chunks, lse, do_chunk
         _ptr_array(dq_chunks), _ptr_array(dk_chunks), _ptr_array(dv_chunks), _ptr(workspace),
         ws_bytes, _stream(stream))
     _check("ulysses_attn_bwd_fused", st)
+
+
+IGNORE_INDEX = -100
+
+
+def ulysses_logits_loss_workspace_size(shard_rows: int, vocab: int) -> int:
+    return int(load_library().ulysses_logits_loss_workspace_size(shard_rows, vocab))
+
+
+def ulysses_logits_loss(h, w, labels, loss_rows, loss_sum, n_good, dh, dw, workspace,
+                        grad_scale: float = 1.0, shard_rows: int = 4096,
+                        ignore_index: int = IGNORE_INDEX, stream=None) -> None:
+    """Language-model loss with the logits formed shard_rows rows at a time.
+    h: bf16 [T, d]; w: bf16 [V, d]; labels: int64 [T]; loss_rows: fp32 [T];
+    loss_sum: fp32 [1]; n_good: int64 [1]; dh: bf16 [T, d]; dw: fp32 [V, d];
+    workspace: at least ulysses_logits_loss_workspace_size(min(shard_rows, T), V) bytes."""
+    T, d = h.shape
+    V = w.shape[0]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load_library().ulysses_logits_loss(
+        _ptr(h), _ptr(w), _ptr(labels), T, d, V, _dtype_code(h), ignore_index, grad_scale,
+        shard_rows, _ptr(loss_rows), _ptr(loss_sum), _ptr(n_good), _ptr(dh), _ptr(dw),
+        _ptr(workspace), ws_bytes, _stream(stream))
+    _check("ulysses_logits_loss", st)

@@ -11,7 +11,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libulysses.so")
-SOURCES = ["api.cpp", "exchange.hip", "attn_fwd.hip", "attn_f32.hip", "attn_bwd.hip", "attn_merge.hip"]
+SOURCES = ["api.cpp", "exchange.hip", "attn_fwd.hip", "attn_f32.hip", "attn_bwd.hip", "attn_merge.hip",
+           "logits_loss.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -40,7 +41,10 @@ def build_lib(jobs: int = 8) -> str:
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB_PATH + ".tmp"
-    subprocess.run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp], check=True)
+    # rocBLAS (plain GEMMs of the language-model loss): in a process that has
+    # imported torch this resolves, by soname, to the copy torch loaded.
+    subprocess.run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-L/opt/rocm/lib",
+                    "-lrocblas", "-o", tmp], check=True)
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 

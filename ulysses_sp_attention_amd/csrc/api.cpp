@@ -2,6 +2,8 @@
 // Every check runs before the first HIP call, so a rejected call launches
 // nothing and leaves every output untouched.  Contracts are stated in
 // include/ulysses.h.
+#include <cmath>
+
 #include "ulysses.h"
 
 #include <math.h>
@@ -367,6 +369,59 @@ ulysses_status_t ulysses_attn_bwd_fused(
       s, table(q_chunks, hq, q0), table(k_chunks, hkv, kv0), table(v_chunks, hkv, kv0),
       table(o_chunks, hq, q0), lse, table(do_chunks, hq, q0), out_table(dq_chunks, hq, q0),
       out_table(dk_chunks, hkv, kv0), out_table(dv_chunks, hkv, kv0), workspace, stream));
+}
+
+size_t ulysses_logits_loss_workspace_size(int64_t shard_rows, int64_t vocab) {
+  if (shard_rows < 1 || vocab < 1 || shard_rows >= (int64_t(1) << 31) ||
+      vocab >= (int64_t(1) << 31))
+    return 0;
+  return ulysses::logits_loss_workspace_bytes(shard_rows, vocab);
+}
+
+ulysses_status_t ulysses_logits_loss(const void* h, const void* w, const int64_t* labels,
+                                     int64_t T, int64_t d, int64_t vocab, ulysses_dtype_t dtype,
+                                     int64_t ignore_index, float grad_scale, int64_t shard_rows,
+                                     float* loss_rows, float* loss_sum, int64_t* n_good, void* dh,
+                                     float* dw, void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream) {
+  if (w == nullptr || loss_sum == nullptr || n_good == nullptr || dw == nullptr)
+    return ULYSSES_ERR_NULL;
+  if (T > 0 && (h == nullptr || labels == nullptr || loss_rows == nullptr || dh == nullptr))
+    return ULYSSES_ERR_NULL;
+  if (elem_size(dtype) == 0) return ULYSSES_ERR_DTYPE;
+  if (T < 0 || d < 1 || vocab < 1 || shard_rows < 1 || !std::isfinite(grad_scale))
+    return ULYSSES_ERR_SHAPE;
+  if (dtype != ULYSSES_BF16) return ULYSSES_ERR_UNSUPPORTED;
+  // The library GEMMs count rows, columns and leading dimensions in 32 bits.
+  if (T >= (int64_t(1) << 31) || d >= (int64_t(1) << 31) || vocab >= (int64_t(1) << 31) ||
+      shard_rows >= (int64_t(1) << 31))
+    return ULYSSES_ERR_UNSUPPORTED;
+  if (!aligned16(h) || !aligned16(w) || !aligned16(dh) || !aligned16(dw) ||
+      reinterpret_cast<uintptr_t>(labels) % 8 != 0 || !aligned4(loss_rows) || !aligned4(loss_sum) ||
+      reinterpret_cast<uintptr_t>(n_good) % 8 != 0)
+    return ULYSSES_ERR_ALIGNMENT;
+  if (T > 0) {
+    const size_t need = ulysses::logits_loss_workspace_bytes(shard_rows < T ? shard_rows : T, vocab);
+    if (workspace == nullptr || workspace_bytes < need) return ULYSSES_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return ULYSSES_ERR_ALIGNMENT;
+  }
+  ulysses::LogitsLossArgs a{};
+  a.h = h;
+  a.w = w;
+  a.labels = labels;
+  a.T = T;
+  a.d = d;
+  a.V = vocab;
+  a.ignore_index = ignore_index;
+  a.shard_rows = shard_rows < T ? shard_rows : (T > 0 ? T : 1);
+  a.grad_scale = grad_scale;
+  a.loss_rows = loss_rows;
+  a.loss_sum = loss_sum;
+  a.n_good = n_good;
+  a.dh = dh;
+  a.dw = dw;
+  a.workspace = workspace;
+  return from_hip(ulysses::launch_logits_loss(a, stream));
 }
 
 }  // extern "C"

@@ -121,4 +121,27 @@ hipError_t launch_attn_merge(bool bf16, const void* o_a, const float* lse_a, con
                              const float* lse_b, int64_t N, int bs, int heads, int hd, void* o,
                              float* lse, hipStream_t stream);
 
+// Language-model loss (lm_head GEMM, cross-entropy over the vocabulary, the
+// gradients of grad_scale * loss_sum) over T tokens, shard_rows rows of
+// logits at a time.  h [T, d] and w [V, d] bf16; labels int64 [T];
+// loss_rows fp32 [T]; loss_sum fp32 [1]; n_good int64 [1]; dh bf16 [T, d];
+// dw fp32 [V, d]; workspace of logits_loss_workspace_bytes(shard_rows, V).
+struct LogitsLossArgs {
+  const void* h;
+  const void* w;
+  const int64_t* labels;
+  int64_t T, d, V, ignore_index, shard_rows;
+  float grad_scale;
+  float* loss_rows;
+  float* loss_sum;
+  int64_t* n_good;
+  void* dh;
+  float* dw;
+  void* workspace;
+};
+size_t logits_loss_workspace_bytes(int64_t shard_rows, int64_t V);
+// hipErrorUnknown: a rocBLAS call failed; hipErrorNotInitialized: no rocBLAS
+// handle could be made.
+hipError_t launch_logits_loss(const LogitsLossArgs& a, hipStream_t stream);
+
 }  // namespace ulysses
