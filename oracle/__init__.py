@@ -48,6 +48,8 @@ def _load():
     lib.oracle_logits_loss.argtypes = [vp, vp, vp, i64, i64, i64, i64, dbl, vp, vp, vp, vp, vp, vp,
                                        vp, vp]
     lib.oracle_logits_loss.restype = ci
+    lib.oracle_swiglu_mlp.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64] + [vp] * 10
+    lib.oracle_swiglu_mlp.restype = ci
     lib.oracle_attn_merge.restype = ci
     lib.oracle_seq_to_head.argtypes = [vp, ci, ci, i64, ci, ci, ci, ci, vp]
     lib.oracle_seq_to_head.restype = ci
@@ -227,3 +229,36 @@ def logits_loss(h, w, labels, grad_scale: float = 1.0, ignore_index: int = IGNOR
     if magnitude:
         return out + (dict(zip(("zmag", "dh", "dw"), mags)),)
     return out
+
+
+def swiglu_mlp(x, wg, wu, wd, dy=None, magnitude: bool = False):
+    """SwiGLU MLP y = (silu(x Wg^T) * (x Wu^T)) Wd^T and, with dy, its
+    gradients (see oracle.c).  x [T, d], wg and wu [I, d], wd [d, I].
+    Returns y, or (y, dx, dwg, dwu, dwd) with dy; with magnitude=True a dict
+    of rounding-bound magnitudes is appended."""
+    x, wg, wu, wd = _f64(x), _f64(wg), _f64(wu), _f64(wd)
+    T, d = x.shape
+    I = wg.shape[0]
+    if wg.shape != (I, d) or wu.shape != (I, d) or wd.shape != (d, I):
+        raise ValueError("swiglu_mlp: shape mismatch")
+    bwd = dy is not None
+    if bwd:
+        dy = _f64(dy)
+        if dy.shape != (T, d):
+            raise ValueError("swiglu_mlp: dy shape")
+    y = np.empty((T, d))
+    grads = [np.empty((T, d)), np.empty((I, d)), np.empty((I, d)), np.empty((d, I))] if bwd \
+        else [None] * 4
+    names = ("y", "dx", "dwg", "dwu", "dwd")
+    shapes = ((T, d), (T, d), (I, d), (I, d), (d, I))
+    mags = [np.empty(sh) if magnitude and (bwd or n == "y") else None
+            for n, sh in zip(names, shapes)]
+    ptr = lambda a: None if a is None else a.ctypes.data
+    rc = _load().oracle_swiglu_mlp(ptr(x), ptr(wg), ptr(wu), ptr(wd), ptr(dy), T, d, I, ptr(y),
+                                   *[ptr(g) for g in grads], *[ptr(m) for m in mags])
+    if rc:
+        raise ValueError(f"oracle_swiglu_mlp: bad arguments ({rc})")
+    out = (y,) + (tuple(grads) if bwd else ())
+    if magnitude:
+        out = out + ({n: m for n, m in zip(names, mags) if m is not None},)
+    return out if (bwd or magnitude) else y

@@ -564,3 +564,114 @@ int oracle_logits_loss(const double* h, const double* w, const int64_t* labels, 
   free(G);
   return 0;
 }
+
+/* ----------------------------------------------------------------------
+ * Sequence-tiled SwiGLU MLP (the integration guide's TiledMLP, section on
+ * the ALST memory tricks): the MLP of a Llama-style block,
+ *   g = x Wg^T,  u = x Wu^T   ([T, I]; Wg, Wu are [I, d])
+ *   a = silu(g) * u,  silu(g) = g / (1 + e^-g)
+ *   y = a Wd^T                ([T, d]; Wd is [d, I])
+ * which TiledMLP runs a shard of tokens at a time to bound the [T, I]
+ * intermediates; rows are independent, so the result is the whole-sequence
+ * MLP and the oracle states that.  Backward, for the upstream gradient dy:
+ *   da = dy Wd,  dWd = dy^T a
+ *   dg = da * u * silu'(g),  silu'(g) = s (1 + g (1 - s)),  s = 1/(1+e^-g)
+ *   du = da * silu(g)
+ *   dx = dg Wg + du Wu,  dWg = dg^T x,  dWu = du^T x.
+ * dy == NULL: forward only (dx, dwg, dwu, dwd unused).  Optional magnitude
+ * outputs (NULL to skip) bound the rounding of a low-precision
+ * implementation that rounds a, dg and du before the products that use them:
+ *   y_mag = |a| |Wd|^T, dx_mag = |dg| |Wg| + |du| |Wu|, dwg_mag = |dg|^T |x|,
+ *   dwu_mag = |du|^T |x|, dwd_mag = |dy|^T |a|.
+ * All matrices row-major.
+ * ---------------------------------------------------------------------- */
+static double sigmoid(double g) { return 1.0 / (1.0 + exp(-g)); }
+
+int oracle_swiglu_mlp(const double* x, const double* wg, const double* wu, const double* wd,
+                      const double* dy, int64_t T, int64_t d, int64_t I, double* y, double* dx,
+                      double* dwg, double* dwu, double* dwd, double* y_mag, double* dx_mag,
+                      double* dwg_mag, double* dwu_mag, double* dwd_mag) {
+  if (T < 0 || d < 1 || I < 1 || !x || !wg || !wu || !wd || !y) return 1;
+  if (dy && (!dx || !dwg || !dwu || !dwd)) return 1;
+  const size_t TI = (size_t)(T > 0 ? T : 1) * (size_t)I;
+  double* a = (double*)malloc(sizeof(double) * TI);
+  double* dg = (double*)malloc(sizeof(double) * TI);
+  double* du = (double*)malloc(sizeof(double) * TI);
+  if (!a || !dg || !du) {
+    free(a);
+    free(dg);
+    free(du);
+    return 3;
+  }
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < T; ++i) {
+    for (int64_t j = 0; j < I; ++j) {
+      double g = 0.0, u = 0.0;
+      for (int64_t k = 0; k < d; ++k) {
+        g += x[i * d + k] * wg[j * d + k];
+        u += x[i * d + k] * wu[j * d + k];
+      }
+      const double s = sigmoid(g);
+      a[(size_t)i * I + j] = g * s * u;
+      if (dy) {
+        double da = 0.0;
+        for (int64_t k = 0; k < d; ++k) da += dy[i * d + k] * wd[k * I + j];
+        dg[(size_t)i * I + j] = da * u * s * (1.0 + g * (1.0 - s));
+        du[(size_t)i * I + j] = da * g * s;
+      }
+    }
+    for (int64_t k = 0; k < d; ++k) {
+      double acc = 0.0, mag = 0.0;
+      for (int64_t j = 0; j < I; ++j) {
+        acc += a[(size_t)i * I + j] * wd[k * I + j];
+        mag += fabs(a[(size_t)i * I + j] * wd[k * I + j]);
+      }
+      y[i * d + k] = acc;
+      if (y_mag) y_mag[i * d + k] = mag;
+    }
+    if (dy)
+      for (int64_t k = 0; k < d; ++k) {
+        double acc = 0.0, mag = 0.0;
+        for (int64_t j = 0; j < I; ++j) {
+          const double p = dg[(size_t)i * I + j] * wg[j * d + k];
+          const double q = du[(size_t)i * I + j] * wu[j * d + k];
+          acc += p + q;
+          mag += fabs(p) + fabs(q);
+        }
+        dx[i * d + k] = acc;
+        if (dx_mag) dx_mag[i * d + k] = mag;
+      }
+  }
+  if (dy) {
+#pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < I; ++j)
+      for (int64_t k = 0; k < d; ++k) {
+        double sg = 0.0, su = 0.0, mg = 0.0, mu = 0.0;
+        for (int64_t i = 0; i < T; ++i) {
+          sg += dg[(size_t)i * I + j] * x[i * d + k];
+          su += du[(size_t)i * I + j] * x[i * d + k];
+          mg += fabs(dg[(size_t)i * I + j] * x[i * d + k]);
+          mu += fabs(du[(size_t)i * I + j] * x[i * d + k]);
+        }
+        dwg[j * d + k] = sg;
+        dwu[j * d + k] = su;
+        if (dwg_mag) dwg_mag[j * d + k] = mg;
+        if (dwu_mag) dwu_mag[j * d + k] = mu;
+      }
+#pragma omp parallel for schedule(static)
+    for (int64_t k = 0; k < d; ++k)
+      for (int64_t j = 0; j < I; ++j) {
+        double acc = 0.0, mag = 0.0;
+        for (int64_t i = 0; i < T; ++i) {
+          acc += dy[i * d + k] * a[(size_t)i * I + j];
+          mag += fabs(dy[i * d + k] * a[(size_t)i * I + j]);
+        }
+        dwd[k * I + j] = acc;
+        if (dwd_mag) dwd_mag[k * I + j] = mag;
+      }
+  }
+  free(a);
+  free(dg);
+  free(du);
+  return 0;
+}

@@ -635,3 +635,61 @@ def test_logits_loss_all_ignored_and_bad_labels():
         oracle.logits_loss(h, w, np.array([0, 1, 5, 2]))        # label == V
     with pytest.raises(ValueError):
         oracle.logits_loss(h, w, np.array([0, -1, 2, 2]))       # negative, not the ignore index
+
+
+# ---------------------------------------------------------------------------
+# Sequence-tiled SwiGLU MLP (TiledMLP): y = (silu(x Wg^T) * (x Wu^T)) Wd^T.
+# ---------------------------------------------------------------------------
+
+def mlp_inputs(T, d, I, seed):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((T, d)), rng.standard_normal((I, d)) / np.sqrt(d),
+            rng.standard_normal((I, d)) / np.sqrt(d), rng.standard_normal((d, I)) / np.sqrt(I),
+            rng.standard_normal((T, d)))
+
+
+@pytest.mark.parametrize("T,d,I", [(5, 4, 7), (12, 8, 20), (1, 16, 3)])
+def test_swiglu_mlp_matches_torch_autograd(T, d, I):
+    x, wg, wu, wd, dy = mlp_inputs(T, d, I, seed=T + d + I)
+    y, dx, dwg, dwu, dwd = oracle.swiglu_mlp(x, wg, wu, wd, dy)
+    t = [torch.tensor(a, requires_grad=True) for a in (x, wg, wu, wd)]
+    yt = (torch.nn.functional.silu(t[0] @ t[1].T) * (t[0] @ t[2].T)) @ t[3].T
+    yt.backward(torch.tensor(dy))
+    np.testing.assert_allclose(y, yt.detach().numpy(), rtol=1e-12, atol=1e-13)
+    for mine, ref in zip((dx, dwg, dwu, dwd), t):
+        np.testing.assert_allclose(mine, ref.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_swiglu_mlp_zero_gate_closed_form():
+    """Wg = 0: g = 0, silu(0) = 0 and silu'(0) = 1/2, so y = 0, dx = 0,
+    dWu = 0, dWd = 0 and dWg = (1/2 (dy Wd) * u)^T x with u = x Wu^T."""
+    x, _, wu, wd, dy = mlp_inputs(6, 5, 4, seed=3)
+    wg = np.zeros_like(wu)
+    y, dx, dwg, dwu, dwd = oracle.swiglu_mlp(x, wg, wu, wd, dy)
+    assert not y.any() and not dx.any() and not dwu.any() and not dwd.any()
+    u = x @ wu.T
+    np.testing.assert_allclose(dwg, (0.5 * (dy @ wd) * u).T @ x, rtol=1e-12, atol=1e-14)
+
+
+def test_swiglu_mlp_gradients_match_finite_differences():
+    x, wg, wu, wd, dy = mlp_inputs(3, 4, 5, seed=9)
+    _, dx, dwg, dwu, dwd = oracle.swiglu_mlp(x, wg, wu, wd, dy)
+    eps = 1e-6
+    args = [x, wg, wu, wd]
+
+    def f(k, idx, delta):
+        a = [m.copy() for m in args]
+        a[k][idx] += delta
+        return float((oracle.swiglu_mlp(*a) * dy).sum())
+
+    for k, grad, idx in [(0, dx, (1, 2)), (1, dwg, (3, 0)), (2, dwu, (4, 3)), (3, dwd, (2, 1))]:
+        fd = (f(k, idx, eps) - f(k, idx, -eps)) / (2 * eps)
+        assert grad[idx] == pytest.approx(fd, abs=1e-7)
+
+
+def test_swiglu_mlp_rows_are_independent():
+    """The property TiledMLP relies on: a shard of rows gives the same rows
+    as the whole sequence."""
+    x, wg, wu, wd, dy = mlp_inputs(10, 6, 9, seed=4)
+    y = oracle.swiglu_mlp(x, wg, wu, wd)
+    np.testing.assert_array_equal(oracle.swiglu_mlp(x[3:7], wg, wu, wd), y[3:7])
