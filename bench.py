@@ -64,7 +64,8 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-logits-loss", action="store_true",
-                    help="skip the language-model loss record (outside the attention step)")
+                    help="skip the language-model loss and tiled MLP records (outside the "
+                         "attention step)")
     ap.add_argument("--cpu-rows", type=int, default=768,
                     help="query rows of the oracle's timed sample")
     ap.add_argument("--pack-sets", type=int, default=4,
@@ -230,6 +231,7 @@ def main():
     breakdown["attn_merge"] = measure_merge(w, uly, torch, stream, args.pack_sets, args.pack_reps)
     if not args.no_logits_loss:
         breakdown["logits_loss"] = measure_logits_loss(uly, torch, np, stream, args)
+        breakdown["tiled_mlp"] = measure_tiled_mlp(uly, torch, np, stream, args)
 
     # Roofline of the dominant unit of the step, timed with events on the
     # stream its kernels run on.  The attention backward is one entry point
@@ -365,6 +367,59 @@ def measure_logits_loss(uly, torch, np, stream, args):
            "method": f"{reps} calls back to back after 2 warm-up calls, HIP events on the "
                      "launch stream; GEMMs by rocBLAS, the row kernel and loss sum by libulysses"}
     del h, w, dh, dw, ws
+    torch.cuda.empty_cache()
+    return out
+
+
+def measure_tiled_mlp(uly, torch, np, stream, args):
+    """The sequence-tiled SwiGLU MLP at the Llama-8B block shape (d = 4096,
+    inter = 14336) over the 128K share's 16384 tokens in ceil(T / d) = 4
+    shards: forward and backward timed separately with HIP events.
+    Algorithmic work: forward 3 products (6 T d I flop), backward 6 products
+    (12 T d I); the backward also recomputes g and u (4 T d I more)."""
+    T, d, inter = 16384, 4096, 14336
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(7)
+    bf = torch.bfloat16
+    x = torch.randn((T, d), device="cuda", generator=gen).to(bf)
+    dy = torch.randn((T, d), device="cuda", generator=gen).to(bf)
+    wg = (torch.randn((inter, d), device="cuda", generator=gen) / d ** 0.5).to(bf)
+    wu = (torch.randn((inter, d), device="cuda", generator=gen) / d ** 0.5).to(bf)
+    wd = (torch.randn((d, inter), device="cuda", generator=gen) / inter ** 0.5).to(bf)
+    y = torch.empty((T, d), dtype=bf, device="cuda")
+    dx = torch.empty((T, d), dtype=bf, device="cuda")
+    dwg = torch.empty((inter, d), device="cuda")
+    dwu = torch.empty((inter, d), device="cuda")
+    dwd = torch.empty((d, inter), device="cuda")
+    ws = torch.empty(uly.ulysses_tiled_mlp_workspace_size(d, d, inter, True), dtype=torch.uint8,
+                     device="cuda")
+
+    def fwd():
+        uly.ulysses_tiled_mlp_fwd(x, wg, wu, wd, y, ws, d)
+
+    def bwd():
+        uly.ulysses_tiled_mlp_bwd(x, wg, wu, wd, dy, dx, dwg, dwu, dwd, ws, d)
+
+    out = {"tokens": T, "hidden": d, "inter": inter, "shard_rows": d}
+    reps = max(args.steps, 3)
+    for name, fn, flop, executed in (("fwd", fwd, 6.0 * T * d * inter, 6.0 * T * d * inter),
+                                     ("bwd", bwd, 12.0 * T * d * inter, 16.0 * T * d * inter)):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        for i in range(reps):
+            ev[i].record(stream)
+            fn()
+        ev[reps].record(stream)
+        torch.cuda.synchronize()
+        ms = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]))
+        tf = flop / (ms * 1e-3) / 1e12
+        out[name] = {"ms": ms, "TFLOP/s": tf, "frac_of_mfma_peak": tf / MFMA_BF16_PEAK_TFLOPS,
+                     "executed_TFLOP/s": executed / (ms * 1e-3) / 1e12}
+    out["method"] = (f"{reps} calls each back to back after 2 warm-up calls, HIP events on the "
+                     "launch stream; GEMMs by rocBLAS, the SwiGLU row kernels by libulysses")
+    del x, dy, wg, wu, wd, y, dx, dwg, dwu, dwd, ws
     torch.cuda.empty_cache()
     return out
 

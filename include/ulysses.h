@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define ULYSSES_ABI_VERSION 5
+#define ULYSSES_ABI_VERSION 6
 
 typedef enum {
   ULYSSES_OK = 0,
@@ -340,6 +340,49 @@ ulysses_status_t ulysses_logits_loss(const void* h, const void* w, const int64_t
                                      float* loss_rows, float* loss_sum, int64_t* n_good, void* dh,
                                      float* dw, void* workspace, size_t workspace_bytes,
                                      hipStream_t stream);
+
+/* Bytes of device workspace the tiled MLP needs for shard_rows rows
+ * (backward != 0: ulysses_tiled_mlp_bwd, else ulysses_tiled_mlp_fwd); 0 for
+ * sizes it rejects. */
+size_t ulysses_tiled_mlp_workspace_size(int64_t shard_rows, int64_t d, int64_t inter,
+                                        int backward);
+
+/*
+ * Sequence-tiled SwiGLU MLP of a Llama-style block (the integration guide's
+ * TiledMLP, section on the ALST memory tricks), shard_rows token rows at a
+ * time so that the [T, inter] intermediates exist for one shard only (the
+ * guide picks ceil(T / d) shards, i.e. shard_rows = d):
+ *   g = x Wg^T,  u = x Wu^T,  a = silu(g) * u,  y = a Wd^T.
+ * The backward recomputes each shard's g and u (nothing is kept from the
+ * forward) and, for the upstream gradient dy, writes
+ *   da = dy Wd,  dg = da * u * silu'(g),  du = da * silu(g),
+ *   dx = dg Wg + du Wu,  dWg = dg^T x,  dWu = du^T x,  dWd = dy^T a.
+ *   x, y, dy, dx  device bf16 [T, d]
+ *   wg, wu        device bf16 [inter, d] (gate_proj, up_proj weights)
+ *   wd            device bf16 [d, inter] (down_proj weight)
+ *   dwg, dwu      device fp32 [inter, d]; dwd device fp32 [d, inter]: fully
+ *                 overwritten (T == 0: zero)
+ *   workspace     ulysses_tiled_mlp_workspace_size(min(shard_rows, T), d,
+ *                 inter, backward) bytes, 16-byte aligned, contents
+ *                 irrelevant
+ * Every pointer 16-byte aligned.  g, u and da are kept in fp32; a, dg and du
+ * are rounded to bf16 as operands of the following products; dx is summed
+ * in fp32 and rounded once.  The products are rocBLAS GEMMs as for
+ * ulysses_logits_loss.  ERR_SHAPE for T < 0, d or inter < 1 or not a
+ * multiple of 8, shard_rows < 1; ERR_UNSUPPORTED for a dtype other than bf16
+ * or a size >= 2^31.
+ */
+ulysses_status_t ulysses_tiled_mlp_fwd(const void* x, const void* wg, const void* wu,
+                                       const void* wd, int64_t T, int64_t d, int64_t inter,
+                                       ulysses_dtype_t dtype, int64_t shard_rows, void* y,
+                                       void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream);
+ulysses_status_t ulysses_tiled_mlp_bwd(const void* x, const void* wg, const void* wu,
+                                       const void* wd, const void* dy, int64_t T, int64_t d,
+                                       int64_t inter, ulysses_dtype_t dtype, int64_t shard_rows,
+                                       void* dx, float* dwg, float* dwu, float* dwd,
+                                       void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream);
 
 #ifdef __cplusplus
 }

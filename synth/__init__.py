@@ -27,6 +27,8 @@ STREAM_Q, STREAM_K, STREAM_V, STREAM_DO, STREAM_DOCS = 1, 2, 3, 4, 5
 # Streams of the language-model loss inputs: hidden states, lm_head weight,
 # labels and the choice of ignored tokens.
 STREAM_HIDDEN, STREAM_LM_HEAD, STREAM_LABELS, STREAM_IGNORE = 6, 7, 8, 9
+# Streams of the MLP weights (gate_proj, up_proj, down_proj).
+STREAM_MLP_GATE, STREAM_MLP_UP, STREAM_MLP_DOWN = 10, 11, 12
 IGNORE_INDEX = -100
 
 

@@ -317,3 +317,54 @@ def test_logits_loss_workspace_size(lib):
 ])
 def test_logits_loss_validation(lib, kw, want):
     assert logits_loss_call(lib, **kw) == want
+
+
+def mlp_call(lib, backward, **kw):
+    a = dict(x=FAKE, wg=FAKE, wu=FAKE, wd=FAKE, dy=FAKE, T=64, d=128, I=256, dt=uly.BF16,
+             shard=32, y=FAKE, dx=FAKE, dwg=FAKE, dwu=FAKE, dwd=FAKE, ws=FAKE, ws_bytes=None)
+    a.update(kw)
+    if a["ws_bytes"] is None:
+        a["ws_bytes"] = max(lib.ulysses_tiled_mlp_workspace_size(
+            min(a["shard"], max(a["T"], 1)), max(a["d"], 1), max(a["I"], 1), int(backward)), 1)
+    if backward:
+        return lib.ulysses_tiled_mlp_bwd(a["x"], a["wg"], a["wu"], a["wd"], a["dy"], a["T"], a["d"],
+                                         a["I"], a["dt"], a["shard"], a["dx"], a["dwg"], a["dwu"],
+                                         a["dwd"], a["ws"], a["ws_bytes"], None)
+    return lib.ulysses_tiled_mlp_fwd(a["x"], a["wg"], a["wu"], a["wd"], a["T"], a["d"], a["I"],
+                                     a["dt"], a["shard"], a["y"], a["ws"], a["ws_bytes"], None)
+
+
+def test_tiled_mlp_workspace_size(lib):
+    S, d, inter = 32, 128, 256
+    f, h = S * inter * 4, S * inter * 2      # multiples of 256 here
+    assert lib.ulysses_tiled_mlp_workspace_size(S, d, inter, 0) == 2 * f + h
+    assert lib.ulysses_tiled_mlp_workspace_size(S, d, inter, 1) == 3 * f + 3 * h + S * d * 4
+    assert lib.ulysses_tiled_mlp_workspace_size(0, d, inter, 1) == 0
+
+
+@pytest.mark.parametrize("backward", [False, True])
+@pytest.mark.parametrize("kw,want", [
+    (dict(wg=None), uly.ERR_NULL), (dict(wd=None), uly.ERR_NULL), (dict(x=None), uly.ERR_NULL),
+    (dict(dt=9), uly.ERR_DTYPE), (dict(dt=uly.FP32), uly.ERR_UNSUPPORTED),
+    (dict(T=-1), uly.ERR_SHAPE), (dict(d=0), uly.ERR_SHAPE), (dict(I=0), uly.ERR_SHAPE),
+    (dict(d=100), uly.ERR_SHAPE), (dict(I=36), uly.ERR_SHAPE),    # not multiples of 8
+    (dict(shard=0), uly.ERR_SHAPE),
+    (dict(I=1 << 31), uly.ERR_UNSUPPORTED),
+    (dict(x=MISALIGNED), uly.ERR_ALIGNMENT), (dict(wu=MISALIGNED), uly.ERR_ALIGNMENT),
+    (dict(ws=None), uly.ERR_WORKSPACE), (dict(ws_bytes=1), uly.ERR_WORKSPACE),
+    (dict(ws=FAKE + 8), uly.ERR_ALIGNMENT),
+])
+def test_tiled_mlp_validation(lib, backward, kw, want):
+    assert mlp_call(lib, backward, **kw) == want
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(dy=None), uly.ERR_NULL), (dict(dx=None), uly.ERR_NULL), (dict(dwd=None), uly.ERR_NULL),
+    (dict(dwg=MISALIGNED), uly.ERR_ALIGNMENT), (dict(dy=MISALIGNED), uly.ERR_ALIGNMENT),
+])
+def test_tiled_mlp_bwd_validation(lib, kw, want):
+    assert mlp_call(lib, True, **kw) == want
+
+
+def test_tiled_mlp_fwd_empty_is_a_no_op(lib):
+    assert mlp_call(lib, False, T=0, x=None, y=None, ws=None) == uly.OK

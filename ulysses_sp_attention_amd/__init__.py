@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_PKG, "libulysses.so")
 OK, ERR_NULL, ERR_SHAPE, ERR_DIVISIBILITY, ERR_DTYPE, ERR_ALIGNMENT, ERR_UNSUPPORTED, \
     ERR_WORKSPACE, ERR_HIP = range(9)
 BF16, FP32 = 0, 1
-ABI_VERSION = 5   # ULYSSES_ABI_VERSION this binding is written for
+ABI_VERSION = 6   # ULYSSES_ABI_VERSION this binding is written for
 _INVALID_DTYPE = 99
 
 # Every symbol include/ulysses.h declares.
@@ -31,6 +31,7 @@ EXPORTED_SYMBOLS = (
     "ulysses_attn_fwd", "ulysses_attn_bwd_workspace_size", "ulysses_attn_bwd",
     "ulysses_attn_merge", "ulysses_attn_fwd_fused", "ulysses_attn_bwd_fused",
     "ulysses_logits_loss_workspace_size", "ulysses_logits_loss",
+    "ulysses_tiled_mlp_workspace_size", "ulysses_tiled_mlp_fwd", "ulysses_tiled_mlp_bwd",
 )
 MAX_BATCH = 4   # ULYSSES_MAX_BATCH
 
@@ -97,6 +98,13 @@ def load_library(path: str = LIB_PATH):
     lib.ulysses_logits_loss.argtypes = [vp, vp, vp, i64, i64, i64, ci, i64, f32, i64, vp, vp, vp, vp,
                                         vp, vp, sz, vp]
     lib.ulysses_logits_loss.restype = ci
+    lib.ulysses_tiled_mlp_workspace_size.argtypes = [i64, i64, i64, ci]
+    lib.ulysses_tiled_mlp_workspace_size.restype = sz
+    lib.ulysses_tiled_mlp_fwd.argtypes = [vp, vp, vp, vp, i64, i64, i64, ci, i64, vp, vp, sz, vp]
+    lib.ulysses_tiled_mlp_fwd.restype = ci
+    lib.ulysses_tiled_mlp_bwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ci, i64, vp, vp, vp,
+                                          vp, vp, sz, vp]
+    lib.ulysses_tiled_mlp_bwd.restype = ci
     _lib = lib
     return lib
 
@@ -306,3 +314,37 @@ def ulysses_logits_loss(h, w, labels, loss_rows, loss_sum, n_good, dh, dw, works
         shard_rows, _ptr(loss_rows), _ptr(loss_sum), _ptr(n_good), _ptr(dh), _ptr(dw),
         _ptr(workspace), ws_bytes, _stream(stream))
     _check("ulysses_logits_loss", st)
+
+
+def ulysses_tiled_mlp_workspace_size(shard_rows: int, d: int, inter: int, backward: bool) -> int:
+    return int(load_library().ulysses_tiled_mlp_workspace_size(shard_rows, d, inter, int(backward)))
+
+
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def ulysses_tiled_mlp_fwd(x, wg, wu, wd, y, workspace, shard_rows=None, stream=None) -> None:
+    """y = (silu(x Wg^T) * (x Wu^T)) Wd^T, shard_rows rows at a time (default
+    d, the guide's ceil(T / d) shards).  x, y: bf16 [T, d]; wg, wu: [I, d];
+    wd: [d, I]."""
+    T, d = x.shape
+    inter = wg.shape[0]
+    st = load_library().ulysses_tiled_mlp_fwd(
+        _ptr(x), _ptr(wg), _ptr(wu), _ptr(wd), T, d, inter, _dtype_code(x),
+        d if shard_rows is None else shard_rows, _ptr(y), _ptr(workspace), _nbytes(workspace),
+        _stream(stream))
+    _check("ulysses_tiled_mlp_fwd", st)
+
+
+def ulysses_tiled_mlp_bwd(x, wg, wu, wd, dy, dx, dwg, dwu, dwd, workspace, shard_rows=None,
+                          stream=None) -> None:
+    """Gradients of ulysses_tiled_mlp_fwd for dy (bf16 [T, d]): dx bf16 [T, d];
+    dwg, dwu fp32 [I, d]; dwd fp32 [d, I]."""
+    T, d = x.shape
+    inter = wg.shape[0]
+    st = load_library().ulysses_tiled_mlp_bwd(
+        _ptr(x), _ptr(wg), _ptr(wu), _ptr(wd), _ptr(dy), T, d, inter, _dtype_code(x),
+        d if shard_rows is None else shard_rows, _ptr(dx), _ptr(dwg), _ptr(dwu), _ptr(dwd),
+        _ptr(workspace), _nbytes(workspace), _stream(stream))
+    _check("ulysses_tiled_mlp_bwd", st)

@@ -424,4 +424,92 @@ ulysses_status_t ulysses_logits_loss(const void* h, const void* w, const int64_t
   return from_hip(ulysses::launch_logits_loss(a, stream));
 }
 
+size_t ulysses_tiled_mlp_workspace_size(int64_t shard_rows, int64_t d, int64_t inter,
+                                        int backward) {
+  if (shard_rows < 1 || d < 1 || inter < 1 || shard_rows >= (int64_t(1) << 31) ||
+      d >= (int64_t(1) << 31) || inter >= (int64_t(1) << 31))
+    return 0;
+  return ulysses::tiled_mlp_workspace_bytes(shard_rows, d, inter, backward != 0);
+}
+
+namespace {
+
+ulysses_status_t tiled_mlp(ulysses::TiledMlpArgs& a, ulysses_dtype_t dtype, size_t ws_bytes,
+                           hipStream_t stream) {
+  if (a.wg == nullptr || a.wu == nullptr || a.wd == nullptr) return ULYSSES_ERR_NULL;
+  if (a.T > 0 && (a.x == nullptr || (a.backward ? (a.dy == nullptr || a.dx == nullptr)
+                                                : a.y == nullptr)))
+    return ULYSSES_ERR_NULL;
+  if (a.backward && (a.dwg == nullptr || a.dwu == nullptr || a.dwd == nullptr))
+    return ULYSSES_ERR_NULL;
+  if (elem_size(dtype) == 0) return ULYSSES_ERR_DTYPE;
+  if (a.T < 0 || a.d < 1 || a.I < 1 || a.shard_rows < 1) return ULYSSES_ERR_SHAPE;
+  // 16-byte rows for the vector loads and stores of the row kernels
+  if (a.d % 8 != 0 || a.I % 8 != 0) return ULYSSES_ERR_SHAPE;
+  if (dtype != ULYSSES_BF16) return ULYSSES_ERR_UNSUPPORTED;
+  if (a.T >= (int64_t(1) << 31) || a.d >= (int64_t(1) << 31) || a.I >= (int64_t(1) << 31) ||
+      a.shard_rows >= (int64_t(1) << 31))
+    return ULYSSES_ERR_UNSUPPORTED;
+  if (!aligned16(a.x) || !aligned16(a.wg) || !aligned16(a.wu) || !aligned16(a.wd) ||
+      !aligned16(a.y) || !aligned16(a.dy) || !aligned16(a.dx) || !aligned16(a.dwg) ||
+      !aligned16(a.dwu) || !aligned16(a.dwd))
+    return ULYSSES_ERR_ALIGNMENT;
+  if (a.shard_rows > a.T && a.T > 0) a.shard_rows = a.T;
+  if (a.T > 0) {
+    const size_t need = ulysses::tiled_mlp_workspace_bytes(a.shard_rows, a.d, a.I, a.backward);
+    if (a.workspace == nullptr || ws_bytes < need) return ULYSSES_ERR_WORKSPACE;
+    if (!aligned16(a.workspace)) return ULYSSES_ERR_ALIGNMENT;
+  } else if (!a.backward) {
+    return ULYSSES_OK;
+  }
+  return from_hip(ulysses::launch_tiled_mlp(a, stream));
+}
+
+}  // namespace
+
+ulysses_status_t ulysses_tiled_mlp_fwd(const void* x, const void* wg, const void* wu,
+                                       const void* wd, int64_t T, int64_t d, int64_t inter,
+                                       ulysses_dtype_t dtype, int64_t shard_rows, void* y,
+                                       void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream) {
+  ulysses::TiledMlpArgs a{};
+  a.x = x;
+  a.wg = wg;
+  a.wu = wu;
+  a.wd = wd;
+  a.T = T;
+  a.d = d;
+  a.I = inter;
+  a.shard_rows = shard_rows;
+  a.backward = false;
+  a.y = y;
+  a.workspace = workspace;
+  return tiled_mlp(a, dtype, workspace_bytes, stream);
+}
+
+ulysses_status_t ulysses_tiled_mlp_bwd(const void* x, const void* wg, const void* wu,
+                                       const void* wd, const void* dy, int64_t T, int64_t d,
+                                       int64_t inter, ulysses_dtype_t dtype, int64_t shard_rows,
+                                       void* dx, float* dwg, float* dwu, float* dwd,
+                                       void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream) {
+  ulysses::TiledMlpArgs a{};
+  a.x = x;
+  a.wg = wg;
+  a.wu = wu;
+  a.wd = wd;
+  a.dy = dy;
+  a.T = T;
+  a.d = d;
+  a.I = inter;
+  a.shard_rows = shard_rows;
+  a.backward = true;
+  a.dx = dx;
+  a.dwg = dwg;
+  a.dwu = dwu;
+  a.dwd = dwd;
+  a.workspace = workspace;
+  return tiled_mlp(a, dtype, workspace_bytes, stream);
+}
+
 }  // extern "C"

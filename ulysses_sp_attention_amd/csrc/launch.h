@@ -144,4 +144,26 @@ size_t logits_loss_workspace_bytes(int64_t shard_rows, int64_t V);
 // handle could be made.
 hipError_t launch_logits_loss(const LogitsLossArgs& a, hipStream_t stream);
 
+// Sequence-tiled SwiGLU MLP over T rows, shard_rows at a time.  x [T, d],
+// wg and wu [I, d], wd [d, I], y/dy/dx [T, d] bf16; dwg, dwu [I, d] and dwd
+// [d, I] fp32; workspace of tiled_mlp_workspace_bytes(shard_rows, d, I,
+// backward).  backward == false: y only; true: dx, dwg, dwu, dwd from dy.
+struct TiledMlpArgs {
+  const void* x;
+  const void* wg;
+  const void* wu;
+  const void* wd;
+  const void* dy;
+  int64_t T, d, I, shard_rows;
+  bool backward;
+  void* y;
+  void* dx;
+  float* dwg;
+  float* dwu;
+  float* dwd;
+  void* workspace;
+};
+size_t tiled_mlp_workspace_bytes(int64_t shard_rows, int64_t d, int64_t I, bool backward);
+hipError_t launch_tiled_mlp(const TiledMlpArgs& a, hipStream_t stream);
+
 }  // namespace ulysses

@@ -14,8 +14,7 @@
 // then one workgroup sums the row losses and counts the kept tokens in a
 // fixed order (bitwise reproducible).  The GEMMs are plain dense products,
 // left to the vendor library; the fused part is the row kernel.
-#include <rocblas/rocblas.h>
-
+#include "blas.h"
 #include "device_common.h"
 #include "launch.h"
 
@@ -150,41 +149,6 @@ __global__ __launch_bounds__(256) void zero_f32_kernel(float* __restrict__ x, in
   if (i < n) x[i] = 0.0f;
 }
 
-// One rocBLAS handle per host thread and device, made on first use with
-// that device current (calls on one handle from two threads would race on
-// its stream).  Split-K atomics are switched off: every result is a fixed
-// sequence of operations.
-rocblas_handle blas_handle() {
-  thread_local rocblas_handle handles[64] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
-  if (!handles[dev]) {
-    rocblas_handle h = nullptr;
-    if (rocblas_create_handle(&h) != rocblas_status_success) return nullptr;
-    if (rocblas_set_atomics_mode(h, rocblas_atomics_not_allowed) != rocblas_status_success) {
-      rocblas_destroy_handle(h);
-      return nullptr;
-    }
-    handles[dev] = h;
-  }
-  return handles[dev];
-}
-
-// Column-major GEMM D = alpha op(A) op(B) + beta D with bf16 A, B and fp32
-// arithmetic; D is fp32 or bf16.
-rocblas_status gemm(rocblas_handle hd, bool ta, bool tb, int64_t m, int64_t n, int64_t k,
-                    const void* a, int64_t lda, const void* b, int64_t ldb, float beta, void* d,
-                    bool d_bf16, int64_t ldd) {
-  const float alpha = 1.0f;
-  const rocblas_datatype dt = d_bf16 ? rocblas_datatype_bf16_r : rocblas_datatype_f32_r;
-  return rocblas_gemm_ex(hd, ta ? rocblas_operation_transpose : rocblas_operation_none,
-                         tb ? rocblas_operation_transpose : rocblas_operation_none, (rocblas_int)m,
-                         (rocblas_int)n, (rocblas_int)k, &alpha, a, rocblas_datatype_bf16_r,
-                         (rocblas_int)lda, b, rocblas_datatype_bf16_r, (rocblas_int)ldb, &beta, d,
-                         dt, (rocblas_int)ldd, d, dt, (rocblas_int)ldd, rocblas_datatype_f32_r,
-                         rocblas_gemm_algo_standard, 0, 0);
-}
-
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 }  // namespace
@@ -215,19 +179,17 @@ hipError_t launch_logits_loss(const LogitsLossArgs& a, hipStream_t stream) {
     const int64_t rows = T - r0 < a.shard_rows ? T - r0 : a.shard_rows;
     const __bf16* hs = h + r0 * d;
     // Z^T (col-major V x rows) = W (col-major d x V)^T . H_s^T (col-major d x rows)
-    if (gemm(hd, true, false, V, rows, d, a.w, d, hs, d, 0.0f, z, false, V) != rocblas_status_success)
+    if (!gemm_bf16(hd, true, false, V, rows, d, a.w, d, hs, d, 0.0f, z, false, V))
       return hipErrorUnknown;
     e = launch_kernel(V % 4 == 0 ? ce_grad_kernel<true> : ce_grad_kernel<false>,
                       dim3((uint32_t)rows), dim3(kCeThreads), 0, stream, z, g, a.labels + r0,
                       a.loss_rows + r0, V, a.ignore_index, a.grad_scale);
     if (e != hipSuccess) return e;
     // dH_s^T (col-major d x rows) = W (col-major d x V) . G^T (col-major V x rows)
-    if (gemm(hd, false, false, d, rows, V, a.w, d, g, V, 0.0f, dh + r0 * d, true, d) !=
-        rocblas_status_success)
+    if (!gemm_bf16(hd, false, false, d, rows, V, a.w, d, g, V, 0.0f, dh + r0 * d, true, d))
       return hipErrorUnknown;
     // dW^T (col-major d x V) (+)= H_s^T (col-major d x rows) . G (col-major V x rows)^T
-    if (gemm(hd, false, true, d, V, rows, hs, d, g, V, r0 == 0 ? 0.0f : 1.0f, a.dw, false, d) !=
-        rocblas_status_success)
+    if (!gemm_bf16(hd, false, true, d, V, rows, hs, d, g, V, r0 == 0 ? 0.0f : 1.0f, a.dw, false, d))
       return hipErrorUnknown;
   }
   return launch_kernel(loss_sum_kernel, dim3(1), dim3(kSumThreads), 0, stream, a.loss_rows,
