@@ -46,8 +46,9 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(
   const int64_t i = ib / bs;
   const int64_t si = ((int64_t)b * heads + h) * N + i;
   const float la = lse_a[si], lb = lse_b[si];
-  const u32x4_t va = *reinterpret_cast<const u32x4_t*>(o_a + r * HD + sub * kVec);
-  const u32x4_t vb = *reinterpret_cast<const u32x4_t*>(o_b + r * HD + sub * kVec);
+  // Streaming accesses (non-temporal): every O byte is touched once.
+  const u32x4_t va = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(o_a + r * HD + sub * kVec));
+  const u32x4_t vb = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(o_b + r * HD + sub * kVec));
 
   const float m = fmaxf(la, lb);
   float merged = -INFINITY, wa = 0.f, wb = 0.f;
@@ -80,7 +81,7 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(
     }
     out = __builtin_bit_cast(u32x4_t, y);
   }
-  *reinterpret_cast<u32x4_t*>(o + r * HD + sub * kVec) = out;
+  __builtin_nontemporal_store(out, reinterpret_cast<u32x4_t*>(o + r * HD + sub * kVec));
   if (sub == 0) lse[si] = merged;
 }
 

@@ -8,9 +8,11 @@
 // thread moves kUnroll vectors (all loads issued before the stores), with
 // consecutive lanes on consecutive 16-byte vectors of a row, so every wave
 // reads and writes whole 64-byte segments.  One vector per thread and many
-// small workgroups measured fastest on MI355X with the caches cold (5.4 TB/s
-// read+write for the 128K query pack, against 5.3 TB/s for a device-to-device
-// hipMemcpy of the same size; 4 or 8 vectors per thread: 4.6 and 3.5 TB/s).
+// small workgroups measured fastest on MI355X with the caches cold; loads and
+// stores are non-temporal (each byte is moved once), which took the four
+// exchanges of a training step, run back to back on cold buffers, from 5.1
+// to 5.7 TB/s read+write, above the 5.4 TB/s of a device-to-device copy of
+// the same bytes (4 or 8 vectors per thread measured slower).
 #include "device_common.h"
 #include "launch.h"
 
@@ -61,12 +63,12 @@ __global__ __launch_bounds__(kThreads) void exchange_kernel(ExchangeArgs a) {
       char* hp = head + (int64_t)row * s.head_row_bytes + (int64_t)col * 16;
       const char* src = kToHead ? cp : hp;
       dst[u] = kToHead ? hp : cp;
-      val[u] = *reinterpret_cast<const u32x4_t*>(src);
+      val[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src));
     }
   }
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u)
-    if (dst[u]) *reinterpret_cast<u32x4_t*>(dst[u]) = val[u];
+    if (dst[u]) __builtin_nontemporal_store(val[u], reinterpret_cast<u32x4_t*>(dst[u]));
 }
 
 }  // namespace
