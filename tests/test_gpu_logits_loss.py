@@ -168,3 +168,49 @@ def test_logits_loss_full_size_llama8b_lm_head_sampled():
     bound = 2.0 ** -7 * s * h.double().abs().sum(dim=0).cpu().numpy()
     assert np.all(np.abs(col) <= bound)
     assert np.isfinite(float(total.item()))
+
+
+def test_logits_loss_from_two_host_threads_at_once():
+    """Each host thread gets its own rocBLAS handle: two threads calling at
+    the same time on their own streams get the same bits as one call alone."""
+    import threading
+    import torch
+    import ulysses_sp_attention_amd as uly
+    T, d, V, shard = 96, 128, 3000, 32
+    h_bits, w_bits, labels = inputs(23, T, d, V, 10)
+    alone = run_gpu(h_bits, w_bits, labels, 0.5, shard)
+    h = to_device(h_bits, "bf16")
+    w = to_device(w_bits, "bf16")
+    lab = torch.tensor(labels, device="cuda")
+    outs, errors = [], []
+
+    def worker():
+        try:
+            stream = torch.cuda.Stream()
+            with torch.cuda.stream(stream):
+                rows = torch.empty(T, device="cuda")
+                total = torch.empty(1, device="cuda")
+                good = torch.empty(1, dtype=torch.int64, device="cuda")
+                dh = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
+                dw = torch.empty((V, d), device="cuda")
+                ws = torch.empty(uly.ulysses_logits_loss_workspace_size(shard, V),
+                                 dtype=torch.uint8, device="cuda")
+                for _ in range(3):
+                    uly.ulysses_logits_loss(h, w, lab, rows, total, good, dh, dw, ws, 0.5, shard)
+            stream.synchronize()
+            outs.append((rows.cpu().numpy().astype(np.float64), float(total.item()),
+                         int(good.item()), dh.float().cpu().numpy().astype(np.float64),
+                         dw.cpu().numpy().astype(np.float64)))
+        except Exception as e:   # reported below, in the test's own thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker) for _ in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=60)
+    assert not errors, errors
+    assert len(outs) == 2
+    for got in outs:
+        for x, y in zip(got, alone):
+            assert np.array_equal(np.asarray(x), np.asarray(y))
