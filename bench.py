@@ -63,6 +63,8 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--loss-shard-rows", type=int, default=4096,
+                    help="rows of logits per shard in the language-model loss record")
     ap.add_argument("--no-logits-loss", action="store_true",
                     help="skip the language-model loss and tiled MLP records (outside the "
                          "attention step)")
@@ -326,12 +328,13 @@ def measure_fused(uly, torch, np, stream, args, rank, scale, lse, ws, tables, fw
 
 def measure_logits_loss(uly, torch, np, stream, args):
     """The language-model loss of one rank's tokens at the Llama-8B lm_head
-    (d = 4096, vocab = 128256) over the 128K share's 16384 tokens, 4096 rows
-    of logits at a time: three GEMMs per shard (6 T V d flop in all) and the
+    (d = 4096, vocab = 128256) over the 128K share's 16384 tokens,
+    --loss-shard-rows rows of logits at a time: three GEMMs per shard (6 T V d
+    flop in all) and the
     row kernel.  Outside the attention step; timed with HIP events on the
     launch stream around each call."""
     import synth
-    T, d, V, shard = 16384, 4096, 128256, 4096
+    T, d, V, shard = 16384, 4096, 128256, args.loss_shard_rows
     gen = torch.Generator(device="cuda")
     gen.manual_seed(99)
     h = torch.randn((T, d), device="cuda", generator=gen).to(torch.bfloat16)
