@@ -97,12 +97,11 @@ __global__ __launch_bounds__(kCeThreads) void ce_grad_kernel(const float* __rest
   const float lse2 = row_stat[0];
   if constexpr (kVec4) {
     for (int64_t v = 4 * (int64_t)tid; v < V; v += 4 * kCeThreads) {
-      const float4 x = *reinterpret_cast<const float4*>(zr + v);
+      const f32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(zr + v));   // last use
       bf16x4_t o;
-      o[0] = (__bf16)(s * (exp2f(x.x * kLog2e - lse2) - (v + 0 == y ? 1.0f : 0.0f)));
-      o[1] = (__bf16)(s * (exp2f(x.y * kLog2e - lse2) - (v + 1 == y ? 1.0f : 0.0f)));
-      o[2] = (__bf16)(s * (exp2f(x.z * kLog2e - lse2) - (v + 2 == y ? 1.0f : 0.0f)));
-      o[3] = (__bf16)(s * (exp2f(x.w * kLog2e - lse2) - (v + 3 == y ? 1.0f : 0.0f)));
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        o[e] = (__bf16)(s * (exp2f(x[e] * kLog2e - lse2) - (v + e == y ? 1.0f : 0.0f)));
       *reinterpret_cast<bf16x4_t*>(gr + v) = o;
     }
   } else {

@@ -32,13 +32,12 @@ __global__ __launch_bounds__(kEwThreads) void swiglu_fwd_kernel(const float* __r
                                                                 __bf16* __restrict__ a, int64_t n) {
   const int64_t i = ((int64_t)blockIdx.x * kEwThreads + threadIdx.x) * 4;
   if (i + 4 <= n) {
-    const float4 gv = *reinterpret_cast<const float4*>(g + i);
-    const float4 uv = *reinterpret_cast<const float4*>(u + i);
+    // g and u are read once: non-temporal
+    const f32x4_t gv = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(g + i));
+    const f32x4_t uv = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(u + i));
     bf16x4_t o;
-    o[0] = (__bf16)(gv.x * sigmoidf(gv.x) * uv.x);
-    o[1] = (__bf16)(gv.y * sigmoidf(gv.y) * uv.y);
-    o[2] = (__bf16)(gv.z * sigmoidf(gv.z) * uv.z);
-    o[3] = (__bf16)(gv.w * sigmoidf(gv.w) * uv.w);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = (__bf16)(gv[e] * sigmoidf(gv[e]) * uv[e]);
     *reinterpret_cast<bf16x4_t*>(a + i) = o;
   } else {
     for (int64_t j = i; j < n; ++j) a[j] = (__bf16)(g[j] * sigmoidf(g[j]) * u[j]);
@@ -66,11 +65,13 @@ __global__ __launch_bounds__(kEwThreads) void swiglu_bwd_kernel(const float* __r
                                                                 __bf16* __restrict__ du, int64_t n) {
   const int64_t i = ((int64_t)blockIdx.x * kEwThreads + threadIdx.x) * 4;
   if (i + 4 <= n) {
-    const float4 gv = *reinterpret_cast<const float4*>(g + i);
-    const float4 uv = *reinterpret_cast<const float4*>(u + i);
-    const float4 dv = *reinterpret_cast<const float4*>(da + i);
-    const SwigluGrad r[4] = {swiglu_bwd_one(gv.x, uv.x, dv.x), swiglu_bwd_one(gv.y, uv.y, dv.y),
-                             swiglu_bwd_one(gv.z, uv.z, dv.z), swiglu_bwd_one(gv.w, uv.w, dv.w)};
+    // g, u and da are read once: non-temporal
+    const f32x4_t gv = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(g + i));
+    const f32x4_t uv = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(u + i));
+    const f32x4_t dv = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(da + i));
+    SwigluGrad r[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = swiglu_bwd_one(gv[e], uv[e], dv[e]);
     bf16x4_t oa, og, ou;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
