@@ -22,6 +22,10 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# A test may point this at a deliberately broken build of oracle.c to show
+# that the pins catch the mistake (tests/test_oracle_mutants.py); that build
+# is never made here.
+_LIB_OVERRIDE = os.environ.get("ULYSSES_ORACLE_LIB")
 _lib = None
 
 
@@ -38,9 +42,12 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB_PATH):
-        build_lib()
-    lib = ctypes.CDLL(_LIB_PATH)
+    if _LIB_OVERRIDE:
+        lib = ctypes.CDLL(_LIB_OVERRIDE)
+    else:
+        if not os.path.exists(_LIB_PATH):
+            build_lib()
+        lib = ctypes.CDLL(_LIB_PATH)
     vp, i64, ci, dbl = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_double
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ci

@@ -693,3 +693,47 @@ def test_swiglu_mlp_rows_are_independent():
     x, wg, wu, wd, dy = mlp_inputs(10, 6, 9, seed=4)
     y = oracle.swiglu_mlp(x, wg, wu, wd)
     np.testing.assert_array_equal(oracle.swiglu_mlp(x[3:7], wg, wu, wd), y[3:7])
+
+
+def test_logits_loss_magnitudes_match_torch_absolute_sums():
+    """The rounding-bound magnitudes of the loss: zmag_i = max_v sum_k
+    |h_ik w_vk|, dh_mag = |G| |W|, dw_mag = |G|^T |H|, with G the gradient of
+    s * loss_sum with respect to the logits, from torch's own cross-entropy
+    and autograd (fp64)."""
+    T, d, V, s = 11, 6, 17, 0.3
+    h, w, labels = lm_inputs(T, d, V, seed=77, ignore_every=3)
+    *_, mags = oracle.logits_loss(h, w, labels, s, magnitude=True)
+    ht, wt = torch.tensor(h), torch.tensor(w)
+    z = (ht @ wt.T).detach().requires_grad_(True)
+    rows = torch.nn.functional.cross_entropy(z, torch.tensor(labels),
+                                             ignore_index=oracle.IGNORE_INDEX, reduction="none")
+    (s * rows.sum()).backward()
+    g_abs = z.grad.abs()
+    want_zmag = (ht.abs()[:, None, :] * wt.abs()[None, :, :]).sum(-1).max(-1).values
+    np.testing.assert_allclose(mags["zmag"], want_zmag.numpy(), rtol=1e-13)
+    np.testing.assert_allclose(mags["dh"], (g_abs @ wt.abs()).numpy(), rtol=1e-11, atol=1e-15)
+    np.testing.assert_allclose(mags["dw"], (g_abs.T @ ht.abs()).numpy(), rtol=1e-11, atol=1e-15)
+    # and they bound the values they describe
+    _, _, _, dh, dw = oracle.logits_loss(h, w, labels, s)
+    assert np.all(np.abs(dh) <= mags["dh"] * (1 + 1e-12)) and np.all(np.abs(dw) <= mags["dw"] * (1 + 1e-12))
+
+
+def test_swiglu_mlp_magnitudes_match_torch_absolute_sums():
+    """The rounding-bound magnitudes of the MLP: y_mag = |a| |Wd|^T,
+    dx_mag = |dg| |Wg| + |du| |Wu|, dwg_mag = |dg|^T |x|, dwu_mag = |du|^T |x|,
+    dwd_mag = |dy|^T |a|, with a, dg and du from torch autograd (fp64)."""
+    T, d, I = 7, 5, 9
+    x, wg, wu, wd, dy = mlp_inputs(T, d, I, seed=31)
+    *_, mags = oracle.swiglu_mlp(x, wg, wu, wd, dy, magnitude=True)
+    xt, wgt, wut, wdt, dyt = (torch.tensor(a) for a in (x, wg, wu, wd, dy))
+    g = (xt @ wgt.T).requires_grad_(True)
+    u = (xt @ wut.T).requires_grad_(True)
+    a = torch.nn.functional.silu(g) * u
+    (a @ wdt.T).backward(dyt)
+    dg, du, aa = g.grad.abs(), u.grad.abs(), a.detach().abs()
+    want = {"y": aa @ wdt.abs().T, "dx": dg @ wgt.abs() + du @ wut.abs(), "dwg": dg.T @ xt.abs(),
+            "dwu": du.T @ xt.abs(), "dwd": dyt.abs().T @ aa}
+    for name, ref in want.items():
+        np.testing.assert_allclose(mags[name], ref.numpy(), rtol=1e-11, atol=1e-15, err_msg=name)
+    y_only = oracle.swiglu_mlp(x, wg, wu, wd, magnitude=True)
+    np.testing.assert_allclose(y_only[1]["y"], want["y"].numpy(), rtol=1e-11, atol=1e-15)
