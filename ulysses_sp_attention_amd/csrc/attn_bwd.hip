@@ -10,7 +10,7 @@
 //   dV_j  = sum_{h in group} sum_i P_ij dO_i
 // P is recomputed from Q, K and the saved LSE; nothing of size N x N is
 // stored.  Three launches on the caller's stream:
-//   1. bwd_stats_kernel: -D and -LSE log2(e) for every query row, into the
+//   1. bwd_stats_kernel: -D and -LSE / scale for every query row, into the
 //      workspace;
 //   2. dQ: a workgroup owns query rows (as in the forward) and walks the
 //      visible key tiles staged in LDS;
@@ -18,7 +18,9 @@
 //      the visible query tiles of every query head of its group, so the GQA
 //      sum over heads happens in registers; no atomics anywhere, so results
 //      are deterministic.
-// Every product is a v_mfma_f32_32x32x16_bf16.  Operands whose contraction
+// Q, K, V and dO enter the products exactly as given (bf16); the softmax
+// scale and log2(e) are applied to the fp32 scores, so they add no bf16
+// rounding.  Every product is a v_mfma_f32_32x32x16_bf16.  Operands whose contraction
 // runs along the sequence (dV = P^T dO, dK = dS^T Q, dQ = dS K) come from
 // LDS through the transposing read ds_read_b64_tr_b16, so all tiles keep
 // their natural row layout in LDS.
@@ -34,7 +36,7 @@ namespace ulysses {
 namespace {
 
 // Workspace: one fp32 array per query row of [bs, hq, N], 256-byte aligned:
-// D for the fp32 path; -D then -LSE log2(e) for the bf16 path.
+// D for the fp32 path; -D then -LSE / scale for the bf16 path.
 size_t stat_array_bytes(const AttnShape& s) {
   return ((size_t)s.N * s.bs * s.hq * sizeof(float) + 255) / 256 * 256;
 }
@@ -44,7 +46,7 @@ struct BwdParams {
   const __bf16* k;
   const __bf16* v;
   const __bf16* dout;
-  const float* nlse2;   // -LSE log2(e), [batch][head][position]
+  const float* nlse_r;  // -LSE / scale (raw score units), [batch][head][position]
   const float* nD;      // -<dO, O>, same layout
   __bf16* dq;
   __bf16* dk;
@@ -71,18 +73,17 @@ struct BwdParams {
 // ------------------------------------------------------------------------
 // A workgroup of 8 waves owns a block of query positions for GPACK query
 // heads of one key/value head, as in the forward: each wave owns 32 query
-// rows of one head and keeps Q' = Q * scale * log2(e) (rounded to bf16 once)
-// and dO in registers.  For every 64-key tile t it forms, transposed so
-// that each lane holds one query row,
-//   S'^T = K Q'^T,  P = exp2(S' - LSE log2(e)),  dP^T = V dO^T,
+// rows of one head and keeps Q and dO in registers.  For every 64-key tile t
+// it forms, transposed so that each lane holds one query row,
+//   S^T = K Q^T,  P = exp2(S scale log2(e) - LSE log2(e)),  dP^T = V dO^T,
 //   dS = P (dP - D),  dQ^T += K^T dS^T
 // (K^T by transposing LDS reads).  As in the forward, matrix and vector work
 // alternate between the two waves of a SIMD: in every phase one wave issues
-// only matrix products (dQ of tile t-1, then S'^T and dP^T of tile t: 48
+// only matrix products (dQ of tile t-1, then S^T and dP^T of tile t: 48
 // products) while its partner forms dS of a tile; the second group of waves
 // runs one phase behind the first.  K and V tiles arrive by direct
 // global-to-LDS copies three tiles ahead.  A K tile is read for two tiles
-// (S'^T now, K^T for dQ next), so K rotates through five buffers (a
+// (S^T now, K^T for dQ next), so K rotates through five buffers (a
 // run-time rotation) and V through four (unrolled, compile-time).
 template <int HD, int GPACK>
 struct DqCfg {
@@ -146,26 +147,23 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_kernel(BwdParams p) {
   const __bf16* vbase = reinterpret_cast<const __bf16*>(wave_uniform(
       kFused ? (int64_t)p.cv.chunk[0] : reinterpret_cast<int64_t>(p.v + ((int64_t)b * p.kv_row_heads + kh) * HD)));
 
-  // B operands of this lane's query row: Q' (scaled, rounded once) and dO.
+  // B operands of this lane's query row: Q and dO as stored.
   bf16x8_t qf[C::kKS], df[C::kKS];
 #pragma unroll
   for (int ks = 0; ks < C::kKS; ++ks) {
-    bf16x8_t rq = bf16x8_t{}, rd = bf16x8_t{};
+    qf[ks] = bf16x8_t{};
+    df[ks] = bf16x8_t{};
     if (qi < N) {
       const __bf16* qrow = kFused ? chunk_row(p.cq, (uint32_t)qi, p.bs, b, h, HD) : p.q + qi * q_tok + qoff;
       const __bf16* drow = kFused ? chunk_row(p.cdo, (uint32_t)qi, p.bs, b, h, HD) : p.dout + qi * q_tok + qoff;
-      rq = *reinterpret_cast<const bf16x8_t*>(qrow + 16 * ks + 8 * half);
-      rd = *reinterpret_cast<const bf16x8_t*>(drow + 16 * ks + 8 * half);
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      qf[ks][e] = (__bf16)((float)rq[e] * p.scale_log2);
-      df[ks][e] = (__bf16)((float)rd[e] * 1.0f);
+      qf[ks] = *reinterpret_cast<const bf16x8_t*>(qrow + 16 * ks + 8 * half);
+      df[ks] = *reinterpret_cast<const bf16x8_t*>(drow + 16 * ks + 8 * half);
     }
   }
+  const float c2 = p.scale_log2;   // softmax scale * log2(e)
   const int64_t stat = ((int64_t)b * p.hq + h) * N + qi;
-  const float nl = qi < N ? p.nlse2[stat] : 0.f;   // -LSE log2(e)
-  const float nd = qi < N ? p.nD[stat] : 0.f;      // -D
+  const float nl = qi < N ? p.nlse_r[stat] * c2 : 0.f;   // -LSE log2(e)
+  const float nd = qi < N ? p.nD[stat] : 0.f;           // -D
 
   // Key range of the block; every wave walks all its tiles (one schedule for
   // all waves), tiles a wave does not see being masked out entirely.
@@ -229,11 +227,11 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_kernel(BwdParams p) {
   f32x16_t acc[C::kDB];   // dQ^T
 #pragma unroll
   for (int db = 0; db < C::kDB; ++db) acc[db] = f32x16_t{};
-  f32x16_t s[2], dp[2];   // S'^T and dP^T of a tile (two 32-key halves)
+  f32x16_t s[2], dp[2];   // S^T and dP^T of a tile (two 32-key halves)
   bf16x8_t dsf[4];        // bf16 dS^T of a tile, B operand of dQ^T
 
   // --- matrix phase: dQ^T += K^T dS^T of tile m-1 (DQ, K buffer lkp), then
-  // S'^T and dP^T of tile m (SP, K buffer lk, V buffer lv) --------------------
+  // S^T and dP^T of tile m (SP, K buffer lk, V buffer lv) ---------------------
   int koff[C::kKS];
 #pragma unroll
   for (int ks = 0; ks < C::kKS; ++ks) koff[ks] = swz<C::kChunks, C::kRowBytes>(r32, 2 * ks + half);
@@ -275,6 +273,11 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_kernel(BwdParams p) {
   auto vector_phase = [&](int m, auto issue) __attribute__((always_inline)) {
     const int jr = m * C::kBC;   // first key of the tile, relative to key0
     issue(0);
+    // Raw fp32 scores to the exp2 domain: S scale log2(e) - LSE log2(e).
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[kb][i] = fmaf(s[kb][i], c2, nl);
     // Element mask without compares (as in the forward): invisible scores
     // become exactly -2^100, whose probability is exactly 0.
     if (jr < flo || jr + C::kBC > fhi) {
@@ -294,7 +297,7 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_kernel(BwdParams p) {
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float pv = __builtin_amdgcn_exp2f(s[kb][i] + nl);
+        const float pv = __builtin_amdgcn_exp2f(s[kb][i]);
         dsf[2 * kb + (i >> 3)][i & 7] = (__bf16)(pv * (dp[kb][i] + nd));
       }
       issue(2 + kb);
@@ -369,7 +372,7 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_kernel(BwdParams p) {
       block_barrier();
     }
 
-    // Pair 0: S'^T and dP^T of tile 0 only.
+    // Pair 0: S^T and dP^T of tile 0 only.
     matrix_phase(false_type{}, true_type{}, k_buf(0), k_buf(0), v_buf(0));
     block_barrier();
     auto issue0 = [&](int k) __attribute__((always_inline)) {
@@ -422,9 +425,10 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_kernel(BwdParams p) {
 // query head of the GQA group within a query tile, so the sum over the
 // group's heads stays in registers (no atomics: results are deterministic).
 // For step n:
-//   the P wave holds K' = K * scale * log2(e) (rounded to bf16 once) and
-//     forms S'_n = Q_n K'^T - LSE log2(e), whose accumulator starts at the
-//     negated statistic, so P_n = exp2(S'_n) needs no further arithmetic;
+//   the P wave holds K and forms S'_n = Q_n K^T - LSE / scale, whose
+//     accumulator starts at the negated statistic, so that
+//     P_n = exp2(S'_n scale log2(e)) needs one multiply per score (K stays
+//     exact: the scale is applied to the fp32 scores; c = scale log2(e));
 //     then dV^T += dO^T P;
 //   the dS wave holds V and forms dP'_n = dO_n V^T - D (likewise seeded),
 //     dS = P dP' and dK^T += Q^T dS.
@@ -433,7 +437,7 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_kernel(BwdParams p) {
 // only vector work, which the SIMD executes alongside:
 //   phase A(n): P wave  S'_n, dV^T += dO_{n-1}^T P_{n-1}        (matrix)
 //               dS wave dS_{n-1} = P_{n-1} dP'_{n-1}, to bf16  (vector)
-//   phase B(n): P wave  mask, P_n = exp2(S'_n)                  (vector)
+//   phase B(n): P wave  scale, mask, P_n = exp2(S'_n c)          (vector)
 //               dS wave dK^T += Q_{n-1}^T dS_{n-1}, dP'_n       (matrix)
 // P reaches the dS wave through LDS as the same bf16 values that form dV
 // (one buffer per block; measured 4% faster than an fp32 hand-off).  Q and dO
@@ -537,24 +541,21 @@ __global__ __launch_bounds__(512) void attn_bwd_dkv_kernel(BwdParams p) {
   const int64_t kv_tok = (int64_t)p.bs * p.kv_row_heads * HD;
   const int64_t kvoff = ((int64_t)b * p.kv_row_heads + kh) * HD;
 
-  // B operand rows of this lane: K' (P wave) or V (dS wave; the multiply by
-  // one leaves it exact).
+  // B operand rows of this lane, as stored: K (P wave) or V (dS wave).
   bf16x8_t bfrag[C::kKS];
   {
     const __bf16* rows = p_wave ? p.k : p.v;
-    const float mul = p_wave ? p.scale_log2 : 1.0f;
     const __bf16* krow = nullptr;
     if (kj < N)
       krow = kFused ? chunk_row(p_wave ? p.ck : p.cv, (uint32_t)kj, p.bs, b, kh, HD)
                     : rows + kj * kv_tok + kvoff;
 #pragma unroll
     for (int ks = 0; ks < C::kKS; ++ks) {
-      bf16x8_t raw = bf16x8_t{};
-      if (kj < N) raw = *reinterpret_cast<const bf16x8_t*>(krow + 16 * ks + 8 * half);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) bfrag[ks][e] = (__bf16)((float)raw[e] * mul);
+      bfrag[ks] = bf16x8_t{};
+      if (kj < N) bfrag[ks] = *reinterpret_cast<const bf16x8_t*>(krow + 16 * ks + 8 * half);
     }
   }
+  const float c2 = p.scale_log2;   // softmax scale * log2(e)
 
   // Queries seen by the workgroup's keys: [q_lo, q_hi).  Steps walk its
   // 64-row query tiles from the last one down (concurrent workgroups then
@@ -609,8 +610,8 @@ __global__ __launch_bounds__(512) void attn_bwd_dkv_kernel(BwdParams p) {
     }
   };
   // Part k of a group's copies for step c: tile slices k < kCopies of Q (or
-  // dO) into tile buffer `tile`, then at k == kCopies its statistic -LSE
-  // log2(e) (or -D) into `stat`.
+  // dO) into tile buffer `tile`, then at k == kCopies its statistic
+  // -LSE / scale (or -D) into `stat`.
   auto copy_part = [&](auto q_tag, const Cursor& c, int k, char* tile, char* stat)
       __attribute__((always_inline)) {
     constexpr bool kQ = decltype(q_tag)::value;
@@ -635,7 +636,7 @@ __global__ __launch_bounds__(512) void attn_bwd_dkv_kernel(BwdParams p) {
       }
       copy_lds16_async_sbase(base, off, tile + cidx * 1024);
     } else if (k == C::kCopies) {
-      const float* src = kQ ? p.nlse2 : p.nD;
+      const float* src = kQ ? p.nlse_r : p.nD;
       const char* base = reinterpret_cast<const char*>(
           wave_uniform(reinterpret_cast<int64_t>(src + ((int64_t)b * p.hq + h) * N + i0)));
       int row = lane;
@@ -738,10 +739,16 @@ __global__ __launch_bounds__(512) void attn_bwd_dkv_kernel(BwdParams p) {
         __builtin_amdgcn_sched_barrier(0);
       }
     };
-    // Vector phase of a step whose first query is i0r: mask, exponentials,
-    // P to LDS; issue(k), k = 0..4, issues part k of the dO copies.
+    // Vector phase of a step whose first query is i0r: scale, mask,
+    // exponentials, P to LDS; issue(k), k = 0..4, issues part k of the dO
+    // copies.
     auto vector = [&](int i0r, auto issue) __attribute__((always_inline)) {
       issue(0);
+      // S' scale log2(e) = S scale log2(e) - LSE log2(e): the exp2 domain.
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[sub][i] *= c2;
       // Element mask without compares: with [lo, hi) the visible queries of
       // this lane's key as offsets into the sub-tile, each score gets
       // clamp(min(q - lo, hi - 1 - q), -1, 0) * 2^100 added: exactly 0 when
@@ -976,7 +983,7 @@ __global__ __launch_bounds__(512) void attn_bwd_dkv_kernel(BwdParams p) {
   }
 }
 
-// -D_i = -<dO_i, O_i> and -LSE_i log2(e) of every query row, stored
+// -D_i = -<dO_i, O_i> and -LSE_i / scale of every query row, stored
 // [batch][head][position]: the dQ kernel reads them per row, the dK/dV
 // kernel as 64-row runs.  kLanes lanes reduce one row.  In the fused form O
 // and dO are read from their sequence chunks (co, cdo).
@@ -985,9 +992,9 @@ __global__ __launch_bounds__(256) void bwd_stats_kernel(const __bf16* __restrict
                                                         const __bf16* __restrict__ dout,
                                                         const float* __restrict__ lse,
                                                         float* __restrict__ nD,
-                                                        float* __restrict__ nlse2, int64_t rows,
-                                                        int64_t N, int bs, int hq, SeqChunks co,
-                                                        SeqChunks cdo) {
+                                                        float* __restrict__ nlse_r, float scale,
+                                                        int64_t rows, int64_t N, int bs, int hq,
+                                                        SeqChunks co, SeqChunks cdo) {
   constexpr int kLanes = HD / 8;
   constexpr int kRowsPerBlock = 256 / kLanes;
   const int64_t r = (int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / kLanes;
@@ -1011,7 +1018,7 @@ __global__ __launch_bounds__(256) void bwd_stats_kernel(const __bf16* __restrict
   if (r < rows && sub == 0) {
     const int64_t idx = ((int64_t)b * hq + h) * N + i;
     nD[idx] = -acc;
-    nlse2[idx] = -(lse[idx] * kLog2e);
+    nlse_r[idx] = -lse[idx] / scale;
   }
 }
 
@@ -1030,9 +1037,9 @@ template <bool kFused, bool kStatsFused = kFused>
 hipError_t launch_bwd(BwdParams& p, const AttnShape& s, const __bf16* o, const SeqChunks& co,
                       const float* lse, void* workspace, hipStream_t stream) {
   float* nD = static_cast<float*>(workspace);
-  float* nlse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + stat_array_bytes(s));
+  float* nlse_r = reinterpret_cast<float*>(static_cast<char*>(workspace) + stat_array_bytes(s));
   p.nD = nD;
-  p.nlse2 = nlse2;
+  p.nlse_r = nlse_r;
   p.N = s.N;
   p.bs = s.bs;
   p.hq = s.hq;
@@ -1052,7 +1059,7 @@ hipError_t launch_bwd(BwdParams& p, const AttnShape& s, const __bf16* o, const S
   hipError_t e = launch_kernel(s.hd == 128 ? bwd_stats_kernel<128, kStatsFused>
                                             : bwd_stats_kernel<64, kStatsFused>,
                                dim3((uint32_t)stat_blocks), dim3(256), 0, stream, o, p.dout, lse,
-                               nD, nlse2, rows, s.N, s.bs, s.hq, co, p.cdo);
+                               nD, nlse_r, s.scale, rows, s.N, s.bs, s.hq, co, p.cdo);
   if (e != hipSuccess) return e;
 
   auto dq_launch = [&](auto hd_tag) -> hipError_t {

@@ -34,11 +34,13 @@
 //    spent on staging), issued by the waves in pieces spread through their
 //    softmax phase, two pairs of phases ahead of use, into four rotating
 //    buffers per tensor (128 KiB of LDS at head size 128).
-//  * Online softmax in the exp2 domain with scale*log2(e) folded into one
-//    FMA per score.  The running max is only raised when a row's max grows by
-//    more than 8 (a factor 256), so O and the row sum are rarely rescaled;
-//    any reference max gives the same result in exact arithmetic.  The row
-//    max of a lane pair uses v_permlane32_swap.
+//  * Online softmax in the exp2 domain.  Q enters the products exactly as
+//    given (bf16); the fp32 score is taken to the exp2 domain by one FMA,
+//    s * scale*log2(e) - m, so the softmax scale adds no bf16 rounding.  The
+//    running max is only raised when a row's max grows by more than 8 (a
+//    factor 256), so O and the row sum are rarely rescaled; any reference max
+//    gives the same result in exact arithmetic.  The row max of a lane pair
+//    uses v_permlane32_swap.
 //  * Key tiles entirely above the diagonal (or outside the documents of a
 //    block) are never visited.  Every wave walks all tiles of its block;
 //    tiles crossing a boundary of some row of the wave (or not seen by it at
@@ -142,20 +144,18 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdParams p) {
     return chunk_row(c, (uint32_t)i, p.bs, b, h, HD);
   };
 
-  // Q fragments (B operand of S^T): lane holds Q[qi][16 ks + 8 half + 0..7],
-  // multiplied by scale*log2(e) and rounded to bf16 once, so that the
-  // products give scores already in the exp2 domain.
+  // Q fragments (B operand of S^T): lane holds Q[qi][16 ks + 8 half + 0..7]
+  // as stored (the scale is applied to the fp32 scores).
   bf16x8_t qf[C::kKS];
 #pragma unroll
   for (int ks = 0; ks < C::kKS; ++ks) {
-    bf16x8_t raw = bf16x8_t{};
+    qf[ks] = bf16x8_t{};
     if (qi < N) {
       const __bf16* row = kFused ? q_row(p.cq, qi) : qbase + qi * q_tok;
-      raw = *reinterpret_cast<const bf16x8_t*>(row + 16 * ks + 8 * half);
+      qf[ks] = *reinterpret_cast<const bf16x8_t*>(row + 16 * ks + 8 * half);
     }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qf[ks][e] = (__bf16)((float)raw[e] * p.scale_log2);
   }
+  const float c2 = p.scale_log2;   // softmax scale * log2(e)
 
   // Key range of the whole block, and the keys of this wave and lane.  Every
   // wave walks all key tiles of its block (so all waves share one schedule);
@@ -235,9 +235,9 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdParams p) {
   for (int db = 0; db < C::kDB; ++db) acc_o[db] = f32x16_t{};
   float m_run = -INFINITY;   // reference max, log2 domain
   float l_run = 0.f;         // this lane's share of the row sum
-  // Every score accumulation starts from -m_run (0 while the row has no
-  // maximum yet), so the products give s * scale*log2(e) - m_run directly.
-  f32x16_t sbias = f32x16_t{};
+  // -m_run, or 0 while the row has no maximum yet: a raw score s becomes
+  // s * scale*log2(e) - m_run.
+  float nbias = 0.f;
   bool ref_ready = false;    // every row of the wave has a reference max
   f32x16_t s[2];             // scores of a tile, from its matrix to its vector phase
   bf16x8_t pf[4];            // bf16 probabilities of a tile, awaiting its PV product
@@ -272,8 +272,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdParams p) {
     for (int idx = 0; idx < NS; ++idx) {
       if (idx + PF < NS) buf[(idx + PF) % (PF + 1)] = frag(idx + PF);
       if (idx < NQ) {
-        const f32x16_t c = idx < 2 ? sbias : s[idx & 1];
-        s[idx & 1] = mfma32(buf[idx % (PF + 1)], qf[idx >> 1], c);
+        s[idx & 1] = mfma32(buf[idx % (PF + 1)], qf[idx >> 1], idx < 2 ? f32x16_t{} : s[idx & 1]);
       } else {
         const int i = idx - NQ;
         acc_o[i % C::kDB] = mfma32(buf[idx % (PF + 1)], pf[i / C::kDB], acc_o[i % C::kDB]);
@@ -289,6 +288,11 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdParams p) {
   auto vector_phase = [&](int m, auto mask_tag, auto issue) __attribute__((always_inline)) {
     const int jr = m * C::kBC;   // first key of the tile, relative to key0
     issue(0);
+    // Raw fp32 scores to the exp2 domain, relative to the reference max.
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[kb][i] = fmaf(s[kb][i], c2, nbias);
     // Element mask on tiles that cross a boundary of some row of the wave,
     // without compares: with lo <= key < hi the visible keys of this row as
     // offsets into the tile, each score gets clamp(min(key - lo,
@@ -313,8 +317,9 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdParams p) {
 
     issue(1);
 
-    // P = exp2(s * scale*log2e - m_run), rounded to bf16 as the B operand of
-    // PV; returns this lane's share of the tile's row sum.
+    // P = exp2(s * scale*log2e - m_run) (s already in that form), rounded to
+    // bf16 as the B operand of PV; returns this lane's share of the tile's
+    // row sum.
     auto exps = [&](auto issue_tag) __attribute__((always_inline)) {
       float lt = 0.f;
 #pragma unroll
@@ -367,9 +372,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdParams p) {
       for (int db = 0; db < C::kDB; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc_o[db][i] *= alpha;
-      const float nb = m_run == -INFINITY ? 0.f : -m_run;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sbias[i] = nb;
+      nbias = m_run == -INFINITY ? 0.f : -m_run;
       const float shift = raise ? mx : 0.0f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
