@@ -1,15 +1,19 @@
 """The exchange fused into attention: the fused forward and backward must
 equal seq_to_head -> attention -> head_to_seq bit for bit (same arithmetic on
-the same values; only where rows are read and written differs), and must
-leave the other ranks' head slots of the output chunks untouched.  Every case
-runs with the chunks as consecutive slices of one tensor (the strided-view
-kernels) and as separate buffers at descending addresses (the chunk-table
-kernels)."""
+the same values; only where rows are read and written differs), must leave
+the other ranks' head slots of the output chunks untouched, and must match
+the oracle's attention on the rank's head slice of the inputs (the oracle's
+own exchange gathers that slice), every element at the small cases and
+sampled rows at the 128K share.  Every case runs with the chunks as
+consecutive slices of one tensor (the strided-view kernels) and as separate
+buffers at descending addresses (the chunk-table kernels)."""
 import numpy as np
 import pytest
 
+import oracle
 import synth
-from helpers import ensure_library, storage_bytes, to_device
+from helpers import (assert_close, assert_grads_close, assert_rows_close, ensure_library,
+                     sample_rows, storage_bytes, to_device, to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -50,6 +54,57 @@ def gather(chunks):
 
 def local_heads(heads, P):
     return heads // P if heads >= P else 1
+
+
+def rank_inputs(host, P, rank):
+    """The rank's head-sharded inputs by the oracle's exchange, from float64
+    host copies [N, bs, H, hd] of the sequence-sharded tensors."""
+    n = host[0].shape[0] // P
+    return [oracle.seq_to_head([np.ascontiguousarray(x[c * n:(c + 1) * n]) for c in range(P)], rank)
+            for x in host]
+
+
+def rank_slice(t, P, rank, rows=None):
+    """This rank's head slots of a gathered [N, bs, H, hd] output, float64."""
+    hl = t.shape[2] // P
+    out = t[:, :, rank * hl:(rank + 1) * hl]
+    if rows is not None:
+        import torch
+        out = out[torch.from_numpy(np.asarray(rows, dtype=np.int64)).to(t.device)]
+    return to_f64(out)
+
+
+_ORACLE_CACHE = {}
+
+
+def head_slices(tensors, P, rank):
+    """The rank's head slice of full-size device tensors [N, bs, H, hd] by
+    plain indexing, float64 (at the 128K share, float64 copies of every head
+    would take 10 GB of host memory); H >= P here, so no head is replicated."""
+    out = []
+    for t in tensors:
+        hl = t.shape[2] // P
+        out.append(to_f64(t[:, :, rank * hl:(rank + 1) * hl]))
+    return out
+
+
+def oracle_fwd(key, host, P, rank, scale, causal, cu, rows=None, sliced=False):
+    """oracle.attn_fwd on the rank's slice (cached per key: both layouts of a
+    case compare with the same values).  host: float64 copies of the
+    sequence-sharded inputs, or (sliced) of the rank's head slice."""
+    if key not in _ORACLE_CACHE:
+        ql, kl, vl = host[:3] if sliced else rank_inputs(host[:3], P, rank)
+        _ORACLE_CACHE[key] = oracle.attn_fwd(ql, kl, vl, scale, causal, cu, rows=rows,
+                                             magnitude=True)
+    return _ORACLE_CACHE[key]
+
+
+def oracle_bwd(key, host, P, rank, scale, causal, cu, rows=None, cols=None, sliced=False):
+    if key not in _ORACLE_CACHE:
+        ql, kl, vl, dol = host if sliced else rank_inputs(host, P, rank)
+        _ORACLE_CACHE[key] = oracle.attn_bwd(ql, kl, vl, dol, scale, causal, cu, dq_rows=rows,
+                                             dkv_cols=cols, magnitude=True)
+    return _ORACLE_CACHE[key]
 
 
 def unfused_fwd(qc, kc, vc, rank, scale, causal, cu_t, o_full):
@@ -95,7 +150,14 @@ def test_fused_fwd_equals_exchange_attention_exchange(P, rank, n, bs, hq, hkv, h
     k = to_device(synth.normal(seed, synth.STREAM_K, (N, bs, hkv, hd), "bf16"), "bf16")
     v = to_device(synth.normal(seed, synth.STREAM_V, (N, bs, hkv, hd), "bf16"), "bf16")
     cu_t = None if cu is None else torch.tensor(cu, dtype=torch.int32, device="cuda")
-    check_fwd(q, k, v, P, rank, scale, causal, cu_t, layout)
+    o, lse = check_fwd(q, k, v, P, rank, scale, causal, cu_t, layout)
+    host = [to_f64(t) for t in (q, k, v)]
+    o_ref, lse_ref, mo = oracle_fwd(("fwd", P, rank, n, bs, hq, hkv, hd, causal, str(cu)), host, P,
+                                    rank, scale, causal, cu)
+    got = rank_slice(o, P, rank)
+    assert_close(got, o_ref, "bf16", "O (fused) against the oracle", mo)
+    assert_rows_close(got, o_ref, "bf16", "O rows (fused) against the oracle")
+    assert_close(to_f64(lse), lse_ref, "bf16", "LSE (fused) against the oracle")
 
 
 def check_fwd(q, k, v, P, rank, scale, causal, cu_t, layout):
@@ -115,20 +177,29 @@ def check_fwd(q, k, v, P, rank, scale, causal, cu_t, layout):
     hl = hq // P
     untouched = torch.cat([o[:, :, :rank * hl], o[:, :, (rank + 1) * hl:]], dim=2)
     assert bool(torch.all(untouched == CANARY))
+    return o, lse
 
 
 @pytest.mark.parametrize("layout", LAYOUTS)
 def test_fused_fwd_full_size_llama8b_128k(layout):
     """The benchmark's shape: P = 8 chunks of 16384 tokens, 32 q / 8 kv heads, rank 3."""
-    import torch
-    P, rank, n, hq, hkv, hd = 8, 3, 16384, 32, 8, 128
-    N = P * n
-    gen = torch.Generator(device="cuda")
-    gen.manual_seed(4242)
-    q = (torch.randn((N, 1, hq, hd), device="cuda", generator=gen) / np.sqrt(hd)).to(torch.bfloat16)
-    k = torch.randn((N, 1, hkv, hd), device="cuda", generator=gen).to(torch.bfloat16)
-    v = torch.randn((N, 1, hkv, hd), device="cuda", generator=gen).to(torch.bfloat16)
-    check_fwd(q, k, v, P, rank, 1.0, True, None, layout)
+    w = synth.WORKLOADS["llama8b-share-128k"]
+    P, rank, N = w.P, w.rank, w.seqlen
+    q, k, v = (to_device(w.seq_tensor(st, heads, scale), "bf16")
+               for st, heads, scale in ((synth.STREAM_Q, w.hq, w.q_prescale),
+                                        (synth.STREAM_K, w.hkv, 1.0), (synth.STREAM_V, w.hkv, 1.0)))
+    o, lse = check_fwd(q, k, v, P, rank, w.softmax_scale, True, None, layout)
+    rows = sample_rows(N, w.seed, n_first=64, n_last=64, n_rand=192)
+    if ("fwd128k",) not in _ORACLE_CACHE:
+        host = head_slices((q, k, v), P, rank)
+    else:
+        host = None
+    o_ref, lse_ref, mo = oracle_fwd(("fwd128k",), host, P, rank, w.softmax_scale, True, None,
+                                    rows=rows, sliced=True)
+    got = rank_slice(o, P, rank, rows)
+    assert_close(got, o_ref, "bf16", "O rows (fused, 128K) against the oracle", mo)
+    assert_rows_close(got, o_ref, "bf16", "O per row (fused, 128K) against the oracle")
+    assert_close(to_f64(lse)[:, :, rows], lse_ref, "bf16", "LSE rows (fused, 128K) against the oracle")
 
 
 def unfused_bwd(qc, kc, vc, oc, lse, doc, rank, scale, causal, cu_t, dq_full, dk_full, dv_full):
@@ -183,6 +254,7 @@ def check_bwd(q, k, v, do, P, rank, scale, causal, cu_t, layout):
         hl = heads // P
         untouched = torch.cat([g[:, :, :rank * hl], g[:, :, (rank + 1) * hl:]], dim=2)
         assert bool(torch.all(untouched == CANARY)), name
+    return [gather(oc) for oc in outs]
 
 
 BWD_CASES = [
@@ -209,19 +281,31 @@ def test_fused_bwd_equals_exchange_backward_exchange(P, rank, n, bs, hq, hkv, hd
     v = to_device(synth.normal(seed, synth.STREAM_V, (N, bs, hkv, hd), "bf16"), "bf16")
     do = to_device(synth.normal(seed, synth.STREAM_DO, (N, bs, hq, hd), "bf16"), "bf16")
     cu_t = None if cu is None else torch.tensor(cu, dtype=torch.int32, device="cuda")
-    check_bwd(q, k, v, do, P, rank, scale, causal, cu_t, layout)
+    dq, dk, dv = check_bwd(q, k, v, do, P, rank, scale, causal, cu_t, layout)
+    host = [to_f64(t) for t in (q, k, v, do)]
+    ref = oracle_bwd(("bwd", P, rank, n, bs, hq, hkv, hd, causal, str(cu)), host, P, rank, scale,
+                     causal, cu)
+    assert_grads_close("bf16", rank_slice(dq, P, rank), rank_slice(dk, P, rank),
+                       rank_slice(dv, P, rank), ref, "fused, against the oracle")
 
 
 @pytest.mark.parametrize("layout", LAYOUTS)
 def test_fused_bwd_full_size_llama8b_128k(layout):
     """The benchmark's shape: P = 8 chunks of 16384 tokens, 32 q / 8 kv heads, rank 3."""
-    import torch
-    P, rank, n, hq, hkv, hd = 8, 3, 16384, 32, 8, 128
-    N = P * n
-    gen = torch.Generator(device="cuda")
-    gen.manual_seed(5252)
-    q = (torch.randn((N, 1, hq, hd), device="cuda", generator=gen) / np.sqrt(hd)).to(torch.bfloat16)
-    k = torch.randn((N, 1, hkv, hd), device="cuda", generator=gen).to(torch.bfloat16)
-    v = torch.randn((N, 1, hkv, hd), device="cuda", generator=gen).to(torch.bfloat16)
-    do = torch.randn((N, 1, hq, hd), device="cuda", generator=gen).to(torch.bfloat16)
-    check_bwd(q, k, v, do, P, rank, 1.0, True, None, layout)
+    w = synth.WORKLOADS["llama8b-share-128k"]
+    P, rank, N = w.P, w.rank, w.seqlen
+    q, k, v, do = (to_device(w.seq_tensor(st, heads, scale), "bf16")
+                   for st, heads, scale in ((synth.STREAM_Q, w.hq, w.q_prescale),
+                                            (synth.STREAM_K, w.hkv, 1.0),
+                                            (synth.STREAM_V, w.hkv, 1.0),
+                                            (synth.STREAM_DO, w.hq, 1.0)))
+    dq, dk, dv = check_bwd(q, k, v, do, P, rank, w.softmax_scale, True, None, layout)
+    # dQ on sampled rows, dK/dV on the last 256 keys (whose visible queries the
+    # oracle can afford)
+    rows = sample_rows(N, w.seed, n_first=32, n_last=32, n_rand=32)
+    cols = np.arange(N - 256, N, dtype=np.int64)
+    host = head_slices((q, k, v, do), P, rank) if ("bwd128k",) not in _ORACLE_CACHE else None
+    ref = oracle_bwd(("bwd128k",), host, P, rank, w.softmax_scale, True, None, rows=rows, cols=cols,
+                     sliced=True)
+    assert_grads_close("bf16", rank_slice(dq, P, rank, rows), rank_slice(dk, P, rank, cols),
+                       rank_slice(dv, P, rank, cols), ref, "fused, 128K, against the oracle")
