@@ -5,6 +5,11 @@ Thin ctypes marshalling over the C-ABI declared in ``include/ulysses.h``:
 each function below has the name of the C entry point it calls, takes torch
 device tensors, passes their data pointers, sizes and the current HIP stream,
 and raises :class:`UlyssesError` when the library returns a non-OK status.
+Before any call it checks every tensor argument -- on the current GPU,
+contiguous, of exactly the shape the entry point reads or writes and of a
+consistent element type -- and raises ``ValueError`` otherwise, because the
+library sees only pointers and sizes: a view, an undersized buffer or a host
+tensor would make its kernels access memory they do not own.
 All computation happens in the library's HIP kernels; torch only supplies
 device memory and the stream.  The library must have been built
 (``ulysses_sp_attention_amd._build.build_lib()``); importing the binding
@@ -127,6 +132,73 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+def _device_ok(t) -> bool:
+    """t lives on the GPU the library launches on (the current device)."""
+    import torch
+    return t.device.type == "cuda" and t.device.index == torch.cuda.current_device()
+
+
+def _need(name: str, t, shape, dtype=None) -> None:
+    """Raise ValueError unless t is a contiguous tensor on the current GPU with
+    exactly `shape` (and element type `dtype`, when given)."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name}: expected a torch tensor, got {type(t).__name__}")
+    if tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(int(x) for x in shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if not _device_ok(t):
+        raise ValueError(f"{name}: must be on the current GPU (got {t.device})")
+
+
+def _need_4d(name: str, t) -> tuple:
+    """A contiguous [seq, bs, heads, head_dim] GPU tensor; returns its shape."""
+    import torch
+    if not isinstance(t, torch.Tensor) or t.dim() != 4:
+        raise ValueError(f"{name}: expected a 4-D [seq, bs, heads, head_dim] tensor")
+    _need(name, t, t.shape)
+    return tuple(t.shape)
+
+
+def _need_chunks(name: str, chunks, heads=None, dtype=None) -> tuple:
+    """P alike contiguous chunks [n_local, bs, heads, head_dim]; returns
+    (P, n_local, bs, heads, head_dim)."""
+    if not isinstance(chunks, (list, tuple)) or len(chunks) == 0:
+        raise ValueError(f"{name}: expected a non-empty list of chunk tensors")
+    n, bs, h, hd = _need_4d(f"{name}[0]", chunks[0])
+    if heads is not None and h != heads:
+        raise ValueError(f"{name}: {h} heads per chunk, expected {heads}")
+    dt = chunks[0].dtype if dtype is None else dtype
+    for i, c in enumerate(chunks):
+        _need(f"{name}[{i}]", c, (n, bs, h, hd), dt)
+    return len(chunks), n, bs, h, hd
+
+
+def _need_workspace(t) -> None:
+    if t is None:
+        return   # the library reports ERR_NULL / ERR_WORKSPACE
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise ValueError("workspace: expected a torch tensor")
+    _need("workspace", t, t.shape)
+
+
+def _need_cu(cu_seqlens) -> None:
+    if cu_seqlens is None:
+        return
+    import torch
+    if not isinstance(cu_seqlens, torch.Tensor) or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens: expected a 1-D tensor of n_docs + 1 >= 2 offsets")
+    _need("cu_seqlens", cu_seqlens, cu_seqlens.shape, torch.int32)
+
+
+def _local_heads(heads: int, P: int) -> int:
+    return heads // P if heads >= P else 1
+
+
 def _stream(stream):
     if stream is not None:
         return stream if isinstance(stream, int) else stream.cuda_stream
@@ -151,7 +223,8 @@ def ulysses_status_string(status: int) -> str:
 
 def ulysses_seq_to_head(chunks, rank: int, out, stream=None) -> None:
     """chunks: P tensors [n_local, bs, heads, head_dim]; out: [P*n_local, bs, heads_l, head_dim]."""
-    n, bs, heads, hd = chunks[0].shape
+    P, n, bs, heads, hd = _need_chunks("chunks", chunks)
+    _need("out", out, (P * n, bs, _local_heads(heads, P), hd), chunks[0].dtype)
     st = load_library().ulysses_seq_to_head(
         _ptr_array(chunks), len(chunks), rank, n, bs, heads, hd, _dtype_code(chunks[0]), _ptr(out),
         _stream(stream))
@@ -160,7 +233,8 @@ def ulysses_seq_to_head(chunks, rank: int, out, stream=None) -> None:
 
 def ulysses_head_to_seq(inp, rank: int, chunks, stream=None) -> None:
     """inp: [P*n_local, bs, heads/P, head_dim]; writes rank's head slots of the P chunks."""
-    n, bs, heads, hd = chunks[0].shape
+    P, n, bs, heads, hd = _need_chunks("chunks", chunks)
+    _need("inp", inp, (P * n, bs, heads // P, hd), chunks[0].dtype)
     st = load_library().ulysses_head_to_seq(
         _ptr(inp), len(chunks), rank, n, bs, heads, hd, _dtype_code(inp), _ptr_array(chunks),
         _stream(stream))
@@ -169,15 +243,16 @@ def ulysses_head_to_seq(inp, rank: int, chunks, stream=None) -> None:
 
 def _batch_descs(pairs):
     """[(chunks, head_tensor)] -> ctypes array of ExchangeTensor (+ keep-alive list)."""
+    if not isinstance(pairs, (list, tuple)) or not pairs:
+        raise ValueError("batched exchange: expected a non-empty list of (chunks, head) pairs")
+    P, n, bs, _, hd = _need_chunks("pairs[0] chunks", pairs[0][0])
+    for i, (chunks, head) in enumerate(pairs):
+        Pi, ni, bsi, hi, hdi = _need_chunks(f"pairs[{i}] chunks", chunks, dtype=pairs[0][0][0].dtype)
+        if (Pi, ni, bsi, hdi) != (P, n, bs, hd):
+            raise ValueError("batched exchange: tensors differ in P, n_local, bs or head_dim")
+        _need(f"pairs[{i}] head", head, (P * n, bs, _local_heads(hi, P), hd), chunks[0].dtype)
     descs = (ExchangeTensor * len(pairs))()
     keep = []
-    n, bs, _, hd = pairs[0][0][0].shape
-    for chunks, head in pairs:
-        # the library takes one (P, n_local, bs, head_dim, dtype) for the whole batch
-        if len(chunks) != len(pairs[0][0]) or head.dtype != pairs[0][1].dtype or any(
-                (c.shape[0], c.shape[1], c.shape[3]) != (n, bs, hd) or c.dtype != head.dtype
-                for c in chunks):
-            raise ValueError("batched exchange: tensors differ in P, n_local, bs, head_dim or dtype")
     for i, (chunks, head) in enumerate(pairs):
         arr = _ptr_array(chunks)
         keep.append(arr)
@@ -190,8 +265,8 @@ def _batch_descs(pairs):
 def ulysses_seq_to_head_batch(pairs, rank: int, stream=None) -> None:
     """pairs: up to MAX_BATCH (chunks, out) as for ulysses_seq_to_head, moved in one launch.
     All tensors share P, n_local, bs, head_dim and dtype; head counts may differ."""
-    n, bs, _, hd = pairs[0][0][0].shape
     descs, keep = _batch_descs(pairs)
+    n, bs, _, hd = pairs[0][0][0].shape
     st = load_library().ulysses_seq_to_head_batch(
         descs, len(pairs), len(pairs[0][0]), rank, n, bs, hd, _dtype_code(pairs[0][0][0]),
         _stream(stream))
@@ -201,8 +276,10 @@ def ulysses_seq_to_head_batch(pairs, rank: int, stream=None) -> None:
 
 def ulysses_head_to_seq_batch(pairs, rank: int, stream=None) -> None:
     """pairs: up to MAX_BATCH (inp, chunks) as for ulysses_head_to_seq, moved in one launch."""
-    n, bs, _, hd = pairs[0][1][0].shape
+    if not isinstance(pairs, (list, tuple)) or not pairs:
+        raise ValueError("batched exchange: expected a non-empty list of (inp, chunks) pairs")
     descs, keep = _batch_descs([(chunks, inp) for inp, chunks in pairs])
+    n, bs, _, hd = pairs[0][1][0].shape
     st = load_library().ulysses_head_to_seq_batch(
         descs, len(pairs), len(pairs[0][1]), rank, n, bs, hd, _dtype_code(pairs[0][0]),
         _stream(stream))
@@ -214,8 +291,14 @@ def ulysses_attn_fwd(q, k, v, o, lse, softmax_scale: float, causal: bool = True,
                      cu_seqlens=None, stream=None) -> None:
     """q, o: [N, bs, hq, hd]; k, v: [N, bs, hkv, hd]; lse: fp32 [bs, hq, N];
     cu_seqlens: optional device int32 [n_docs + 1]."""
-    N, bs, hq, hd = q.shape
-    hkv = k.shape[2]
+    import torch
+    N, bs, hq, hd = _need_4d("q", q)
+    hkv = _need_4d("k", k)[2]
+    _need("k", k, (N, bs, hkv, hd), q.dtype)
+    _need("v", v, (N, bs, hkv, hd), q.dtype)
+    _need("o", o, (N, bs, hq, hd), q.dtype)
+    _need("lse", lse, (bs, hq, N), torch.float32)
+    _need_cu(cu_seqlens)
     n_docs = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
     st = load_library().ulysses_attn_fwd(
         _ptr(q), _ptr(k), _ptr(v), N, bs, hq, hkv, hd, _dtype_code(q), softmax_scale, int(causal),
@@ -232,8 +315,15 @@ def ulysses_attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, softmax_scale
                      causal: bool = True, cu_seqlens=None, stream=None) -> None:
     """Gradients of ulysses_attn_fwd.  workspace: device tensor of at least
     ulysses_attn_bwd_workspace_size(...) bytes."""
-    N, bs, hq, hd = q.shape
-    hkv = k.shape[2]
+    import torch
+    N, bs, hq, hd = _need_4d("q", q)
+    hkv = _need_4d("k", k)[2]
+    for name, t, h in (("k", k, hkv), ("v", v, hkv), ("o", o, hq), ("dout", dout, hq),
+                       ("dq", dq, hq), ("dk", dk, hkv), ("dv", dv, hkv)):
+        _need(name, t, (N, bs, h, hd), q.dtype)
+    _need("lse", lse, (bs, hq, N), torch.float32)
+    _need_cu(cu_seqlens)
+    _need_workspace(workspace)
     n_docs = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = load_library().ulysses_attn_bwd(
@@ -247,7 +337,12 @@ def ulysses_attn_merge(o_a, lse_a, o_b, lse_b, o, lse, stream=None) -> None:
     """Merge of two partial attention results over disjoint key sets.
     o_a, o_b, o: [N, bs, heads, hd]; lse_a, lse_b, lse: fp32 [bs, heads, N].
     o may be o_a or o_b and lse may be lse_a or lse_b (in place)."""
-    N, bs, heads, hd = o_a.shape
+    import torch
+    N, bs, heads, hd = _need_4d("o_a", o_a)
+    _need("o_b", o_b, (N, bs, heads, hd), o_a.dtype)
+    _need("o", o, (N, bs, heads, hd), o_a.dtype)
+    for name, t in (("lse_a", lse_a), ("lse_b", lse_b), ("lse", lse)):
+        _need(name, t, (bs, heads, N), torch.float32)
     st = load_library().ulysses_attn_merge(
         _ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b), N, bs, heads, hd, _dtype_code(o_a),
         _ptr(o), _ptr(lse), _stream(stream))
@@ -261,8 +356,17 @@ def ulysses_attn_fwd_fused(q_chunks, k_chunks, v_chunks, o_chunks, lse, rank: in
     [n_local, bs, hq, hd] (all heads), k_chunks, v_chunks P tensors
     [n_local, bs, hkv, hd]; lse: fp32 [bs, hq/P, P*n_local].  Writes only this
     rank's head slots of o_chunks."""
-    n, bs, hq, hd = q_chunks[0].shape
-    hkv = k_chunks[0].shape[2]
+    import torch
+    P, n, bs, hq, hd = _need_chunks("q_chunks", q_chunks)
+    hkv = _need_chunks("k_chunks", k_chunks, dtype=q_chunks[0].dtype)[3]
+    for name, chunks, h in (("k_chunks", k_chunks, hkv), ("v_chunks", v_chunks, hkv),
+                            ("o_chunks", o_chunks, hq)):
+        if _need_chunks(name, chunks, h, q_chunks[0].dtype)[:3] != (P, n, bs) or \
+                chunks[0].shape[3] != hd:
+            raise ValueError(f"{name}: chunks differ from q_chunks in P, n_local, bs or head_dim")
+    if hq % P == 0:   # otherwise the library reports ERR_DIVISIBILITY
+        _need("lse", lse, (bs, hq // P, P * n), torch.float32)
+    _need_cu(cu_seqlens)
     n_docs = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
     st = load_library().ulysses_attn_fwd_fused(
         _ptr_array(q_chunks), _ptr_array(k_chunks), _ptr_array(v_chunks), len(q_chunks), rank, n,
@@ -279,8 +383,20 @@ def ulysses_attn_bwd_fused(q_chunks, k_chunks, v_chunks, o_chunks, lse, do_chunk
     dv); lse: fp32 [bs, hq/P, P*n_local] from ulysses_attn_fwd_fused;
     workspace as for ulysses_attn_bwd at the rank's head counts.  Writes only
     this rank's head slots of dq_chunks, dk_chunks and dv_chunks."""
-    n, bs, hq, hd = q_chunks[0].shape
-    hkv = k_chunks[0].shape[2]
+    import torch
+    P, n, bs, hq, hd = _need_chunks("q_chunks", q_chunks)
+    hkv = _need_chunks("k_chunks", k_chunks, dtype=q_chunks[0].dtype)[3]
+    for name, chunks, h in (("k_chunks", k_chunks, hkv), ("v_chunks", v_chunks, hkv),
+                            ("o_chunks", o_chunks, hq), ("do_chunks", do_chunks, hq),
+                            ("dq_chunks", dq_chunks, hq), ("dk_chunks", dk_chunks, hkv),
+                            ("dv_chunks", dv_chunks, hkv)):
+        if _need_chunks(name, chunks, h, q_chunks[0].dtype)[:3] != (P, n, bs) or \
+                chunks[0].shape[3] != hd:
+            raise ValueError(f"{name}: chunks differ from q_chunks in P, n_local, bs or head_dim")
+    if hq % P == 0:
+        _need("lse", lse, (bs, hq // P, P * n), torch.float32)
+    _need_cu(cu_seqlens)
+    _need_workspace(workspace)
     n_docs = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = load_library().ulysses_attn_bwd_fused(
@@ -306,8 +422,21 @@ def ulysses_logits_loss(h, w, labels, loss_rows, loss_sum, n_good, dh, dw, works
     h: bf16 [T, d]; w: bf16 [V, d]; labels: int64 [T]; loss_rows: fp32 [T];
     loss_sum: fp32 [1]; n_good: int64 [1]; dh: bf16 [T, d]; dw: fp32 [V, d];
     workspace: at least ulysses_logits_loss_workspace_size(min(shard_rows, T), V) bytes."""
+    import torch
+    if not isinstance(h, torch.Tensor) or h.dim() != 2 or not isinstance(w, torch.Tensor) or \
+            w.dim() != 2:
+        raise ValueError("h and w must be 2-D tensors [T, d] and [V, d]")
     T, d = h.shape
     V = w.shape[0]
+    _need("h", h, (T, d))
+    _need("w", w, (V, d), h.dtype)
+    _need("labels", labels, (T,), torch.int64)
+    _need("loss_rows", loss_rows, (T,), torch.float32)
+    _need("loss_sum", loss_sum, (1,), torch.float32)
+    _need("n_good", n_good, (1,), torch.int64)
+    _need("dh", dh, (T, d), h.dtype)
+    _need("dw", dw, (V, d), torch.float32)
+    _need_workspace(workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = load_library().ulysses_logits_loss(
         _ptr(h), _ptr(w), _ptr(labels), T, d, V, _dtype_code(h), ignore_index, grad_scale,
@@ -320,6 +449,20 @@ def ulysses_tiled_mlp_workspace_size(shard_rows: int, d: int, inter: int, backwa
     return int(load_library().ulysses_tiled_mlp_workspace_size(shard_rows, d, inter, int(backward)))
 
 
+def _need_mlp(x, wg, wu, wd):
+    import torch
+    if not isinstance(x, torch.Tensor) or x.dim() != 2 or not isinstance(wg, torch.Tensor) or \
+            wg.dim() != 2:
+        raise ValueError("x and wg must be 2-D tensors [T, d] and [I, d]")
+    T, d = x.shape
+    inter = wg.shape[0]
+    _need("x", x, (T, d))
+    _need("wg", wg, (inter, d), x.dtype)
+    _need("wu", wu, (inter, d), x.dtype)
+    _need("wd", wd, (d, inter), x.dtype)
+    return T, d, inter
+
+
 def _nbytes(t):
     return 0 if t is None else t.numel() * t.element_size()
 
@@ -328,8 +471,9 @@ def ulysses_tiled_mlp_fwd(x, wg, wu, wd, y, workspace, shard_rows=None, stream=N
     """y = (silu(x Wg^T) * (x Wu^T)) Wd^T, shard_rows rows at a time (default
     d, the guide's ceil(T / d) shards).  x, y: bf16 [T, d]; wg, wu: [I, d];
     wd: [d, I]."""
-    T, d = x.shape
-    inter = wg.shape[0]
+    T, d, inter = _need_mlp(x, wg, wu, wd)
+    _need("y", y, (T, d), x.dtype)
+    _need_workspace(workspace)
     st = load_library().ulysses_tiled_mlp_fwd(
         _ptr(x), _ptr(wg), _ptr(wu), _ptr(wd), T, d, inter, _dtype_code(x),
         d if shard_rows is None else shard_rows, _ptr(y), _ptr(workspace), _nbytes(workspace),
@@ -341,8 +485,14 @@ def ulysses_tiled_mlp_bwd(x, wg, wu, wd, dy, dx, dwg, dwu, dwd, workspace, shard
                           stream=None) -> None:
     """Gradients of ulysses_tiled_mlp_fwd for dy (bf16 [T, d]): dx bf16 [T, d];
     dwg, dwu fp32 [I, d]; dwd fp32 [d, I]."""
-    T, d = x.shape
-    inter = wg.shape[0]
+    import torch
+    T, d, inter = _need_mlp(x, wg, wu, wd)
+    _need("dy", dy, (T, d), x.dtype)
+    _need("dx", dx, (T, d), x.dtype)
+    _need("dwg", dwg, (inter, d), torch.float32)
+    _need("dwu", dwu, (inter, d), torch.float32)
+    _need("dwd", dwd, (d, inter), torch.float32)
+    _need_workspace(workspace)
     st = load_library().ulysses_tiled_mlp_bwd(
         _ptr(x), _ptr(wg), _ptr(wu), _ptr(wd), _ptr(dy), T, d, inter, _dtype_code(x),
         d if shard_rows is None else shard_rows, _ptr(dx), _ptr(dwg), _ptr(dwu), _ptr(dwd),
