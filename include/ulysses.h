@@ -19,14 +19,30 @@
  *   ulysses_attn_fwd     -- causal (GQA, optionally document-masked)
  *                           softmax attention, returning O and the LSE
  *   ulysses_attn_bwd     -- its backward pass (dQ, dK, dV)
+ *   ulysses_attn_fwd_fused, ulysses_attn_bwd_fused
+ *                        -- the same with the exchange fused into the
+ *                           attention kernels' addressing
+ *   ulysses_attn_merge   -- merge of two partial results (ring / blockwise
+ *                           attention step)
+ *   ulysses_logits_loss, ulysses_tiled_mlp_fwd/bwd
+ *                        -- the sequence-tiled language-model loss and
+ *                           SwiGLU MLP of the ALST memory recipe
  *
  * Tensor layout is the pages' [sl, bs, hc, hs] (sequence, batch, heads, head
  * size), contiguous row-major (DeepSpeed Ulysses SP + ALST integration guide,
  * zwxr.cn, section on the attention adapter).
  *
  * Conventions for every entry point:
- *  - Device buffers are owned by the caller.  The library never allocates or
- *    frees memory and keeps no mutable global state; calls are re-entrant.
+ *  - Device buffers are owned by the caller; scratch memory comes from a
+ *    caller-provided workspace.  Library state and allocation, precisely:
+ *      * the exchange, attention (forward, backward, fused) and merge calls
+ *        allocate and free nothing and keep no state between calls;
+ *      * ulysses_logits_loss and ulysses_tiled_mlp_fwd/bwd run their plain
+ *        GEMMs through rocBLAS on a handle the library creates on the first
+ *        such call of each host thread on each device and keeps until the
+ *        process ends; rocBLAS may allocate device memory of its own inside
+ *        that handle (on creation or on the first GEMM of a shape);
+ *    Calls are re-entrant: different host threads may call concurrently.
  *  - Calls are asynchronous: they validate their arguments on the host,
  *    enqueue kernels on `stream` and return.  Inputs must stay valid until
  *    the stream work completes.  A NULL stream is the default stream.
@@ -213,13 +229,19 @@ ulysses_status_t ulysses_attn_fwd_fused(const void* const* q_chunks, const void*
                                         const int32_t* cu_seqlens, int n_docs,
                                         void* const* o_chunks, float* lse, hipStream_t stream);
 
-/* Bytes of device workspace ulysses_attn_bwd needs for these sizes. */
+/* Bytes of device workspace ulysses_attn_bwd needs for these sizes (the
+ * per-row statistics of the backward below; 0 for sizes it rejects). */
 size_t ulysses_attn_bwd_workspace_size(int64_t seqlen, int bs, int hq, int hkv, int head_dim,
                                        ulysses_dtype_t dtype);
 
 /*
- * Backward pass of ulysses_attn_fwd: given O and LSE from the forward call
- * and the upstream gradient dO (same layout as O), computes
+ * Backward pass of ulysses_attn_fwd, which training runs through every
+ * Ulysses attention layer (integration guide, the training-loop example:
+ * the loss aggregated over the ranks is backpropagated through the model;
+ * the gradients cross the two all-to-alls in the opposite direction, so on
+ * one rank the backward of the local attention is this call).  Given O and
+ * LSE from the forward call and the upstream gradient dO (same layout as
+ * O), computes
  *   D_i = <dO_i, O_i>,  P_ij = exp(s_ij - LSE_i),  dS_ij = P_ij (<dO_i, v_j> - D_i)
  *   dQ_i = scale * sum_j dS_ij k_j
  *   dK_j = scale * sum_{h in group(j)} sum_i dS_ij q_i
