@@ -27,6 +27,9 @@
  *   ulysses_logits_loss, ulysses_tiled_mlp_fwd/bwd
  *                        -- the sequence-tiled language-model loss and
  *                           SwiGLU MLP of the ALST memory recipe
+ *   ulysses_attn_bwd_noalloc
+ *                        -- ulysses_attn_bwd for callers that cannot
+ *                           allocate
  *
  * Tensor layout is the pages' [sl, bs, hc, hs] (sequence, batch, heads, head
  * size), contiguous row-major (DeepSpeed Ulysses SP + ALST integration guide,
@@ -42,7 +45,12 @@
  *        such call of each host thread on each device and keeps until the
  *        process ends; rocBLAS may allocate device memory of its own inside
  *        that handle (on creation or on the first GEMM of a shape);
- *    Calls are re-entrant: different host threads may call concurrently.
+ *      * ulysses_attn_bwd_noalloc uses a fixed device array that every GPU
+ *        the library runs on holds until the process ends, and caches that
+ *        array's address per device (a mutex guards the cache).
+ *    Calls are re-entrant: different host threads may call concurrently,
+ *    except that concurrent ulysses_attn_bwd_noalloc calls on one GPU race
+ *    on its shared array.
  *  - Calls are asynchronous: they validate their arguments on the host,
  *    enqueue kernels on `stream` and return.  Inputs must stay valid until
  *    the stream work completes.  A NULL stream is the default stream.
@@ -66,7 +74,7 @@
 extern "C" {
 #endif
 
-#define ULYSSES_ABI_VERSION 6
+#define ULYSSES_ABI_VERSION 7
 
 typedef enum {
   ULYSSES_OK = 0,
@@ -258,6 +266,32 @@ ulysses_status_t ulysses_attn_bwd(const void* q, const void* k, const void* v, c
                                   float softmax_scale, int causal, const int32_t* cu_seqlens,
                                   int n_docs, void* dq, void* dk, void* dv, void* workspace,
                                   size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * ulysses_attn_bwd for callers that cannot allocate memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  It
+ * takes no workspace; the backward's per-row statistics live instead in a
+ * fixed scratch array of ULYSSES_NOALLOC_SCRATCH_BYTES that the library
+ * holds on every GPU it runs on until the process ends.  The call itself
+ * allocates and frees nothing.
+ *   Arguments, results and errors as in ulysses_attn_bwd, plus
+ *   ULYSSES_ERR_WORKSPACE when ulysses_attn_bwd_workspace_size(...) of these
+ *   sizes exceeds ULYSSES_NOALLOC_SCRATCH_BYTES (bf16: seqlen * bs * hq up
+ *   to 2^21 rows; fp32: 2^22), with nothing launched.
+ * All calls on one GPU share its scratch array: calls that overlap in time
+ * on one GPU (several streams or host threads) race and give wrong results;
+ * calls ordered on one stream are safe.  The array's contents left by one
+ * call do not matter to the next (every statistic is written before it is
+ * read).  ULYSSES_ERR_HIP also when the scratch address cannot be obtained.
+ */
+#define ULYSSES_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+ulysses_status_t ulysses_attn_bwd_noalloc(const void* q, const void* k, const void* v,
+                                          const void* o, const float* lse, const void* dout,
+                                          int64_t seqlen, int bs, int hq, int hkv, int head_dim,
+                                          ulysses_dtype_t dtype, float softmax_scale, int causal,
+                                          const int32_t* cu_seqlens, int n_docs, void* dq,
+                                          void* dk, void* dv, hipStream_t stream);
 
 /*
  * ulysses_attn_bwd with the layout exchange fused in, the backward of

@@ -368,3 +368,20 @@ def test_tiled_mlp_bwd_validation(lib, kw, want):
 
 def test_tiled_mlp_fwd_empty_is_a_no_op(lib):
     assert mlp_call(lib, False, T=0, x=None, y=None, ws=None) == uly.OK
+
+
+def test_attn_bwd_noalloc_validation(lib):
+    """The entry point without a workspace checks like ulysses_attn_bwd and
+    refuses sizes whose statistics exceed its fixed scratch, before any HIP
+    call; an empty sequence is a no-op that never looks the scratch up."""
+    limit_rows = uly.NOALLOC_SCRATCH_BYTES // 8   # bf16: 2 fp32 statistics per row
+
+    def call(N, hq=4, hkv=1, dtype=uly.BF16, ptr=FAKE, hd=128):
+        return lib.ulysses_attn_bwd_noalloc(ptr, FAKE, FAKE, FAKE, FAKE, FAKE, N, 1, hq, hkv, hd,
+                                            dtype, 0.088, 1, None, 0, FAKE, FAKE, FAKE, None)
+    assert call(limit_rows // 4 + 64) == uly.ERR_WORKSPACE
+    assert call(2 * limit_rows // 4 + 64, dtype=uly.FP32) == uly.ERR_WORKSPACE   # one statistic
+    assert call(64, ptr=None) == uly.ERR_NULL
+    assert call(64, ptr=MISALIGNED) == uly.ERR_ALIGNMENT
+    assert call(64, hq=6, hkv=4) == uly.ERR_DIVISIBILITY
+    assert call(0) == uly.OK

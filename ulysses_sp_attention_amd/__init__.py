@@ -26,7 +26,7 @@ LIB_PATH = os.path.join(_PKG, "libulysses.so")
 OK, ERR_NULL, ERR_SHAPE, ERR_DIVISIBILITY, ERR_DTYPE, ERR_ALIGNMENT, ERR_UNSUPPORTED, \
     ERR_WORKSPACE, ERR_HIP = range(9)
 BF16, FP32 = 0, 1
-ABI_VERSION = 6   # ULYSSES_ABI_VERSION this binding is written for
+ABI_VERSION = 7   # ULYSSES_ABI_VERSION this binding is written for
 _INVALID_DTYPE = 99
 
 # Every symbol include/ulysses.h declares.
@@ -34,11 +34,13 @@ EXPORTED_SYMBOLS = (
     "ulysses_abi_version", "ulysses_status_string", "ulysses_seq_to_head", "ulysses_head_to_seq",
     "ulysses_seq_to_head_batch", "ulysses_head_to_seq_batch",
     "ulysses_attn_fwd", "ulysses_attn_bwd_workspace_size", "ulysses_attn_bwd",
+    "ulysses_attn_bwd_noalloc",
     "ulysses_attn_merge", "ulysses_attn_fwd_fused", "ulysses_attn_bwd_fused",
     "ulysses_logits_loss_workspace_size", "ulysses_logits_loss",
     "ulysses_tiled_mlp_workspace_size", "ulysses_tiled_mlp_fwd", "ulysses_tiled_mlp_bwd",
 )
 MAX_BATCH = 4   # ULYSSES_MAX_BATCH
+NOALLOC_SCRATCH_BYTES = 16 << 20   # ULYSSES_NOALLOC_SCRATCH_BYTES
 
 
 class ExchangeTensor(ctypes.Structure):
@@ -90,6 +92,9 @@ def load_library(path: str = LIB_PATH):
     lib.ulysses_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, ci, ci, ci, ci, ci, f32, ci, vp, ci,
                                      vp, vp, vp, vp, sz, vp]
     lib.ulysses_attn_bwd.restype = ci
+    lib.ulysses_attn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i64, ci, ci, ci, ci, ci, f32, ci,
+                                             vp, ci, vp, vp, vp, vp]
+    lib.ulysses_attn_bwd_noalloc.restype = ci
     lib.ulysses_attn_merge.argtypes = [vp, vp, vp, vp, i64, ci, ci, ci, ci, vp, vp, vp]
     lib.ulysses_attn_merge.restype = ci
     lib.ulysses_attn_fwd_fused.argtypes = [vp, vp, vp, ci, ci, i64, ci, ci, ci, ci, ci, f32, ci, vp,
@@ -331,6 +336,27 @@ def ulysses_attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, softmax_scale
         _dtype_code(q), softmax_scale, int(causal), _ptr(cu_seqlens), n_docs, _ptr(dq), _ptr(dk),
         _ptr(dv), _ptr(workspace), ws_bytes, _stream(stream))
     _check("ulysses_attn_bwd", st)
+
+
+def ulysses_attn_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, softmax_scale: float,
+                             causal: bool = True, cu_seqlens=None, stream=None) -> None:
+    """ulysses_attn_bwd without a workspace: the statistics go to the
+    library's fixed per-GPU scratch (NOALLOC_SCRATCH_BYTES), so the call
+    allocates nothing.  Calls overlapping in time on one GPU race."""
+    import torch
+    N, bs, hq, hd = _need_4d("q", q)
+    hkv = _need_4d("k", k)[2]
+    for name, t, h in (("k", k, hkv), ("v", v, hkv), ("o", o, hq), ("dout", dout, hq),
+                       ("dq", dq, hq), ("dk", dk, hkv), ("dv", dv, hkv)):
+        _need(name, t, (N, bs, h, hd), q.dtype)
+    _need("lse", lse, (bs, hq, N), torch.float32)
+    _need_cu(cu_seqlens)
+    n_docs = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
+    st = load_library().ulysses_attn_bwd_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), N, bs, hq, hkv, hd,
+        _dtype_code(q), softmax_scale, int(causal), _ptr(cu_seqlens), n_docs, _ptr(dq), _ptr(dk),
+        _ptr(dv), _stream(stream))
+    _check("ulysses_attn_bwd_noalloc", st)
 
 
 def ulysses_attn_merge(o_a, lse_a, o_b, lse_b, o, lse, stream=None) -> None:

@@ -12,7 +12,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libulysses.so")
 SOURCES = ["api.cpp", "exchange.hip", "attn_fwd.hip", "attn_f32.hip", "attn_bwd.hip", "attn_merge.hip",
-           "logits_loss.hip", "tiled_mlp.hip"]
+           "logits_loss.hip", "tiled_mlp.hip", "noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -254,26 +254,32 @@ size_t ulysses_attn_bwd_workspace_size(int64_t seqlen, int bs, int hq, int hkv, 
   return ulysses::attn_bwd_workspace_bytes(s, dtype == ULYSSES_BF16);
 }
 
-ulysses_status_t ulysses_attn_bwd(const void* q, const void* k, const void* v, const void* o,
-                                  const float* lse, const void* dout, int64_t seqlen, int bs,
-                                  int hq, int hkv, int head_dim, ulysses_dtype_t dtype,
-                                  float softmax_scale, int causal, const int32_t* cu_seqlens,
-                                  int n_docs, void* dq, void* dk, void* dv, void* workspace,
-                                  size_t workspace_bytes, hipStream_t stream) {
+namespace {
+
+// Argument checks shared by ulysses_attn_bwd and ulysses_attn_bwd_noalloc
+// (everything but the workspace); fills *s.
+ulysses_status_t check_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                                const float* lse, const void* dout, int64_t seqlen, int bs, int hq,
+                                int hkv, int head_dim, ulysses_dtype_t dtype, float softmax_scale,
+                                int causal, const int32_t* cu_seqlens, int n_docs, const void* dq,
+                                const void* dk, const void* dv, AttnShape* s) {
   if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || lse == nullptr ||
       dout == nullptr || dq == nullptr || dk == nullptr || dv == nullptr)
     return ULYSSES_ERR_NULL;
-  AttnShape s;
   ulysses_status_t st = check_attn(seqlen, bs, hq, hkv, head_dim, dtype, softmax_scale, causal,
-                                   cu_seqlens, n_docs, &s);
+                                   cu_seqlens, n_docs, s);
   if (st != ULYSSES_OK) return st;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
       !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned4(lse))
     return ULYSSES_ERR_ALIGNMENT;
-  const size_t need = ulysses::attn_bwd_workspace_bytes(s, dtype == ULYSSES_BF16);
-  if (seqlen > 0 && (workspace == nullptr || workspace_bytes < need)) return ULYSSES_ERR_WORKSPACE;
-  if (seqlen > 0 && !aligned16(workspace)) return ULYSSES_ERR_ALIGNMENT;
-  if (seqlen == 0) return ULYSSES_OK;
+  return ULYSSES_OK;
+}
+
+// The backward's launches, with a workspace that has passed its checks.
+ulysses_status_t attn_bwd_launch(const AttnShape& s, ulysses_dtype_t dtype, const void* q,
+                                 const void* k, const void* v, const void* o, const float* lse,
+                                 const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                                 hipStream_t stream) {
   if (dtype == ULYSSES_BF16)
     return from_hip(ulysses::launch_attn_bwd_bf16(s, q, k, v, o, lse, dout, dq, dk, dv, workspace,
                                                   stream));
@@ -281,6 +287,43 @@ ulysses_status_t ulysses_attn_bwd(const void* q, const void* k, const void* v, c
       s, static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
       static_cast<const float*>(o), lse, static_cast<const float*>(dout), static_cast<float*>(dq),
       static_cast<float*>(dk), static_cast<float*>(dv), workspace, stream));
+}
+
+}  // namespace
+
+ulysses_status_t ulysses_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                                  const float* lse, const void* dout, int64_t seqlen, int bs,
+                                  int hq, int hkv, int head_dim, ulysses_dtype_t dtype,
+                                  float softmax_scale, int causal, const int32_t* cu_seqlens,
+                                  int n_docs, void* dq, void* dk, void* dv, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+  AttnShape s;
+  ulysses_status_t st = check_attn_bwd(q, k, v, o, lse, dout, seqlen, bs, hq, hkv, head_dim, dtype,
+                                       softmax_scale, causal, cu_seqlens, n_docs, dq, dk, dv, &s);
+  if (st != ULYSSES_OK) return st;
+  const size_t need = ulysses::attn_bwd_workspace_bytes(s, dtype == ULYSSES_BF16);
+  if (seqlen > 0 && (workspace == nullptr || workspace_bytes < need)) return ULYSSES_ERR_WORKSPACE;
+  if (seqlen > 0 && !aligned16(workspace)) return ULYSSES_ERR_ALIGNMENT;
+  if (seqlen == 0) return ULYSSES_OK;
+  return attn_bwd_launch(s, dtype, q, k, v, o, lse, dout, dq, dk, dv, workspace, stream);
+}
+
+ulysses_status_t ulysses_attn_bwd_noalloc(const void* q, const void* k, const void* v,
+                                          const void* o, const float* lse, const void* dout,
+                                          int64_t seqlen, int bs, int hq, int hkv, int head_dim,
+                                          ulysses_dtype_t dtype, float softmax_scale, int causal,
+                                          const int32_t* cu_seqlens, int n_docs, void* dq,
+                                          void* dk, void* dv, hipStream_t stream) {
+  AttnShape s;
+  ulysses_status_t st = check_attn_bwd(q, k, v, o, lse, dout, seqlen, bs, hq, hkv, head_dim, dtype,
+                                       softmax_scale, causal, cu_seqlens, n_docs, dq, dk, dv, &s);
+  if (st != ULYSSES_OK) return st;
+  if (ulysses::attn_bwd_workspace_bytes(s, dtype == ULYSSES_BF16) > ulysses::noalloc_scratch_bytes())
+    return ULYSSES_ERR_WORKSPACE;
+  if (seqlen == 0) return ULYSSES_OK;
+  void* scratch = nullptr;
+  if (ulysses::noalloc_scratch(&scratch) != hipSuccess) return ULYSSES_ERR_HIP;
+  return attn_bwd_launch(s, dtype, q, k, v, o, lse, dout, dq, dk, dv, scratch, stream);
 }
 
 ulysses_status_t ulysses_attn_merge(const void* o_a, const float* lse_a, const void* o_b,

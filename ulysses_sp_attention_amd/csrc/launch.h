@@ -101,6 +101,12 @@ hipError_t launch_attn_fwd_f32(const AttnShape& s, const float* q, const float* 
                                float* o, float* lse, hipStream_t stream);
 
 size_t attn_bwd_workspace_bytes(const AttnShape& s, bool bf16);
+
+// The fixed per-GPU scratch of ulysses_attn_bwd_noalloc (noalloc.hip): its
+// size, and its device address on the current device (looked up once per
+// device, then cached).
+size_t noalloc_scratch_bytes();
+hipError_t noalloc_scratch(void** out);
 hipError_t launch_attn_bwd_bf16(const AttnShape& s, const void* q, const void* k, const void* v,
                                 const void* o, const float* lse, const void* dout, void* dq,
                                 void* dk, void* dv, void* workspace, hipStream_t stream);
