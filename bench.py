@@ -14,6 +14,14 @@ inputs already resident in HBM:
 Workload: the Llama-8B-shaped rank share at P=8 and N=131072 (32 query /
 8 key-value heads globally, so 4 query heads and 1 key/value head per rank,
 head size 128, bf16, causal).  Prints one JSON line.
+
+Besides the step, `breakdown.configs` holds the other workloads of the
+measurement plan, each timed alone (HIP events around every call, median
+over the iterations): the same share at N=32768, the 262144-token forward
+and the packed-document 65536-token forward and backward (block-diagonal
+causal mask).  `--oracle-plan` instead times the CPU oracle on the whole
+plan (full passes where they take minutes, sampled rows with a labelled
+extrapolation where they would take hours) and prints that as JSON.
 """
 from __future__ import annotations
 
@@ -60,8 +68,12 @@ def traffic_if_current(unit):
 def parse_args():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-workload records of the other configurations")
+    ap.add_argument("--oracle-plan", action="store_true",
+                    help="time the CPU oracle on the measurement plan instead (no GPU use)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--loss-shard-rows", type=int, default=4096,
                     help="rows of logits per shard in the language-model loss record")
@@ -88,12 +100,32 @@ def git_sha():
         return None
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def median_ms(events):
+    """Median of the elapsed times of consecutive event pairs."""
+    import numpy as np
+    return float(np.median([a.elapsed_time(b) for a, b in events]))
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share of the path; --gpus {args.gpus} is not supported "
               "(this build runs on a single GPU, with no collectives between GPUs)", file=sys.stderr)
         return 2
+    if args.oracle_plan:
+        print(json.dumps(oracle_plan()))
+        return 0
 
     import numpy as np
     import torch
@@ -190,7 +222,8 @@ def main():
     for ev in events:
         for i, nm in enumerate(names):
             seg_ms[nm].append(ev[i].elapsed_time(ev[i + 1]))
-    avg = {nm: float(np.mean(v_)) for nm, v_ in seg_ms.items()}
+    # per-segment median over the timed steps (HIP events on the launch stream)
+    avg = {nm: float(np.median(v_)) for nm, v_ in seg_ms.items()}
 
     # Algorithmic work (causal pairs per query head; recompute not counted).
     pairs = w.causal_pairs()
@@ -234,6 +267,13 @@ def main():
     if not args.no_logits_loss:
         breakdown["logits_loss"] = measure_logits_loss(uly, torch, np, stream, args)
         breakdown["tiled_mlp"] = measure_tiled_mlp(uly, torch, np, stream, args)
+    if not args.no_configs:
+        del q_full, k_full, v_full, do_full, o_full, dq_full, dk_full, dv_full
+        del q, k, v, o, do, dq, dk, dv, ws
+        torch.cuda.empty_cache()
+        breakdown["configs"] = {name: measure_config(synth.WORKLOADS[name], uly, torch, np, stream,
+                                                     args)
+                                for name in ("llama8b-share-32k", "long-256k", "packed-docs-64k")}
 
     # Roofline of the dominant unit of the step, timed with events on the
     # stream its kernels run on.  The attention backward is one entry point
@@ -280,6 +320,8 @@ def main():
         "config": {"workload": WORKLOAD, "seqlen": N, "P": P, "rank": r, "bs": 1,
                    "hq_local": hl, "hkv_local": kl, "head_dim": hd, "causal": True,
                    "step": "pack QKV + attn fwd + unpack O + pack dO + attn bwd + unpack dQ/dK/dV"},
+        "timing": "per-segment figures are medians over the timed steps; value and ms_per_step "
+                  "are the wall clock of all timed steps",
         "breakdown": breakdown,
         "roofline": roofline,
         "cpu_baseline": cpu,
@@ -288,6 +330,176 @@ def main():
     }
     print(json.dumps(line))
     return 0
+
+
+def measure_config(w, uly, torch, np, stream, args):
+    """One workload of the measurement plan on its own: the rank-share path
+    (exchange of Q, K, V from the P chunks, attention forward, exchange of O;
+    with a backward, exchange of dO, attention backward, exchange of dQ, dK,
+    dV), or the forward alone on head-sharded inputs.  Each call is bracketed
+    by HIP events on the launch stream; figures are medians over the
+    iterations.  Work is algorithmic: 4 hd flop per visible (query, key) pair
+    and query head forward, 10 hd backward; exchanges move each byte of the
+    rank's slice once each way."""
+    import synth
+    N, hl, kl, hd = w.seqlen, w.hq_local, w.hkv_local, w.head_dim
+    bf = torch.bfloat16
+    reps = max(args.steps, 5)
+    warm = max(1, min(args.warmup, 3))
+    cu = w.cu_seqlens()
+    cu_t = None if cu is None else torch.tensor(cu, dtype=torch.int32, device="cuda")
+    pairs = w.causal_pairs()
+    fwd_flop = 4.0 * hd * hl * pairs
+    bwd_flop = 10.0 * hd * hl * pairs
+
+    def dev(host):
+        return torch.from_numpy(host.view(np.int16)).view(bf).cuda()
+
+    out = {"seqlen": N, "hq_local": hl, "hkv_local": kl, "head_dim": hd, "causal": True,
+           "documents": None if cu is None else len(cu) - 1, "visible_pairs_per_head": pairs,
+           "iterations": reps, "warmup": warm}
+    lse = torch.empty((1, hl, N), dtype=torch.float32, device="cuda")
+    segs = {}
+    if w.head_sharded_inputs:
+        q = dev(w.head_tensor(synth.STREAM_Q, hl, scale=w.q_prescale))
+        k = dev(w.head_tensor(synth.STREAM_K, kl))
+        v = dev(w.head_tensor(synth.STREAM_V, kl))
+        o = torch.empty_like(q)
+        segs["attn_fwd"] = lambda: uly.ulysses_attn_fwd(q, k, v, o, lse, w.softmax_scale, True, cu_t)
+        order = ["attn_fwd"]
+    else:
+        P, n, r = w.P, w.n_local, w.rank
+        full = {s_: dev(w.seq_tensor(s_, h_, scale=w.q_prescale if s_ == synth.STREAM_Q else 1.0))
+                for s_, h_ in ((synth.STREAM_Q, w.hq), (synth.STREAM_K, w.hkv),
+                               (synth.STREAM_V, w.hkv), (synth.STREAM_DO, w.hq))}
+        ch = {s_: [t[c * n:(c + 1) * n] for c in range(P)] for s_, t in full.items()}
+        outs = {nm: torch.zeros_like(full[s_]) for nm, s_ in (("o", 1), ("dq", 1), ("dk", 2), ("dv", 3))}
+        och = {nm: [t[c * n:(c + 1) * n] for c in range(P)] for nm, t in outs.items()}
+        q = torch.empty((N, 1, hl, hd), dtype=bf, device="cuda")
+        k = torch.empty((N, 1, kl, hd), dtype=bf, device="cuda")
+        v, o, do = torch.empty_like(k), torch.empty_like(q), torch.empty_like(q)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(k)
+        ws = torch.empty(uly.ulysses_attn_bwd_workspace_size(N, 1, hl, kl, hd, uly.BF16),
+                         dtype=torch.uint8, device="cuda")
+        segs["pack_qkv"] = lambda: uly.ulysses_seq_to_head_batch(
+            [(ch[1], q), (ch[2], k), (ch[3], v)], r)
+        segs["attn_fwd"] = lambda: uly.ulysses_attn_fwd(q, k, v, o, lse, w.softmax_scale, True, cu_t)
+        segs["unpack_o"] = lambda: uly.ulysses_head_to_seq(o, r, och["o"])
+        segs["pack_do"] = lambda: uly.ulysses_seq_to_head(ch[4], r, do)
+        segs["attn_bwd"] = lambda: uly.ulysses_attn_bwd(q, k, v, o, lse, do, dq, dk, dv, ws,
+                                                        w.softmax_scale, True, cu_t)
+        segs["unpack_dqkv"] = lambda: uly.ulysses_head_to_seq_batch(
+            [(dq, och["dq"]), (dk, och["dk"]), (dv, och["dv"])], r)
+        order = ["pack_qkv", "attn_fwd", "unpack_o", "pack_do", "attn_bwd", "unpack_dqkv"]
+    for _ in range(warm):
+        for nm in order:
+            segs[nm]()
+    torch.cuda.synchronize()
+    ev = {nm: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)] for nm in order}
+    for i in range(reps):
+        for nm in order:
+            ev[nm][i][0].record(stream)
+            segs[nm]()
+            ev[nm][i][1].record(stream)
+    torch.cuda.synchronize()
+    e = 2
+    xbytes = {"pack_qkv": 2.0 * N * (hl + 2 * kl) * hd * e, "unpack_o": 2.0 * N * hl * hd * e,
+              "pack_do": 2.0 * N * hl * hd * e, "unpack_dqkv": 2.0 * N * (hl + 2 * kl) * hd * e}
+    for nm in order:
+        ms = median_ms(ev[nm])
+        if nm.startswith("attn"):
+            flop = fwd_flop if nm == "attn_fwd" else bwd_flop
+            tf = flop / (ms * 1e-3) / 1e12
+            out[nm] = {"ms": ms, "TFLOP/s": tf, "frac_of_mfma_peak": tf / MFMA_BF16_PEAK_TFLOPS,
+                       "flop": flop}
+        else:
+            gb = xbytes[nm] / (ms * 1e-3) / 1e9
+            out[nm] = {"ms": ms, "GB/s": gb, "frac_of_hbm_peak": gb / HBM_PEAK_GBPS}
+    out["method"] = (f"{reps} iterations after {warm} warm-up, each call bracketed by HIP events on "
+                     "the launch stream, median")
+    del segs
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
+def oracle_plan():
+    """The CPU oracle (fp64, OpenMP over output rows) timed on this host over
+    the measurement plan: the forward of the tiny P=2 share (both ranks) and
+    of the 32K share in full, the packed-document 64K share forward and
+    backward in full, and sampled query rows (first 256, last 256, 1024
+    seeded random; all heads) of the 128K and 256K forwards, each with the
+    full-pass time extrapolated from the sample's algorithmic flop (labelled
+    as such).  A reported baseline, not a target."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    def f64(w, s_, heads, scale=1.0):
+        return synth.to_f64(w.head_tensor(s_, heads, scale=scale), w.dtype)
+
+    res = {"cores": oracle.num_threads(), "cpu_model": cpu_model(), "kind": "oracle", "runs": {}}
+
+    def record(name, flop, dt, **extra):
+        res["runs"][name] = dict({"seconds": dt, "flop": flop, "TFLOP/s": flop / dt / 1e12}, **extra)
+        print(f"oracle plan: {name} {dt:.1f} s", file=sys.stderr, flush=True)
+
+    # tiny P=2 share: both ranks' forward (fp32 inputs)
+    w = synth.WORKLOADS["tiny-p2"]
+    t0 = time.perf_counter()
+    flop = 0.0
+    for r in range(w.P):
+        q, k, v = (synth.to_f64(synth.normal(w.seed, s_, (w.seqlen, 1, w.hq, w.head_dim), "f32"), "f32")
+                   [:, :, r * w.hq_local:(r + 1) * w.hq_local] for s_ in (1, 2, 3))
+        oracle.attn_fwd(np.ascontiguousarray(q), np.ascontiguousarray(k), np.ascontiguousarray(v),
+                        w.softmax_scale, True)
+        flop += 4.0 * w.head_dim * w.hq_local * w.causal_pairs()
+    record("tiny-p2 forward (both ranks, full)", flop, time.perf_counter() - t0)
+
+    for name, bwd in (("llama8b-share-32k", False), ("packed-docs-64k", True)):
+        w = synth.WORKLOADS[name]
+        q = f64(w, synth.STREAM_Q, w.hq_local, w.q_prescale)
+        k, v = f64(w, synth.STREAM_K, w.hkv_local), f64(w, synth.STREAM_V, w.hkv_local)
+        cu = w.cu_seqlens()
+        flop = 4.0 * w.head_dim * w.hq_local * w.causal_pairs()
+        t0 = time.perf_counter()
+        oracle.attn_fwd(q, k, v, w.softmax_scale, True, cu)
+        record(f"{name} forward (full)", flop, time.perf_counter() - t0)
+        if bwd:
+            # Documents are independent (block-diagonal mask), so the full
+            # backward is each document's backward in turn; one progress line
+            # per document.
+            do = f64(w, synth.STREAM_DO, w.hq_local)
+            t0 = time.perf_counter()
+            for d0, d1 in zip(cu[:-1], cu[1:]):
+                sl = slice(int(d0), int(d1))
+                oracle.attn_bwd(np.ascontiguousarray(q[sl]), np.ascontiguousarray(k[sl]),
+                                np.ascontiguousarray(v[sl]), np.ascontiguousarray(do[sl]),
+                                w.softmax_scale, True)
+                print(f"oracle plan: {name} backward, document of {d1 - d0} tokens done "
+                      f"({time.perf_counter() - t0:.1f} s)", file=sys.stderr, flush=True)
+            record(f"{name} backward (full, document by document)", 2.5 * flop,
+                   time.perf_counter() - t0)
+
+    for name in ("llama8b-share-128k", "long-256k"):
+        w = synth.WORKLOADS[name]
+        N = w.seqlen
+        rng = np.random.default_rng(w.seed)
+        rows = np.unique(np.concatenate([np.arange(256), np.arange(N - 256, N),
+                                         rng.integers(0, N, size=1024)])).astype(np.int64)
+        q = f64(w, synth.STREAM_Q, w.hq_local, w.q_prescale)
+        k, v = f64(w, synth.STREAM_K, w.hkv_local), f64(w, synth.STREAM_V, w.hkv_local)
+        flop = 4.0 * w.head_dim * w.hq_local * float(np.sum(rows + 1))
+        t0 = time.perf_counter()
+        oracle.attn_fwd(q, k, v, w.softmax_scale, True, None, rows=rows)
+        dt = time.perf_counter() - t0
+        full = 4.0 * w.head_dim * w.hq_local * w.causal_pairs()
+        record(f"{name} forward ({len(rows)} sampled rows)", flop, dt,
+               extrapolated_full_seconds=dt * full / flop,
+               extrapolation="sample time x (full algorithmic flop / sample flop); not measured")
+    return res
 
 
 def measure_fused(uly, torch, np, stream, args, rank, scale, lse, ws, tables, fwd_flop,
@@ -590,7 +802,7 @@ def cpu_baseline(w, n_rows):
     dt = time.perf_counter() - t0
     flop = 4.0 * w.head_dim * w.hq_local * float(np.sum(rows + 1))
     return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle", "seconds": dt,
+            "cpu_model": cpu_model(), "kind": "oracle", "seconds": dt,
             "sample": f"attention forward for {n_rows} evenly spaced query rows of N={N} "
                       f"(all {w.hq_local} heads), fp64, {flop:.3e} algorithmic flop"}
 
