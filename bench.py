@@ -580,7 +580,7 @@ def measure_logits_loss(uly, torch, np, stream, args):
            "flop": flop, "tokens": T, "hidden": d, "vocab": V, "shard_rows": shard,
            "loss_sum_finite": bool(torch.isfinite(total).item()),
            "method": f"{reps} calls back to back after 2 warm-up calls, HIP events on the "
-                     "launch stream; GEMMs by rocBLAS, the row kernel and loss sum by libulysses"}
+                     "launch stream; every kernel (matrix-core GEMMs, the row kernel and the loss sum) by libulysses"}
     del h, w, dh, dw, ws
     torch.cuda.empty_cache()
     return out
@@ -633,7 +633,7 @@ def measure_tiled_mlp(uly, torch, np, stream, args):
         out[name] = {"ms": ms, "TFLOP/s": tf, "frac_of_mfma_peak": tf / MFMA_BF16_PEAK_TFLOPS,
                      "executed_TFLOP/s": executed / (ms * 1e-3) / 1e12}
     out["method"] = (f"{reps} calls each back to back after 2 warm-up calls, HIP events on the "
-                     "launch stream; GEMMs by rocBLAS, the SwiGLU row kernels by libulysses")
+                     "launch stream; every kernel (matrix-core GEMMs and the SwiGLU row kernels) by libulysses")
     del x, dy, wg, wu, wd, y, dx, dwg, dwu, dwd, ws
     torch.cuda.empty_cache()
     return out

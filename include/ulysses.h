@@ -38,13 +38,8 @@
  * Conventions for every entry point:
  *  - Device buffers are owned by the caller; scratch memory comes from a
  *    caller-provided workspace.  Library state and allocation, precisely:
- *      * the exchange, attention (forward, backward, fused) and merge calls
- *        allocate and free nothing and keep no state between calls;
- *      * ulysses_logits_loss and ulysses_tiled_mlp_fwd/bwd run their plain
- *        GEMMs through rocBLAS on a handle the library creates on the first
- *        such call of each host thread on each device and keeps until the
- *        process ends; rocBLAS may allocate device memory of its own inside
- *        that handle (on creation or on the first GEMM of a shape);
+ *      * every call except ulysses_attn_bwd_noalloc allocates and frees
+ *        nothing and keeps no state between calls;
  *      * ulysses_attn_bwd_noalloc uses a fixed device array that every GPU
  *        the library runs on holds until the process ends, and caches that
  *        array's address per device (a mutex guards the cache).
@@ -371,24 +366,28 @@ size_t ulysses_logits_loss_workspace_size(int64_t shard_rows, int64_t vocab);
  *   h          device bf16 [T, d] (16-byte aligned)
  *   w          device bf16 [vocab, d] (16-byte aligned)
  *   labels     device int64 [T] (8-byte aligned)
- *   dtype      ULYSSES_BF16 (inputs and dh; fp32 logits and accumulation;
- *              G rounded to bf16 before the two gradient products)
+ *   dtype      ULYSSES_BF16 (inputs and dh; fp32 logits, statistics and
+ *              accumulation; exp(z - tile max) kept in bf16, G rounded to
+ *              bf16 before the two gradient products)
  *   loss_rows  device fp32 [T]; loss_sum device fp32 [1]; n_good device
  *              int64 [1] (8-byte aligned)
  *   dh         device bf16 [T, d]; dw device fp32 [vocab, d]: fully
  *              overwritten (T == 0: dw = 0, loss_sum = 0, n_good = 0)
  *   workspace  device memory of at least
  *              ulysses_logits_loss_workspace_size(min(shard_rows, T), vocab)
- *              bytes, 16-byte aligned, contents irrelevant (fp32 logits
- *              and bf16 G of one shard)
+ *              bytes, 16-byte aligned, contents irrelevant (bf16
+ *              exp(z - tile max), turned into G in place, the per-tile
+ *              statistics and the label logits of one shard)
  * A label outside [0, vocab) other than ignore_index gives a NaN loss row
  * and a NaN gradient row, without an out-of-bounds access.  The three
- * products per shard are rocBLAS GEMMs (split-K atomics off, so results are
- * reproducible) on a rocBLAS handle that the library makes per host thread
- * and device on first use and keeps.  ERR_SHAPE for T < 0, d < 1,
- * vocab < 1, shard_rows < 1 or a non-finite grad_scale; ERR_UNSUPPORTED for
- * a dtype other than bf16 or a size >= 2^31; ERR_HIP also when a rocBLAS
- * call fails.
+ * products per shard run on the library's own matrix-core GEMM.  The fp32
+ * logits never reach memory: the epilogue of the Z product writes, per row
+ * and 256-column tile, the tile's max m and sum of exp(z - m), the label's
+ * logit, and exp(z - m) in bf16, which one pass turns into G in place.
+ * Every sum is taken in a fixed order, so results are bitwise
+ * reproducible.  ERR_SHAPE for T < 0, d < 1
+ * or not a multiple of 8, vocab < 1, shard_rows < 1 or a non-finite
+ * grad_scale; ERR_UNSUPPORTED for a dtype other than bf16 or a size >= 2^31.
  */
 ulysses_status_t ulysses_logits_loss(const void* h, const void* w, const int64_t* labels,
                                      int64_t T, int64_t d, int64_t vocab, ulysses_dtype_t dtype,
@@ -423,8 +422,9 @@ size_t ulysses_tiled_mlp_workspace_size(int64_t shard_rows, int64_t d, int64_t i
  *                 irrelevant
  * Every pointer 16-byte aligned.  g, u and da are kept in fp32; a, dg and du
  * are rounded to bf16 as operands of the following products; dx is summed
- * in fp32 and rounded once.  The products are rocBLAS GEMMs as for
- * ulysses_logits_loss.  ERR_SHAPE for T < 0, d or inter < 1 or not a
+ * in fp32 and rounded once.  The products run on the library's own
+ * matrix-core GEMM, in the layout each operand is stored in (no transposed
+ * copies), in a fixed order (bitwise reproducible).  ERR_SHAPE for T < 0, d or inter < 1 or not a
  * multiple of 8, shard_rows < 1; ERR_UNSUPPORTED for a dtype other than bf16
  * or a size >= 2^31.
  */

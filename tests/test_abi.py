@@ -292,9 +292,12 @@ def logits_loss_call(lib, **kw):
 
 
 def test_logits_loss_workspace_size(lib):
-    # fp32 logits and bf16 G of one shard, each rounded up to 256 bytes
-    assert lib.ulysses_logits_loss_workspace_size(32, 1000) == 128000 + 64000
-    assert lib.ulysses_logits_loss_workspace_size(3, 5) == 256 + 256
+    # bf16 exp(Z - m) / G of one shard with rows padded to 8 columns, the
+    # (max, sum) pair of every row and 256-column tile, and one fp32 label
+    # logit per row, each region rounded up to 256 bytes
+    assert lib.ulysses_logits_loss_workspace_size(32, 1000) == 64000 + 1024 + 256
+    assert lib.ulysses_logits_loss_workspace_size(3, 5) == 256 + 256 + 256
+    assert lib.ulysses_logits_loss_workspace_size(2, 300) == 256 * 5 + 256 + 256
     assert lib.ulysses_logits_loss_workspace_size(0, 5) == 0
     assert lib.ulysses_logits_loss_workspace_size(4, 1 << 31) == 0
 
@@ -305,6 +308,7 @@ def test_logits_loss_workspace_size(lib):
     (dict(dt=9), uly.ERR_DTYPE),
     (dict(dt=uly.FP32), uly.ERR_UNSUPPORTED),
     (dict(T=-1), uly.ERR_SHAPE), (dict(d=0), uly.ERR_SHAPE), (dict(V=0), uly.ERR_SHAPE),
+    (dict(d=12), uly.ERR_SHAPE),
     (dict(shard=0), uly.ERR_SHAPE), (dict(s=float("nan")), uly.ERR_SHAPE),
     (dict(s=float("inf")), uly.ERR_SHAPE),
     (dict(V=1 << 31), uly.ERR_UNSUPPORTED), (dict(d=1 << 31), uly.ERR_UNSUPPORTED),
@@ -312,7 +316,7 @@ def test_logits_loss_workspace_size(lib):
     (dict(labels=FAKE + 4), uly.ERR_ALIGNMENT), (dict(good=FAKE + 4), uly.ERR_ALIGNMENT),
     (dict(rows=FAKE + 2), uly.ERR_ALIGNMENT),
     (dict(ws=None), uly.ERR_WORKSPACE),
-    (dict(ws_bytes=32 * 1000 * 6 - 1), uly.ERR_WORKSPACE),
+    (dict(ws_bytes=64000 + 1024 + 256 - 1), uly.ERR_WORKSPACE),
     (dict(ws=FAKE + 8), uly.ERR_ALIGNMENT),
 ])
 def test_logits_loss_validation(lib, kw, want):

@@ -2,12 +2,14 @@
 formed one shard of rows at a time) against the oracle, element by element.
 
 Tolerances follow from the arithmetic (bf16 inputs are exact in fp32
-products; logits accumulate in fp32; G is rounded to bf16 before the two
-gradient products; dh is rounded to bf16, dw stays fp32), with the oracle's
-magnitudes zmag_i = max_v sum_k |h_ik w_vk|, |G| |W| and |G|^T |H|:
+products; logits, the row statistics and the label logit stay fp32; each G
+element carries two bf16 roundings, of exp(z - tile max) and of G itself,
+so |dG| <= (2^-8 + 2^-20) |G|; dh is rounded to bf16, dw stays fp32), with
+the oracle's magnitudes zmag_i = max_v sum_k |h_ik w_vk|, |G| |W| and
+|G|^T |H|, each bar twice the bound:
   loss_i : 2 d 2^-24 zmag_i + 1e-5 (1 + |loss_i|)
   dh     : 2^-7 (|G||W|) + 2^-8 |dh|
-  dw     : 2^-8 (|G|^T|H|)
+  dw     : 2^-7 (|G|^T|H|)
 """
 import numpy as np
 import pytest
@@ -63,7 +65,7 @@ def check(got, ref, mags, d):
     assert abs(total - r_total) <= tol_rows.sum() + 1e-6 * abs(r_total)
     tol_dh = 2.0 ** -7 * mags["dh"] + 2.0 ** -8 * np.abs(r_dh)
     assert np.all(np.abs(dh - r_dh) <= tol_dh), np.max(np.abs(dh - r_dh) - tol_dh)
-    tol_dw = 2.0 ** -8 * mags["dw"]
+    tol_dw = 2.0 ** -7 * mags["dw"]
     assert np.all(np.abs(dw - r_dw) <= tol_dw), np.max(np.abs(dw - r_dw) - tol_dw)
 
 
@@ -160,18 +162,19 @@ def test_logits_loss_full_size_llama8b_lm_head_sampled():
     assert np.all(np.abs(g_rows - r_rows) <= tol)
     g_dh = dh.float().cpu().numpy()[sample].astype(np.float64)
     assert np.all(np.abs(g_dh - r_dh) <= 2.0 ** -7 * mags["dh"] + 2.0 ** -8 * np.abs(r_dh))
-    # every row of G sums to zero, so sum_v dW_v = 0 up to rounding: G to bf16
-    # moves a row's sum by at most 2^-9 sum_v |G_iv| <= 2^-8 s; the fp32 GEMM
-    # sums (4096 rows per shard) add at most 2^-12 * 2 s per row; the fp32
-    # softmax's own sum error is below 2^-20 s
+    # every row of G sums to zero, so sum_v dW_v = 0 up to rounding: the two
+    # bf16 roundings of each G element (exp(z - tile max), then G) move a
+    # row's sum by at most 2^-8 sum_v |G_iv| <= 2^-7 s; the fp32 GEMM sums
+    # (4096 rows per shard) add at most 2^-12 * 2 s per row; the fp32
+    # softmax's own sum error is below 2^-20 s: in all below 2^-6 s per row
     col = dw.double().sum(dim=0).cpu().numpy()
-    bound = 2.0 ** -7 * s * h.double().abs().sum(dim=0).cpu().numpy()
+    bound = 2.0 ** -6 * s * h.double().abs().sum(dim=0).cpu().numpy()
     assert np.all(np.abs(col) <= bound)
     assert np.isfinite(float(total.item()))
 
 
 def test_logits_loss_from_two_host_threads_at_once():
-    """Each host thread gets its own rocBLAS handle: two threads calling at
+    """The call keeps no state between calls: two host threads calling at
     the same time on their own streams get the same bits as one call alone."""
     import threading
     import torch

@@ -12,7 +12,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libulysses.so")
 SOURCES = ["api.cpp", "exchange.hip", "attn_fwd.hip", "attn_f32.hip", "attn_bwd.hip", "attn_merge.hip",
-           "logits_loss.hip", "tiled_mlp.hip", "noalloc.hip"]
+           "logits_loss.hip", "tiled_mlp.hip", "noalloc.hip", "gemm.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -20,14 +20,17 @@ ARCH = "gfx950"
 COMMON_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-I", INCLUDE, "-I", CSRC, "-Wall",
 ]
+# The kernels work on their matrix-core accumulators with vector
+# instructions (softmax, masks, the loss epilogue) and run two or more waves
+# per SIMD, so they keep them in ordinary VGPRs.
+VGPR_FORM_FLAGS = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON_FLAGS]
+    cmd = [HIPCC, *COMMON_FLAGS, *VGPR_FORM_FLAGS]
     if src.endswith(".hip"):
         cmd += ["-x", "hip"]
     cmd += ["-c", os.path.join(CSRC, src), "-o", obj]
@@ -41,10 +44,8 @@ def build_lib(jobs: int = 8) -> str:
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB_PATH + ".tmp"
-    # rocBLAS (plain GEMMs of the language-model loss): in a process that has
-    # imported torch this resolves, by soname, to the copy torch loaded.
-    subprocess.run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-L/opt/rocm/lib",
-                    "-lrocblas", "-o", tmp], check=True)
+    subprocess.run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp],
+                   check=True)
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 

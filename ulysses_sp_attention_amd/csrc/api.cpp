@@ -432,10 +432,10 @@ ulysses_status_t ulysses_logits_loss(const void* h, const void* w, const int64_t
   if (T > 0 && (h == nullptr || labels == nullptr || loss_rows == nullptr || dh == nullptr))
     return ULYSSES_ERR_NULL;
   if (elem_size(dtype) == 0) return ULYSSES_ERR_DTYPE;
-  if (T < 0 || d < 1 || vocab < 1 || shard_rows < 1 || !std::isfinite(grad_scale))
+  if (T < 0 || d < 1 || d % 8 != 0 || vocab < 1 || shard_rows < 1 || !std::isfinite(grad_scale))
     return ULYSSES_ERR_SHAPE;
   if (dtype != ULYSSES_BF16) return ULYSSES_ERR_UNSUPPORTED;
-  // The library GEMMs count rows, columns and leading dimensions in 32 bits.
+  // The GEMM counts rows, columns and the inner size in 32 bits.
   if (T >= (int64_t(1) << 31) || d >= (int64_t(1) << 31) || vocab >= (int64_t(1) << 31) ||
       shard_rows >= (int64_t(1) << 31))
     return ULYSSES_ERR_UNSUPPORTED;

@@ -150,19 +150,23 @@ __device__ __forceinline__ void block_barrier() {
 // sequence rows that match the accumulator layout of the other operand.  The
 // swizzle depends on the low four row bits only, so for row0 a multiple of 16
 // the address is tile + row0 * kRowBytes + a per-lane offset for each (8-row
-// half, db), computed once.
-template <int kChunks, int kRowBytes, int kDB>
+// half, db), computed once.  db0 shifts the column blocks read to db0 ..
+// db0 + kDB - 1 (db stays a compile-time index into off).  kNaturalK: the 8
+// rows of lane l are instead 8 (l / 32) .. + 7 in order, the k order of a
+// plain 16-byte read of a k-major operand.
+template <int kChunks, int kRowBytes, int kDB, bool kNaturalK = false>
 struct TrReader {
   int off[2][kDB];
-  __device__ __forceinline__ explicit TrReader(int lane) {
+  __device__ __forceinline__ explicit TrReader(int lane, int db0 = 0) {
     const int grp = lane >> 4;
     const int u = lane & 15;
 #pragma unroll
     for (int jh = 0; jh < 2; ++jh)
 #pragma unroll
       for (int db = 0; db < kDB; ++db) {
-        const int row = 8 * jh + 4 * (grp >> 1) + (u >> 2);
-        const int col = db * 32 + 16 * (grp & 1) + 4 * (u & 3);
+        const int row = kNaturalK ? 8 * (grp >> 1) + 4 * jh + (u >> 2)
+                                  : 8 * jh + 4 * (grp >> 1) + (u >> 2);
+        const int col = (db0 + db) * 32 + 16 * (grp & 1) + 4 * (u & 3);
         off[jh][db] = swz<kChunks, kRowBytes>(row, col >> 3) + ((col >> 2) & 1) * 8;
       }
   }

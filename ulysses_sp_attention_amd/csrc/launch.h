@@ -146,9 +146,38 @@ struct LogitsLossArgs {
   void* workspace;
 };
 size_t logits_loss_workspace_bytes(int64_t shard_rows, int64_t V);
-// hipErrorUnknown: a rocBLAS call failed; hipErrorNotInitialized: no rocBLAS
-// handle could be made.
 hipError_t launch_logits_loss(const LogitsLossArgs& a, hipStream_t stream);
+
+// Dense bf16 product on the matrix cores (gemm.hip):
+//   C[x][y] (+)= sum_k X(x, k) Y(y, k),   x < nx, y < ny, k < K,
+// fp32 accumulation.  An operand is k-major (element (r, k) at p[r*ld + k],
+// ld >= round_up(K, 8)) or row-major over k (element (r, k) at p[k*ld + r],
+// ld >= round_up(rows, 8)); ld % 8 == 0 and p 16-byte aligned either way.
+// C is fp32 (stored, or added to when accumulate) or bf16 (c_bf16), row
+// stride ldc % 4 == 0.  stats (the loss's logits: both operands k-major,
+// c_bf16, labels and label_logit set): for every row x and 256-column tile t
+// of the product Z, m = the tile's row max goes to stats[(x *
+// gemm_tiles_y(ny) + t) * 2], C receives exp(Z - m) instead of Z, their sum
+// goes to stats[... + 1], and Z[x][labels[x]] to label_logit[x] (rows whose
+// label is outside [0, ny) get no label_logit).
+struct GemmOperand {
+  const void* p;
+  int64_t ld;
+  bool kmajor;
+};
+struct GemmOp {
+  GemmOperand x, y;
+  int64_t nx, ny, K;
+  void* c;
+  int64_t ldc;
+  bool c_bf16;
+  bool accumulate;
+  float* stats;
+  const int64_t* labels;
+  float* label_logit;
+};
+int gemm_tiles_y(int64_t ny);
+hipError_t launch_gemm(const GemmOp& op, hipStream_t stream);
 
 // Sequence-tiled SwiGLU MLP over T rows, shard_rows at a time.  x [T, d],
 // wg and wu [I, d], wd [d, I], y/dy/dx [T, d] bf16; dwg, dwu [I, d] and dwd

@@ -5,17 +5,18 @@
 // keeping them (the guide's tiled compute replays the forward in the
 // backward).  Rows are independent, so sharding changes no result.
 //
-// Per shard of S rows (intermediates in the workspace):
-//   forward : g = x_s Wg^T, u = x_s Wu^T (fp32)   rocBLAS
+// Per shard of S rows (intermediates in the workspace; every product on the
+// library's matrix-core GEMM, gemm.hip, with operands in whatever layout
+// they are stored in):
+//   forward : g = x_s Wg^T, u = x_s Wu^T (fp32)
 //             a = bf16(silu(g) u)                  swiglu_fwd_kernel
-//             y_s = a Wd^T (bf16)                  rocBLAS
-//   backward: g, u as above; da = dy_s Wd (fp32)   rocBLAS
+//             y_s = a Wd^T (bf16)
+//   backward: g, u as above; da = dy_s Wd (fp32)
 //             a, dg = bf16(da u silu'(g)), du = bf16(da silu(g))
 //                                                  swiglu_bwd_kernel
 //             dWd (+)= dy_s^T a; dWg (+)= dg^T x_s; dWu (+)= du^T x_s (fp32)
-//             dx_s = dg Wg + du Wu (fp32, then bf16) rocBLAS + cast
+//             dx_s = dg Wg + du Wu (fp32, then bf16 by f32_to_bf16_kernel)
 // g, u and da stay fp32; only the operands of a GEMM are rounded to bf16.
-#include "blas.h"
 #include "device_common.h"
 #include "launch.h"
 
@@ -143,12 +144,31 @@ MlpWork carve(void* ws, int64_t S, int64_t d, int64_t I) {
   return w;
 }
 
-// g and u of rows [r0, r0 + rows).
-bool gate_up(rocblas_handle hd, const TiledMlpArgs& a, const MlpWork& w, int64_t r0, int64_t rows) {
+// C (+)= X Y^T on the matrix-core GEMM; each operand given as (pointer,
+// leading dimension, k-major?).
+hipError_t gemm(const void* x, int64_t ldx, bool xk, const void* y, int64_t ldy, bool yk,
+                int64_t nx, int64_t ny, int64_t K, void* c, int64_t ldc, bool c_bf16,
+                bool accumulate, hipStream_t stream) {
+  GemmOp op{};
+  op.x = GemmOperand{x, ldx, xk};
+  op.y = GemmOperand{y, ldy, yk};
+  op.nx = nx;
+  op.ny = ny;
+  op.K = K;
+  op.c = c;
+  op.ldc = ldc;
+  op.c_bf16 = c_bf16;
+  op.accumulate = accumulate;
+  return launch_gemm(op, stream);
+}
+
+// g and u of rows [r0, r0 + rows): g[s][i] = sum_k x[s][k] Wg[i][k].
+hipError_t gate_up(const TiledMlpArgs& a, const MlpWork& w, int64_t r0, int64_t rows,
+                   hipStream_t stream) {
   const __bf16* xs = static_cast<const __bf16*>(a.x) + r0 * a.d;
-  // g^T (col-major I x rows) = Wg (col-major d x I)^T . x_s^T (col-major d x rows)
-  return gemm_bf16(hd, true, false, a.I, rows, a.d, a.wg, a.d, xs, a.d, 0.0f, w.g, false, a.I) &&
-         gemm_bf16(hd, true, false, a.I, rows, a.d, a.wu, a.d, xs, a.d, 0.0f, w.u, false, a.I);
+  hipError_t e = gemm(xs, a.d, true, a.wg, a.d, true, rows, a.I, a.d, w.g, a.I, false, false, stream);
+  if (e != hipSuccess) return e;
+  return gemm(xs, a.d, true, a.wu, a.d, true, rows, a.I, a.d, w.u, a.I, false, false, stream);
 }
 
 }  // namespace
@@ -160,9 +180,6 @@ size_t tiled_mlp_workspace_bytes(int64_t shard_rows, int64_t d, int64_t I, bool 
 }
 
 hipError_t launch_tiled_mlp(const TiledMlpArgs& a, hipStream_t stream) {
-  rocblas_handle hd = blas_handle();
-  if (!hd) return hipErrorNotInitialized;
-  if (rocblas_set_stream(hd, stream) != rocblas_status_success) return hipErrorUnknown;
   const int64_t d = a.d, I = a.I;
   const MlpWork w = carve(a.workspace, a.shard_rows, d, I);
   hipError_t e;
@@ -176,36 +193,42 @@ hipError_t launch_tiled_mlp(const TiledMlpArgs& a, hipStream_t stream) {
   for (int64_t r0 = 0; r0 < a.T; r0 += a.shard_rows) {
     const int64_t rows = a.T - r0 < a.shard_rows ? a.T - r0 : a.shard_rows;
     const int64_t n = rows * I;
-    if (!gate_up(hd, a, w, r0, rows)) return hipErrorUnknown;
+    if ((e = gate_up(a, w, r0, rows, stream)) != hipSuccess) return e;
     if (!a.backward) {
       e = launch_kernel(swiglu_fwd_kernel, ew_grid(n), dim3(kEwThreads), 0, stream, w.g, w.u, w.a, n);
       if (e != hipSuccess) return e;
-      // y_s^T (col-major d x rows) = Wd (col-major I x d)^T . a^T (col-major I x rows)
-      if (!gemm_bf16(hd, true, false, d, rows, I, a.wd, I, w.a, I, 0.0f,
-                     static_cast<__bf16*>(a.y) + r0 * d, true, d))
-        return hipErrorUnknown;
+      // y_s[s][j] = sum_i a[s][i] Wd[j][i]
+      e = gemm(w.a, I, true, a.wd, I, true, rows, d, I, static_cast<__bf16*>(a.y) + r0 * d, d,
+               true, false, stream);
+      if (e != hipSuccess) return e;
       continue;
     }
     const __bf16* xs = static_cast<const __bf16*>(a.x) + r0 * d;
     const __bf16* dys = static_cast<const __bf16*>(a.dy) + r0 * d;
-    const float beta = r0 == 0 ? 0.0f : 1.0f;
-    // da^T (col-major I x rows) = Wd (col-major I x d) . dy_s^T (col-major d x rows)
-    if (!gemm_bf16(hd, false, false, I, rows, d, a.wd, I, dys, d, 0.0f, w.da, false, I))
-      return hipErrorUnknown;
+    const bool acc = r0 > 0;   // weight gradients: stored by the first shard, added to after
+    // da[s][i] = sum_j dy[s][j] Wd[j][i]
+    if ((e = gemm(dys, d, true, a.wd, I, false, rows, I, d, w.da, I, false, false, stream)) !=
+        hipSuccess)
+      return e;
     e = launch_kernel(swiglu_bwd_kernel, ew_grid(n), dim3(kEwThreads), 0, stream, w.g, w.u, w.da,
                       w.a, w.dg, w.du, n);
     if (e != hipSuccess) return e;
-    // dWd^T (col-major I x d) (+)= a^T (col-major I x rows) . dy_s (col-major d x rows)^T
-    if (!gemm_bf16(hd, false, true, I, d, rows, w.a, I, dys, d, beta, a.dwd, false, I))
-      return hipErrorUnknown;
-    // dWg^T (col-major d x I) (+)= x_s^T (col-major d x rows) . dg (col-major I x rows)^T
-    if (!gemm_bf16(hd, false, true, d, I, rows, xs, d, w.dg, I, beta, a.dwg, false, d) ||
-        !gemm_bf16(hd, false, true, d, I, rows, xs, d, w.du, I, beta, a.dwu, false, d))
-      return hipErrorUnknown;
-    // dx_s^T (col-major d x rows) = Wg (col-major d x I) . dg^T + Wu . du^T
-    if (!gemm_bf16(hd, false, false, d, rows, I, a.wg, d, w.dg, I, 0.0f, w.dx, false, d) ||
-        !gemm_bf16(hd, false, false, d, rows, I, a.wu, d, w.du, I, 1.0f, w.dx, false, d))
-      return hipErrorUnknown;
+    // dWd[j][i] (+)= sum_s dy[s][j] a[s][i]
+    if ((e = gemm(dys, d, false, w.a, I, false, d, I, rows, a.dwd, I, false, acc, stream)) !=
+        hipSuccess)
+      return e;
+    // dWg[i][j] (+)= sum_s dg[s][i] x[s][j]; dWu likewise with du
+    if ((e = gemm(w.dg, I, false, xs, d, false, I, d, rows, a.dwg, d, false, acc, stream)) !=
+            hipSuccess ||
+        (e = gemm(w.du, I, false, xs, d, false, I, d, rows, a.dwu, d, false, acc, stream)) !=
+            hipSuccess)
+      return e;
+    // dx[s][j] = sum_i dg[s][i] Wg[i][j] + sum_i du[s][i] Wu[i][j]
+    if ((e = gemm(w.dg, I, true, a.wg, d, false, rows, d, I, w.dx, d, false, false, stream)) !=
+            hipSuccess ||
+        (e = gemm(w.du, I, true, a.wu, d, false, rows, d, I, w.dx, d, false, true, stream)) !=
+            hipSuccess)
+      return e;
     e = launch_kernel(f32_to_bf16_kernel, ew_grid(rows * d), dim3(kEwThreads), 0, stream, w.dx,
                       static_cast<__bf16*>(a.dx) + r0 * d, rows * d);
     if (e != hipSuccess) return e;
