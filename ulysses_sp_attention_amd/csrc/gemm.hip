@@ -358,6 +358,39 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmParams p) {
       }
     }
   }
+  if constexpr (kOut == kAccumF32) {
+    // The wave's whole 128 x 64 block inside C: the old values of row block
+    // i + 1 are loaded before block i is stored back, so each load's latency
+    // overlaps the previous block's adds and stores.
+    if (x0 + 128 * wx + 128 <= p.nx && y0 + 64 * wy + 64 <= p.ny) {
+      float* cb = static_cast<float*>(p.c) + (int64_t)(x0 + 128 * wx + r32) * p.ldc + y0 +
+                  64 * wy + 4 * half;
+      f32x4_t old[2][2][4];   // [row block % 2][jy][q]
+      auto load_old = [&](int i) __attribute__((always_inline)) {
+#pragma unroll
+        for (int jy = 0; jy < 2; ++jy)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            old[i & 1][jy][q] = *reinterpret_cast<const f32x4_t*>(cb + (int64_t)32 * i * p.ldc +
+                                                                  32 * jy + 8 * q);
+      };
+      load_old(0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (i < 3) load_old(i + 1);
+#pragma unroll
+        for (int jy = 0; jy < 2; ++jy)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f32x4_t v = {acc[i][jy][4 * q], acc[i][jy][4 * q + 1], acc[i][jy][4 * q + 2],
+                               acc[i][jy][4 * q + 3]};
+            *reinterpret_cast<f32x4_t*>(cb + (int64_t)32 * i * p.ldc + 32 * jy + 8 * q) =
+                old[i & 1][jy][q] + v;
+          }
+      }
+      return;
+    }
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     __builtin_amdgcn_sched_barrier(0);   // one 32-row block's accumulators live at a time
