@@ -23,12 +23,17 @@
 //    is the MFMA's A operand and the X fragment its B operand, so every
 //    lane's accumulators hold one row x of C: the loss's row statistics need
 //    no cross-lane shuffles beyond one lane swap and one LDS merge.
-//  * K advances 32 at a time through five LDS stages (5 x 32 KiB, all of a
-//    CU's LDS).  Operand tiles reach LDS by direct global-to-LDS copies (no
-//    registers spent on staging), issued four steps ahead of their products
-//    so that a fetch from L2 or the Infinity Cache has two to three steps to
-//    land (measured: the copies, not the LDS reads, are what keeps the
-//    matrix pipe from its peak; one stage fewer is ~6% slower); a k-major tile
+//  * K advances 32 at a time through four LDS stages (4 x 32 KiB; the X
+//    tiles of all stages first, then the Y tiles).  Operand tiles reach LDS
+//    by direct global-to-LDS copies (no registers spent on staging), issued
+//    three steps ahead of their products so that a fetch from L2 or the
+//    Infinity Cache has one to two steps to land (measured: the copies, not
+//    the LDS reads, are what keeps the matrix pipe from its peak).  The step
+//    loop is unrolled by the stage count, so every LDS address is a
+//    per-lane register plus a constant offset (X tiles within 0..64 KiB, Y
+//    tiles within 64..128 KiB) and the 12 to 24 fragment reads of a step
+//    cost no address arithmetic: ~10% faster with a row-major operand,
+//    whose transposing reads are twice as many; a k-major tile
 //    is stored as 256 rows of 4 16-byte chunks, the chunk index XORed with
 //    bits 2-3 of the row, a row-major one as two halves of 32 k-rows x 16
 //    chunks swizzled as in device_common.h (swz), so both the 16-byte row
@@ -57,10 +62,10 @@ namespace ulysses {
 namespace {
 
 constexpr int kBX = 256, kBY = 256, kBK = 32;
-constexpr int kStages = 5;                          // copies run kStages - 1 steps ahead
+constexpr int kStages = 4;                          // copies run kStages - 1 steps ahead
 constexpr int kTileBytes = 256 * kBK * 2;           // 16 KiB per operand and stage
-constexpr int kStageBytes = 2 * kTileBytes;         // X then Y
-constexpr int kSmem = kStages * kStageBytes;        // 160 KiB
+constexpr int kStageBytes = 2 * kTileBytes;         // one X and one Y tile
+constexpr int kSmem = kStages * kStageBytes;        // 128 KiB
 constexpr int kGroupY = 4;                          // y-tiles per group of the tile order
 constexpr int kWaves = 8;
 constexpr int kCopies = kTileBytes / 1024 / kWaves; // wave copies per operand and step
@@ -172,12 +177,16 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmParams p) {
   // Copies of step kt (clamped to the last step: such a copy refills a stage
   // nobody reads again, and keeps every step's count of pending copies the
   // same) into stage kt % kStages.
+  auto xtile = [&](int st) __attribute__((always_inline)) { return smem + st * kTileBytes; };
+  auto ytile = [&](int st) __attribute__((always_inline)) {
+    return smem + (kStages + st) * kTileBytes;
+  };
   auto copy_stage = [&](int kt) __attribute__((always_inline)) {
     const int kc = kt < nk ? kt : nk - 1;
-    char* st = smem + (kt % kStages) * kStageBytes;
-    copy_operand(std::integral_constant<bool, kXK>{}, p.x, p.ldx, p.nx, x0, kc * kBK, st, -1);
+    copy_operand(std::integral_constant<bool, kXK>{}, p.x, p.ldx, p.nx, x0, kc * kBK,
+                 xtile(kt % kStages), -1);
     copy_operand(std::integral_constant<bool, kYK>{}, p.y, p.ldy, p.ny, y0, kc * kBK,
-                 st + kTileBytes, -1);
+                 ytile(kt % kStages), -1);
   };
 
   // ---- fragment reads -----------------------------------------------------
@@ -204,8 +213,8 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmParams p) {
   // Fragments of 16-deep k step ks of stage `stage` into slot bsel.
   bf16x8_t xf[2][4], yf[2][2];
   auto load = [&](int stage, int ks, int bsel) __attribute__((always_inline)) {
-    const char* tx_ = smem + stage * kStageBytes;
-    const char* ty_ = tx_ + kTileBytes;
+    const char* tx_ = xtile(stage);
+    const char* ty_ = ytile(stage);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if constexpr (kXK)
@@ -254,12 +263,12 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmParams p) {
   static_assert(kBK == 32 && kCopies == 2, "two k steps per stage, two copies per operand");
 
   // ---- main loop ----------------------------------------------------------
-  // Step t reads stage t % 5.  Its copies went out during step t - 4; the
+  // Step t reads stage t % 4.  Its copies went out during step t - 3; the
   // barrier after step t - 2 published them (each wave first waits until
-  // only the copies of the two steps after are pending), so during step t - 1
+  // only the copies of the step after are pending), so during step t - 1
   // every wave can already read the first fragments of step t: the barrier
   // after a step does not wait for fragment reads in flight, and no matrix
-  // product waits for a barrier-to-read round trip.  The copies of step t + 4
+  // product waits for a barrier-to-read round trip.  The copies of step t + 3
   // go to the stage step t - 1 read, whose fragments every wave consumed
   // before that barrier.  Copies past the last step are clamped to it (they
   // refill a stage nobody reads again; each step keeps the same count of
@@ -268,21 +277,29 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmParams p) {
   constexpr int kStepCopies = 2 * kCopies;   // per wave and step
 #pragma unroll
   for (int t = 0; t < kStages - 1; ++t) copy_stage(t);
-  wait_vmem_n<(kStages - 3) * kStepCopies>();   // steps 0 and 1 landed (2, 3 may be pending)
+  wait_vmem_n<(kStages - 3) * kStepCopies>();   // steps 0 and 1 landed (2 may be pending)
   block_barrier();
   load(0, 0, 0);
-  for (int kt = 0; kt + 1 < nk; ++kt) {
+  // Step kt, reading stage st = kt % kStages.
+  auto step = [&](int kt, int st) __attribute__((always_inline)) {
     const int cs = kt + kStages - 1;                      // step whose copies go out now
     const int kc = cs < nk ? cs : nk - 1;
-    char* ct = smem + (cs % kStages) * kStageBytes;
-    load(kt % kStages, 1, 1);
-    products(0, std::false_type{}, kt * kBK, std::integral_constant<int, 0>{}, kc, ct);
-    load((kt + 1) % kStages, 0, 0);
+    const int cst = (st + kStages - 1) % kStages;         // its stage
+    load(st, 1, 1);
+    products(0, std::false_type{}, kt * kBK, std::integral_constant<int, 0>{}, kc, xtile(cst));
+    load((st + 1) % kStages, 0, 0);
     products(1, std::false_type{}, kt * kBK + 16, std::integral_constant<int, 1>{}, kc,
-             ct + kTileBytes);
+             ytile(cst));
     wait_vmem_n<(kStages - 3) * kStepCopies>();   // the copies of step kt + 2 landed
     asm volatile("s_barrier" ::: "memory");
+  };
+  // Whole rounds of kStages steps with the stage a constant, then the rest.
+  int kt0 = 0;
+  for (; kt0 + kStages < nk; kt0 += kStages) {
+#pragma unroll
+    for (int u = 0; u < kStages; ++u) step(kt0 + u, u);
   }
+  for (int kt = kt0; kt + 1 < nk; ++kt) step(kt, kt % kStages);
   {
     const int kt = nk - 1;
     load(kt % kStages, 1, 1);
