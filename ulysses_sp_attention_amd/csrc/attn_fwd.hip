@@ -251,12 +251,27 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdParams p) {
   int koff[C::kKS];
 #pragma unroll
   for (int ks = 0; ks < C::kKS; ++ks) koff[ks] = swz<C::kChunks, C::kRowBytes>(r32, 2 * ks + half);
-  const TrReader<C::kChunks, C::kRowBytes, C::kDB> vtr(lane);
+  // The V buffers start past a ds_read's 16-bit offset field (64 KiB at
+  // head size 128).  Their start is folded into the transposing reader's
+  // lane offsets, behind an empty asm so the compiler cannot split it back
+  // out, and V tiles are addressed from the K region's start: every V read
+  // is then a lane register plus an immediate, with no vector add per read.
+  TrReader<C::kChunks, C::kRowBytes, C::kDB> vtr(lane);
+  {
+    int vregion = C::kBufs * C::kTileBytes;
+    asm volatile("" : "+v"(vregion));
+#pragma unroll
+    for (int jh = 0; jh < 2; ++jh)
+#pragma unroll
+      for (int db = 0; db < C::kDB; ++db) vtr.off[jh][db] += vregion;
+  }
   auto kfrag = [&](const char* lk, int idx) __attribute__((always_inline)) {
     const int ks = idx >> 1, kb = idx & 1;
     return *reinterpret_cast<const bf16x8_t*>(lk + kb * 32 * C::kRowBytes + koff[ks]);
   };
-  auto vfrag = [&](const char* lv, int idx) __attribute__((always_inline)) { return vtr.load(lv, 16 * (idx / C::kDB), idx % C::kDB); };
+  auto vfrag = [&](const char* lv, int idx) __attribute__((always_inline)) {
+    return vtr.load(lv - C::kBufs * C::kTileBytes, 16 * (idx / C::kDB), idx % C::kDB);
+  };
   auto matrix_phase = [&](auto qk_tag, auto pv_tag, const char* lk, const char* lv) __attribute__((always_inline)) {
     constexpr bool kQK = decltype(qk_tag)::value;
     constexpr bool kPV = decltype(pv_tag)::value;
