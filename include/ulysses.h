@@ -71,7 +71,12 @@ extern "C" {
 
 #define ULYSSES_ABI_VERSION 7
 
-typedef enum {
+/* Status codes and element types are plain ints (the enumerators below name
+ * their values), so that any value a caller passes in, valid or not, is
+ * defined behaviour: an unknown dtype gets ULYSSES_ERR_DTYPE and an unknown
+ * status "unknown status". */
+typedef int ulysses_status_t;
+enum {
   ULYSSES_OK = 0,
   ULYSSES_ERR_NULL = 1,           /* a required pointer is NULL */
   ULYSSES_ERR_SHAPE = 2,          /* non-positive size, or head_dim not supported */
@@ -81,12 +86,13 @@ typedef enum {
   ULYSSES_ERR_UNSUPPORTED = 6,    /* valid request this build does not implement */
   ULYSSES_ERR_WORKSPACE = 7,      /* workspace NULL or smaller than required */
   ULYSSES_ERR_HIP = 8             /* kernel launch failed */
-} ulysses_status_t;
+};
 
-typedef enum {
+typedef int ulysses_dtype_t;
+enum {
   ULYSSES_BF16 = 0,   /* bfloat16 storage, fp32 accumulation */
   ULYSSES_FP32 = 1    /* float32 storage and arithmetic */
-} ulysses_dtype_t;
+};
 
 /* ABI version of the loaded library (ULYSSES_ABI_VERSION it was built with). */
 int ulysses_abi_version(void);

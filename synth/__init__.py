@@ -20,6 +20,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "synth.c")
 _LIB_PATH = os.path.join(_HERE, "libsynth.so")
+# The host-sanitizer test (tests/test_sanitizers.py) loads an instrumented
+# build of synth.c through this; nothing else sets it.
+_LIB_OVERRIDE = os.environ.get("ULYSSES_SYNTH_LIB")
 _lib = None
 
 # Stream ids of the seeded inputs.
@@ -55,9 +58,12 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB_PATH):
-        build_lib()
-    lib = ctypes.CDLL(_LIB_PATH)
+    if _LIB_OVERRIDE:
+        lib = ctypes.CDLL(_LIB_OVERRIDE)
+    else:
+        if not os.path.exists(_LIB_PATH):
+            build_lib()
+        lib = ctypes.CDLL(_LIB_PATH)
     u64, i64, dbl, vp = ctypes.c_uint64, ctypes.c_int64, ctypes.c_double, ctypes.c_void_p
     lib.synth_words.argtypes = [u64, u64, u64, i64, vp]
     lib.synth_splitmix64_sequence.argtypes = [u64, i64, vp]

@@ -21,7 +21,10 @@ import ctypes
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libulysses.so")
+# ULYSSES_LIB loads another build of the same library instead (the
+# host-sanitizer build that tests/test_sanitizers.py makes); nothing else
+# sets it.
+LIB_PATH = os.environ.get("ULYSSES_LIB") or os.path.join(_PKG, "libulysses.so")
 
 OK, ERR_NULL, ERR_SHAPE, ERR_DIVISIBILITY, ERR_DTYPE, ERR_ALIGNMENT, ERR_UNSUPPORTED, \
     ERR_WORKSPACE, ERR_HIP = range(9)
