@@ -238,8 +238,11 @@ ulysses_status_t ulysses_attn_fwd_fused(const void* const* q_chunks, const void*
                                         const int32_t* cu_seqlens, int n_docs,
                                         void* const* o_chunks, float* lse, hipStream_t stream);
 
-/* Bytes of device workspace ulysses_attn_bwd needs for these sizes (the
- * per-row statistics of the backward below; 0 for sizes it rejects). */
+/* Bytes of device workspace ulysses_attn_bwd needs for these sizes: the
+ * per-row statistics of the backward below and, in bf16 when the 128-key
+ * blocks number fewer than 1024 (seqlen * bs * hkv < 131072), the fp32
+ * partial dK/dV of its split key blocks (2 or 4 parts of 8 bytes per key,
+ * KV head and head-dim element); 0 for sizes it rejects. */
 size_t ulysses_attn_bwd_workspace_size(int64_t seqlen, int bs, int hq, int hkv, int head_dim,
                                        ulysses_dtype_t dtype);
 
@@ -259,7 +262,10 @@ size_t ulysses_attn_bwd_workspace_size(int64_t seqlen, int bs, int hq, int hkv, 
  * dq has q's layout, dk/dv have k's; all in `dtype`.  Other arguments as in
  * ulysses_attn_fwd.  `workspace` is device memory of at least
  * ulysses_attn_bwd_workspace_size(...) bytes, 256-byte aligned, whose
- * contents on entry do not matter.  dq, dk, dv are fully overwritten.
+ * contents on entry do not matter.  dq, dk, dv are fully overwritten.  In
+ * bf16 with few key blocks, each block's queries are shared over 2 or 4
+ * workgroups whose fp32 partial dK/dV are added in a fixed order, so the
+ * results stay bitwise reproducible for given sizes.
  */
 ulysses_status_t ulysses_attn_bwd(const void* q, const void* k, const void* v, const void* o,
                                   const float* lse, const void* dout, int64_t seqlen, int bs,
@@ -276,9 +282,13 @@ ulysses_status_t ulysses_attn_bwd(const void* q, const void* k, const void* v, c
  * holds on every GPU it runs on until the process ends.  The call itself
  * allocates and frees nothing.
  *   Arguments, results and errors as in ulysses_attn_bwd, plus
- *   ULYSSES_ERR_WORKSPACE when ulysses_attn_bwd_workspace_size(...) of these
- *   sizes exceeds ULYSSES_NOALLOC_SCRATCH_BYTES (bf16: seqlen * bs * hq up
- *   to 2^21 rows; fp32: 2^22), with nothing launched.
+ *   ULYSSES_ERR_WORKSPACE when the statistics of these sizes exceed
+ *   ULYSSES_NOALLOC_SCRATCH_BYTES (bf16: seqlen * bs * hq up to 2^21 rows;
+ *   fp32: 2^22), with nothing launched.  When the bf16 dK/dV split's
+ *   partials do not fit beside the statistics, dK/dV run unsplit here: they
+ *   may then differ from ulysses_attn_bwd's in the last bit (the order of one
+ *   fp32 sum), within the same accuracy; otherwise both calls give the same
+ *   bits.
  * All calls on one GPU share its scratch array: calls that overlap in time
  * on one GPU (several streams or host threads) race and give wrong results;
  * calls ordered on one stream are safe.  The array's contents left by one

@@ -1,15 +1,20 @@
 """The backward entry point that allocates nothing (ulysses_attn_bwd_noalloc),
 through the C-ABI, against the workspace entry point (ulysses_attn_bwd) it
-varies: the same kernels with the statistics in the library's fixed per-GPU
-scratch instead of a caller's workspace, so the gradients must agree bit for
-bit (which is within every parity bar).  Two calls in a row on the shared
-scratch, the second smaller, each checked; then the first again, to show
-that the contents a smaller call leaves behind do not matter."""
+varies: the same kernels with the statistics (and, where they fit, the dK/dV
+split's partials) in the library's fixed per-GPU scratch instead of a
+caller's workspace.  Where the split's partials fit the scratch both run the
+same launches and must agree bit for bit (which is within every parity
+bar): two calls in a row on the shared scratch, the second smaller, each
+checked; then the first again, to show that the contents a smaller call
+leaves behind do not matter.  Where they do not fit, the scratch entry point
+runs dK/dV unsplit, which changes the order of one fp32 sum: both results are
+then held to the parity bar against the oracle."""
 import numpy as np
 import pytest
 
+import oracle
 import synth
-from helpers import ensure_library, storage_bytes, to_device
+from helpers import assert_grads_close, ensure_library, storage_bytes, to_device, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -27,7 +32,8 @@ def case_inputs(N, hq, hkv, hd, dtype, seed):
     return q, k, v, do
 
 
-def run_case(N, hq, hkv, hd, dtype, cu, seed):
+def run_both(N, hq, hkv, hd, dtype, cu, seed):
+    """(inputs, workspace-entry-point gradients, scratch-entry-point gradients)."""
     import torch
     import ulysses_sp_attention_amd as uly
     q, k, v, do = case_inputs(N, hq, hkv, hd, dtype, seed)
@@ -44,14 +50,21 @@ def run_case(N, hq, hkv, hd, dtype, cu, seed):
     got = [torch.full_like(t, float("nan")) for t in (q, k, v)]
     uly.ulysses_attn_bwd_noalloc(q, k, v, o, lse, do, *got, scale, True, cu_t)
     torch.cuda.synchronize()
+    for name, g in zip(("dq", "dk", "dv"), got):
+        assert not torch.isnan(g.float()).any(), name
+    return (q, k, v, do, scale), want, got
+
+
+def run_case(N, hq, hkv, hd, dtype, cu, seed):
+    _, want, got = run_both(N, hq, hkv, hd, dtype, cu, seed)
     for name, g, w in zip(("dq", "dk", "dv"), got, want):
         assert storage_bytes(g) == storage_bytes(w), f"{name} differs at N={N}"
-        assert not torch.isnan(g.float()).any(), name
 
 
 CASES = [
-    # N, hq, hkv, hd, dtype, cu: the 32K share's head counts at 16K rows, then smaller
-    (16384, 4, 1, 128, "bf16", None),
+    # N, hq, hkv, hd, dtype, cu: the 32K share's head counts at 2K rows (the
+    # dK/dV split's partials, 8 MiB, fit the scratch), then smaller
+    (2048, 4, 1, 128, "bf16", None),
     (777, 8, 2, 64, "bf16", [0, 100, 101, 777]),
 ]
 
@@ -62,6 +75,21 @@ def test_noalloc_backward_equals_workspace_backward_two_calls():
     # the large case again, after the smaller one left its statistics behind
     N, hq, hkv, hd, dtype, cu = CASES[0]
     run_case(N, hq, hkv, hd, dtype, cu, seed=900)
+
+
+def test_noalloc_backward_unsplit_when_partials_do_not_fit():
+    """At 4160 rows of 4 heads the split's fp32 partials (17 MB) exceed the
+    16 MiB scratch: the scratch entry point runs dK/dV unsplit and the two
+    entry points' dK/dV may differ in the last bit; dQ (no split) agrees bit
+    for bit, and both sets of gradients meet the parity bar against the
+    oracle, end to end from the same GPU forward."""
+    N, hq, hkv, hd = 4160, 4, 1, 128
+    (q, k, v, do, scale), want, got = run_both(N, hq, hkv, hd, "bf16", None, seed=907)
+    assert storage_bytes(got[0]) == storage_bytes(want[0])
+    ref = oracle.attn_bwd(to_f64(q), to_f64(k), to_f64(v), to_f64(do), scale, True, None,
+                          magnitude=True)
+    for what, grads in (("workspace entry point", want), ("scratch entry point", got)):
+        assert_grads_close("bf16", *(to_f64(t) for t in grads), ref, what)
 
 
 def test_noalloc_backward_fp32():

@@ -279,10 +279,10 @@ ulysses_status_t check_attn_bwd(const void* q, const void* k, const void* v, con
 ulysses_status_t attn_bwd_launch(const AttnShape& s, ulysses_dtype_t dtype, const void* q,
                                  const void* k, const void* v, const void* o, const float* lse,
                                  const void* dout, void* dq, void* dk, void* dv, void* workspace,
-                                 hipStream_t stream) {
+                                 size_t workspace_bytes, hipStream_t stream) {
   if (dtype == ULYSSES_BF16)
     return from_hip(ulysses::launch_attn_bwd_bf16(s, q, k, v, o, lse, dout, dq, dk, dv, workspace,
-                                                  stream));
+                                                  workspace_bytes, stream));
   return from_hip(ulysses::launch_attn_bwd_f32(
       s, static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
       static_cast<const float*>(o), lse, static_cast<const float*>(dout), static_cast<float*>(dq),
@@ -305,7 +305,8 @@ ulysses_status_t ulysses_attn_bwd(const void* q, const void* k, const void* v, c
   if (seqlen > 0 && (workspace == nullptr || workspace_bytes < need)) return ULYSSES_ERR_WORKSPACE;
   if (seqlen > 0 && !aligned16(workspace)) return ULYSSES_ERR_ALIGNMENT;
   if (seqlen == 0) return ULYSSES_OK;
-  return attn_bwd_launch(s, dtype, q, k, v, o, lse, dout, dq, dk, dv, workspace, stream);
+  return attn_bwd_launch(s, dtype, q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes,
+                         stream);
 }
 
 ulysses_status_t ulysses_attn_bwd_noalloc(const void* q, const void* k, const void* v,
@@ -318,12 +319,16 @@ ulysses_status_t ulysses_attn_bwd_noalloc(const void* q, const void* k, const vo
   ulysses_status_t st = check_attn_bwd(q, k, v, o, lse, dout, seqlen, bs, hq, hkv, head_dim, dtype,
                                        softmax_scale, causal, cu_seqlens, n_docs, dq, dk, dv, &s);
   if (st != ULYSSES_OK) return st;
-  if (ulysses::attn_bwd_workspace_bytes(s, dtype == ULYSSES_BF16) > ulysses::noalloc_scratch_bytes())
+  // The statistics must fit the scratch; the dK/dV split's partials are
+  // used only when they fit too.
+  if (ulysses::attn_bwd_min_workspace_bytes(s, dtype == ULYSSES_BF16) >
+      ulysses::noalloc_scratch_bytes())
     return ULYSSES_ERR_WORKSPACE;
   if (seqlen == 0) return ULYSSES_OK;
   void* scratch = nullptr;
   if (ulysses::noalloc_scratch(&scratch) != hipSuccess) return ULYSSES_ERR_HIP;
-  return attn_bwd_launch(s, dtype, q, k, v, o, lse, dout, dq, dk, dv, scratch, stream);
+  return attn_bwd_launch(s, dtype, q, k, v, o, lse, dout, dq, dk, dv, scratch,
+                         ulysses::noalloc_scratch_bytes(), stream);
 }
 
 ulysses_status_t ulysses_attn_merge(const void* o_a, const float* lse_a, const void* o_b,
@@ -411,7 +416,8 @@ ulysses_status_t ulysses_attn_bwd_fused(
   return from_hip(ulysses::launch_attn_bwd_bf16_fused(
       s, table(q_chunks, hq, q0), table(k_chunks, hkv, kv0), table(v_chunks, hkv, kv0),
       table(o_chunks, hq, q0), lse, table(do_chunks, hq, q0), out_table(dq_chunks, hq, q0),
-      out_table(dk_chunks, hkv, kv0), out_table(dv_chunks, hkv, kv0), workspace, stream));
+      out_table(dk_chunks, hkv, kv0), out_table(dv_chunks, hkv, kv0), workspace,
+      workspace_bytes, stream));
 }
 
 size_t ulysses_logits_loss_workspace_size(int64_t shard_rows, int64_t vocab) {

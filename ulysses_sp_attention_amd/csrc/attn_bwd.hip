@@ -41,6 +41,21 @@ size_t stat_array_bytes(const AttnShape& s) {
   return ((size_t)s.N * s.bs * s.hq * sizeof(float) + 255) / 256 * 256;
 }
 
+// dK/dV split.  With fewer than four workgroups of 128-key blocks per CU,
+// the long early key blocks of a causal share (the first sees every query,
+// the last only its own tile) set the kernel's time.  Each key block's
+// query tiles are then shared out, in contiguous runs, over `split`
+// workgroups, which write fp32 partial dK/dV to the workspace; a reduction
+// adds the parts in a fixed order (bitwise reproducible) and rounds once.
+int dkv_split(const AttnShape& s) {
+  const int64_t blocks = (s.N + 127) / 128 * s.bs * s.hkv;
+  return blocks >= 1024 ? 1 : (blocks >= 512 ? 2 : 4);
+}
+size_t dkv_part_bytes(const AttnShape& s, int split) {
+  if (split <= 1) return 0;
+  return ((size_t)split * 2 * s.bs * s.hkv * s.N * s.hd * sizeof(float) + 255) / 256 * 256;
+}
+
 struct BwdParams {
   const __bf16* q;
   const __bf16* k;
@@ -63,6 +78,10 @@ struct BwdParams {
   const int32_t* cu;
   int n_docs;
   int64_t num_blocks;
+  // dK/dV split (dkv_split): parts per key block, and with split > 1 the
+  // fp32 partials [part][dK, dV][batch][kv head][position][head dim].
+  int split;
+  float* dkv_part;
   // Fused form only: the operands in their sequence chunks (the pointers
   // above, except the statistics, are unused).
   SeqChunks cq, ck, cv, cdo, cdq, cdk, cdv;
@@ -533,7 +552,11 @@ __global__ __launch_bounds__(512) void attn_bwd_dkv_kernel(BwdParams p) {
   const int64_t N = wave_uniform(p.N);
   const int kh = blockIdx.y % p.hkv;
   const int b = blockIdx.y / p.hkv;
-  const int64_t k0 = (int64_t)blockIdx.x * C::kBK;   // heaviest (smallest keys) first
+  // Workgroup x = key block * split + part: heaviest (smallest keys) first,
+  // the parts of a block next to each other.
+  const int split = p.split;
+  const int part = (int)(blockIdx.x % (uint32_t)split);
+  const int64_t k0 = (int64_t)(blockIdx.x / (uint32_t)split) * C::kBK;
   const int64_t kw = k0 + 32 * pair;                // first key of the block
   const int64_t kj = kw + r32;                      // this lane's key
 
@@ -563,8 +586,13 @@ __global__ __launch_bounds__(512) void attn_bwd_dkv_kernel(BwdParams p) {
   const int64_t k_last = (k0 + C::kBK < N ? k0 + C::kBK : N) - 1;
   const int64_t q_lo = p.causal ? k0 : doc_start_of(p.cu, p.n_docs, k0);
   const int64_t q_hi = doc_end_of(p.cu, p.n_docs, k_last, N);
-  const int qt_lo = (int)wave_uniform(q_lo / C::kBQ);
-  const int qt_hi = (int)wave_uniform((q_hi + C::kBQ - 1) / C::kBQ);
+  const int qt_blo = (int)wave_uniform(q_lo / C::kBQ);
+  const int qt_bhi = (int)wave_uniform((q_hi + C::kBQ - 1) / C::kBQ);
+  // This part's contiguous run of the block's query tiles (all of them
+  // without a split).
+  const int64_t nt = qt_bhi - qt_blo;
+  const int qt_lo = qt_blo + (int)(nt * part / split);
+  const int qt_hi = qt_blo + (int)(nt * (part + 1) / split);
   const int n_steps = (qt_hi - qt_lo) * p.g;
   const int t_tail = (int)wave_uniform(N / C::kBQ);   // tiles from here on run past N
   // Query positions from here on are relative to the first query tile
@@ -968,19 +996,70 @@ __global__ __launch_bounds__(512) void attn_bwd_dkv_kernel(BwdParams p) {
   wait_vmem();
 
   if (kj < N) {
-    __bf16* row = kFused ? chunk_row(p_wave ? p.cdv : p.cdk, (uint32_t)kj, p.bs, b, kh, HD)
-                         : (p_wave ? p.dv : p.dk) + kj * kv_tok + kvoff;
     const float mul = p_wave ? 1.f : p.scale;
+    if (split > 1) {   // fp32 partial of this part
+      float* row = p.dkv_part +
+                   ((((int64_t)part * 2 + (p_wave ? 1 : 0)) * p.bs + b) * p.hkv + kh) * N * HD +
+                   kj * HD;
 #pragma unroll
-    for (int d = 0; d < C::kDB; ++d)
+      for (int d = 0; d < C::kDB; ++d)
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        bf16x4_t w;
+        for (int r4 = 0; r4 < 4; ++r4) {
+          f32x4_t w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = (__bf16)(acc[d][4 * r4 + e] * mul);
-        *reinterpret_cast<bf16x4_t*>(row + d * 32 + 8 * r4 + 4 * half) = w;
-      }
+          for (int e = 0; e < 4; ++e) w[e] = acc[d][4 * r4 + e] * mul;
+          *reinterpret_cast<f32x4_t*>(row + d * 32 + 8 * r4 + 4 * half) = w;
+        }
+    } else {
+      __bf16* row = kFused ? chunk_row(p_wave ? p.cdv : p.cdk, (uint32_t)kj, p.bs, b, kh, HD)
+                           : (p_wave ? p.dv : p.dk) + kj * kv_tok + kvoff;
+#pragma unroll
+      for (int d = 0; d < C::kDB; ++d)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          bf16x4_t w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = (__bf16)(acc[d][4 * r4 + e] * mul);
+          *reinterpret_cast<bf16x4_t*>(row + d * 32 + 8 * r4 + 4 * half) = w;
+        }
+    }
   }
+}
+
+// dK and dV from the split's fp32 partials: parts added in order 0, 1, ...
+// and rounded once to bf16.  One thread per 4 consecutive head-dim values
+// of a (tensor, batch, kv head, key) row.
+template <int HD, bool kFused>
+__global__ __launch_bounds__(256) void dkv_reduce_kernel(BwdParams p) {
+  constexpr int kQuads = HD / 4;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t N = p.N;
+  const int64_t rows = 2 * (int64_t)p.bs * p.hkv * N;
+  if (i >= rows * kQuads) return;
+  const int qd = (int)(i % kQuads);
+  int64_t r = i / kQuads;
+  const int64_t kj = r % N;
+  r /= N;
+  const int kh = (int)(r % p.hkv);
+  r /= p.hkv;
+  const int b = (int)(r % p.bs);
+  const int tensor = (int)(r / p.bs);   // 0: dK, 1: dV
+  const int64_t plane = rows * HD;      // floats per part
+  const float* src = p.dkv_part + (((int64_t)tensor * p.bs + b) * p.hkv + kh) * N * HD + kj * HD + 4 * qd;
+  f32x4_t sum = *reinterpret_cast<const f32x4_t*>(src);
+  for (int part = 1; part < p.split; ++part) {
+    const f32x4_t x = *reinterpret_cast<const f32x4_t*>(src + part * plane);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sum[e] += x[e];
+  }
+  bf16x4_t w;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) w[e] = (__bf16)sum[e];
+  const int64_t kv_tok = (int64_t)p.bs * p.kv_row_heads * HD;
+  const int64_t kvoff = ((int64_t)b * p.kv_row_heads + kh) * HD;
+  __bf16* row = kFused ? chunk_row(tensor ? p.cdv : p.cdk, (uint32_t)kj, p.bs, b, kh, HD)
+                       : (tensor ? p.dv : p.dk) + kj * kv_tok + kvoff;
+  *reinterpret_cast<bf16x4_t*>(row + 4 * qd) = w;
 }
 
 // -D_i = -<dO_i, O_i> and -LSE_i / scale of every query row, stored
@@ -1035,11 +1114,18 @@ hipError_t launch_dq(BwdParams p, const AttnShape& s, hipStream_t stream) {
 // statistics) feed the statistics.
 template <bool kFused, bool kStatsFused = kFused>
 hipError_t launch_bwd(BwdParams& p, const AttnShape& s, const __bf16* o, const SeqChunks& co,
-                      const float* lse, void* workspace, hipStream_t stream) {
+                      const float* lse, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
   float* nD = static_cast<float*>(workspace);
   float* nlse_r = reinterpret_cast<float*>(static_cast<char*>(workspace) + stat_array_bytes(s));
   p.nD = nD;
   p.nlse_r = nlse_r;
+  // The split runs when the workspace holds its partials (always for a
+  // workspace of attn_bwd_workspace_bytes; the fixed scratch of the
+  // allocation-free entry point may not).
+  p.split = dkv_split(s);
+  if (2 * stat_array_bytes(s) + dkv_part_bytes(s, p.split) > workspace_bytes) p.split = 1;
+  p.dkv_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + 2 * stat_array_bytes(s));
   p.N = s.N;
   p.bs = s.bs;
   p.hq = s.hq;
@@ -1072,8 +1158,14 @@ hipError_t launch_bwd(BwdParams& p, const AttnShape& s, const __bf16* o, const S
   auto dkv_launch = [&](auto hd_tag) -> hipError_t {
     constexpr int HD = decltype(hd_tag)::value;
     using C = DkvCfg<HD>;
-    dim3 grid((uint32_t)((s.N + C::kBK - 1) / C::kBK), (uint32_t)(s.bs * s.hkv));
-    return launch_kernel(attn_bwd_dkv_kernel<HD, kFused>, grid, dim3(C::kThreads), 0, stream, p);
+    static_assert(C::kBK == 128, "dkv_split counts 128-key blocks");
+    dim3 grid((uint32_t)((s.N + C::kBK - 1) / C::kBK * p.split), (uint32_t)(s.bs * s.hkv));
+    hipError_t e2 = launch_kernel(attn_bwd_dkv_kernel<HD, kFused>, grid, dim3(C::kThreads), 0,
+                                  stream, p);
+    if (e2 != hipSuccess || p.split == 1) return e2;
+    const int64_t quads = 2 * (int64_t)s.bs * s.hkv * s.N * (HD / 4);
+    return launch_kernel(dkv_reduce_kernel<HD, kFused>, dim3((uint32_t)((quads + 255) / 256)),
+                         dim3(256), 0, stream, p);
   };
   if (s.hd == 128) {
     if ((e = dq_launch(std::integral_constant<int, 128>{})) != hipSuccess) return e;
@@ -1087,12 +1179,18 @@ hipError_t launch_bwd(BwdParams& p, const AttnShape& s, const __bf16* o, const S
 
 
 size_t attn_bwd_workspace_bytes(const AttnShape& s, bool bf16) {
+  if (!bf16) return stat_array_bytes(s);
+  return 2 * stat_array_bytes(s) + dkv_part_bytes(s, dkv_split(s));
+}
+
+size_t attn_bwd_min_workspace_bytes(const AttnShape& s, bool bf16) {
   return (bf16 ? 2 : 1) * stat_array_bytes(s);
 }
 
 hipError_t launch_attn_bwd_bf16(const AttnShape& s, const void* q, const void* k, const void* v,
                                 const void* o, const float* lse, const void* dout, void* dq,
-                                void* dk, void* dv, void* workspace, hipStream_t stream) {
+                                void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
   if (s.N == 0) return hipSuccess;
   BwdParams p{};
   p.q = static_cast<const __bf16*>(q);
@@ -1102,14 +1200,15 @@ hipError_t launch_attn_bwd_bf16(const AttnShape& s, const void* q, const void* k
   p.dq = static_cast<__bf16*>(dq);
   p.dk = static_cast<__bf16*>(dk);
   p.dv = static_cast<__bf16*>(dv);
-  return launch_bwd<false>(p, s, static_cast<const __bf16*>(o), p.cq, lse, workspace, stream);
+  return launch_bwd<false>(p, s, static_cast<const __bf16*>(o), p.cq, lse, workspace,
+                           workspace_bytes, stream);
 }
 
 hipError_t launch_attn_bwd_bf16_fused(const AttnShape& s, const SeqChunks& q, const SeqChunks& k,
                                       const SeqChunks& v, const SeqChunks& o, const float* lse,
                                       const SeqChunks& dout, const SeqChunks& dq,
                                       const SeqChunks& dk, const SeqChunks& dv, void* workspace,
-                                      hipStream_t stream) {
+                                      size_t workspace_bytes, hipStream_t stream) {
   if (s.N == 0) return hipSuccess;
   BwdParams p{};
   p.cdo = dout;   // the statistics read O and dO from their chunks either way
@@ -1132,7 +1231,7 @@ hipError_t launch_attn_bwd_bf16_fused(const AttnShape& s, const SeqChunks& q, co
     p.dv = reinterpret_cast<__bf16*>(base[6]);
     p.q_row_heads = q.row_heads;
     p.kv_row_heads = k.row_heads;
-    return launch_bwd<false, true>(p, s, nullptr, o, lse, workspace, stream);
+    return launch_bwd<false, true>(p, s, nullptr, o, lse, workspace, workspace_bytes, stream);
   }
   p.cq = q;
   p.ck = k;
@@ -1141,7 +1240,7 @@ hipError_t launch_attn_bwd_bf16_fused(const AttnShape& s, const SeqChunks& q, co
   p.cdq = dq;
   p.cdk = dk;
   p.cdv = dv;
-  return launch_bwd<true>(p, s, nullptr, o, lse, workspace, stream);
+  return launch_bwd<true>(p, s, nullptr, o, lse, workspace, workspace_bytes, stream);
 }
 
 }  // namespace ulysses

@@ -101,6 +101,9 @@ hipError_t launch_attn_fwd_f32(const AttnShape& s, const float* q, const float* 
                                float* o, float* lse, hipStream_t stream);
 
 size_t attn_bwd_workspace_bytes(const AttnShape& s, bool bf16);
+// The statistics alone: a smaller workspace runs the bf16 dK/dV kernel
+// without its split (same results up to the order of one fp32 sum).
+size_t attn_bwd_min_workspace_bytes(const AttnShape& s, bool bf16);
 
 // The fixed per-GPU scratch of ulysses_attn_bwd_noalloc (noalloc.hip): its
 // size, and its device address on the current device (looked up once per
@@ -109,14 +112,15 @@ size_t noalloc_scratch_bytes();
 hipError_t noalloc_scratch(void** out);
 hipError_t launch_attn_bwd_bf16(const AttnShape& s, const void* q, const void* k, const void* v,
                                 const void* o, const float* lse, const void* dout, void* dq,
-                                void* dk, void* dv, void* workspace, hipStream_t stream);
+                                void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream);
 // The backward with every operand in its sequence chunks (dq, dk, dv written
 // into the rank's head slots).
 hipError_t launch_attn_bwd_bf16_fused(const AttnShape& s, const SeqChunks& q, const SeqChunks& k,
                                       const SeqChunks& v, const SeqChunks& o, const float* lse,
                                       const SeqChunks& dout, const SeqChunks& dq,
                                       const SeqChunks& dk, const SeqChunks& dv, void* workspace,
-                                      hipStream_t stream);
+                                      size_t workspace_bytes, hipStream_t stream);
 hipError_t launch_attn_bwd_f32(const AttnShape& s, const float* q, const float* k, const float* v,
                                const float* o, const float* lse, const float* dout, float* dq,
                                float* dk, float* dv, void* workspace, hipStream_t stream);
