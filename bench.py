@@ -344,8 +344,10 @@ def measure_config(w, uly, torch, np, stream, args):
     import synth
     N, hl, kl, hd = w.seqlen, w.hq_local, w.hkv_local, w.head_dim
     bf = torch.bfloat16
-    reps = max(args.steps, 5)
-    warm = max(1, min(args.warmup, 3))
+    # The measurement plan's counts: at least 20 timed iterations (5 for the
+    # 256K forward, 55 ms each) after 3 warm-up calls.
+    reps = max(args.steps, 5 if N >= 262144 else 20)
+    warm = max(3, args.warmup)
     cu = w.cu_seqlens()
     cu_t = None if cu is None else torch.tensor(cu, dtype=torch.int32, device="cuda")
     pairs = w.causal_pairs()
