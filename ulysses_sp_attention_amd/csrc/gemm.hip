@@ -84,6 +84,11 @@ struct GemmParams {
   float* stats;              // loss epilogue: [nx][tiles_y] x (max, sum exp(z - max))
   const int64_t* labels;     // loss epilogue: label of row x; C[x][label] goes to zlabel[x]
   float* zlabel;
+  // Second product of a pair launch (grid z = 1): same sizes, layouts and
+  // output mode, its own operands and output.
+  const __bf16* x2;
+  const __bf16* y2;
+  void* c2;
   int tiles_x, tiles_y;
 };
 
@@ -110,6 +115,10 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // Operands and output of this product (blockIdx.z of a pair launch).
+  const __bf16* const gx = blockIdx.z ? p.x2 : p.x;
+  const __bf16* const gy = blockIdx.z ? p.y2 : p.y;
+  void* const gc = blockIdx.z ? p.c2 : p.c;
   const int half = lane >> 5;
   const int r32 = lane & 31;
   const int wx = wave & 1;    // X rows 128 wx ..
@@ -183,9 +192,9 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmParams p) {
   };
   auto copy_stage = [&](int kt) __attribute__((always_inline)) {
     const int kc = kt < nk ? kt : nk - 1;
-    copy_operand(std::integral_constant<bool, kXK>{}, p.x, p.ldx, p.nx, x0, kc * kBK,
+    copy_operand(std::integral_constant<bool, kXK>{}, gx, p.ldx, p.nx, x0, kc * kBK,
                  xtile(kt % kStages), -1);
-    copy_operand(std::integral_constant<bool, kYK>{}, p.y, p.ldy, p.ny, y0, kc * kBK,
+    copy_operand(std::integral_constant<bool, kYK>{}, gy, p.ldy, p.ny, y0, kc * kBK,
                  ytile(kt % kStages), -1);
   };
 
@@ -251,10 +260,10 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmParams p) {
       for (int jy = 0; jy < 2; ++jy) acc[i][jy] = mfma32(yf[bsel][jy], xf[bsel][i], acc[i][jy]);
       if (i & 1) {
         if constexpr (kCopy == 0)
-          copy_operand(std::integral_constant<bool, kXK>{}, p.x, p.ldx, p.nx, x0, kc * kBK,
+          copy_operand(std::integral_constant<bool, kXK>{}, gx, p.ldx, p.nx, x0, kc * kBK,
                        copy_tile, i >> 1);
         else if constexpr (kCopy == 1)
-          copy_operand(std::integral_constant<bool, kYK>{}, p.y, p.ldy, p.ny, y0, kc * kBK,
+          copy_operand(std::integral_constant<bool, kYK>{}, gy, p.ldy, p.ny, y0, kc * kBK,
                        copy_tile, i >> 1);
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -380,7 +389,7 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmParams p) {
     // i + 1 are loaded before block i is stored back, so each load's latency
     // overlaps the previous block's adds and stores.
     if (x0 + 128 * wx + 128 <= p.nx && y0 + 64 * wy + 64 <= p.ny) {
-      float* cb = static_cast<float*>(p.c) + (int64_t)(x0 + 128 * wx + r32) * p.ldc + y0 +
+      float* cb = static_cast<float*>(gc) + (int64_t)(x0 + 128 * wx + r32) * p.ldc + y0 +
                   64 * wy + 4 * half;
       f32x4_t old[2][2][4];   // [row block % 2][jy][q]
       auto load_old = [&](int i) __attribute__((always_inline)) {
@@ -421,7 +430,7 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmParams p) {
         const f32x4_t v = {acc[i][jy][4 * q], acc[i][jy][4 * q + 1], acc[i][jy][4 * q + 2],
                            acc[i][jy][4 * q + 3]};
         if constexpr (kOut == kStoreBF16) {
-          __bf16* cp = static_cast<__bf16*>(p.c) + (int64_t)x * p.ldc + y;
+          __bf16* cp = static_cast<__bf16*>(gc) + (int64_t)x * p.ldc + y;
           if (y + 3 < p.ny) {
             bf16x4_t o;
 #pragma unroll
@@ -433,7 +442,7 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmParams p) {
               if (y + e < p.ny) cp[e] = (__bf16)v[e];
           }
         } else {
-          float* cp = static_cast<float*>(p.c) + (int64_t)x * p.ldc + y;
+          float* cp = static_cast<float*>(gc) + (int64_t)x * p.ldc + y;
           if (y + 3 < p.ny) {
             if constexpr (kOut == kAccumF32) {
               const f32x4_t old = *reinterpret_cast<const f32x4_t*>(cp);
@@ -452,8 +461,9 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmParams p) {
 }
 
 template <bool kXK, bool kYK>
-hipError_t launch_layout(const GemmParams& p, int out, bool stats, hipStream_t stream) {
-  const dim3 grid((uint32_t)(p.tiles_x * p.tiles_y)), block(512);
+hipError_t launch_layout(const GemmParams& p, int out, bool stats, int products,
+                         hipStream_t stream) {
+  const dim3 grid((uint32_t)(p.tiles_x * p.tiles_y), 1, (uint32_t)products), block(512);
   if (stats) {
     if constexpr (kXK && kYK)
       return launch_kernel(gemm_bf16_kernel<true, true, kStoreBF16, true>, grid, block, 0, stream, p);
@@ -474,9 +484,9 @@ hipError_t launch_layout(const GemmParams& p, int out, bool stats, hipStream_t s
 
 int gemm_tiles_y(int64_t ny) { return (int)((ny + kBY - 1) / kBY); }
 
-hipError_t launch_gemm(const GemmOp& op, hipStream_t stream) {
-  if (op.nx <= 0 || op.ny <= 0) return hipSuccess;
-  if (op.K <= 0) return hipErrorInvalidValue;   // callers never ask for an empty sum
+namespace {
+
+GemmParams make_params(const GemmOp& op) {
   GemmParams p{};
   p.x = static_cast<const __bf16*>(op.x.p);
   p.y = static_cast<const __bf16*>(op.y.p);
@@ -492,13 +502,44 @@ hipError_t launch_gemm(const GemmOp& op, hipStream_t stream) {
   p.zlabel = op.label_logit;
   p.tiles_x = (int)((op.nx + kBX - 1) / kBX);
   p.tiles_y = gemm_tiles_y(op.ny);
+  return p;
+}
+
+hipError_t launch_params(const GemmOp& op, const GemmParams& p, int products, hipStream_t stream) {
   const int out = op.accumulate ? kAccumF32 : (op.c_bf16 ? kStoreBF16 : kStoreF32);
   if (op.stats != nullptr && (out != kStoreBF16 || op.labels == nullptr || op.label_logit == nullptr))
     return hipErrorInvalidValue;
-  if (op.x.kmajor && op.y.kmajor) return launch_layout<true, true>(p, out, op.stats != nullptr, stream);
-  if (op.x.kmajor && !op.y.kmajor) return launch_layout<true, false>(p, out, false, stream);
-  if (!op.x.kmajor && !op.y.kmajor) return launch_layout<false, false>(p, out, false, stream);
-  return launch_layout<false, true>(p, out, false, stream);
+  const bool st = op.stats != nullptr;
+  if (op.x.kmajor && op.y.kmajor) return launch_layout<true, true>(p, out, st, products, stream);
+  if (op.x.kmajor && !op.y.kmajor) return launch_layout<true, false>(p, out, false, products, stream);
+  if (!op.x.kmajor && !op.y.kmajor) return launch_layout<false, false>(p, out, false, products, stream);
+  return launch_layout<false, true>(p, out, false, products, stream);
+}
+
+}  // namespace
+
+hipError_t launch_gemm(const GemmOp& op, hipStream_t stream) {
+  if (op.nx <= 0 || op.ny <= 0) return hipSuccess;
+  if (op.K <= 0) return hipErrorInvalidValue;   // callers never ask for an empty sum
+  return launch_params(op, make_params(op), 1, stream);
+}
+
+hipError_t launch_gemm_pair(const GemmOp& a, const GemmOp& b, hipStream_t stream) {
+  const bool same = a.nx == b.nx && a.ny == b.ny && a.K == b.K && a.x.ld == b.x.ld &&
+                    a.y.ld == b.y.ld && a.x.kmajor == b.x.kmajor && a.y.kmajor == b.y.kmajor &&
+                    a.ldc == b.ldc && a.c_bf16 == b.c_bf16 && a.accumulate == b.accumulate &&
+                    a.stats == nullptr && b.stats == nullptr;
+  if (!same) {
+    const hipError_t e = launch_gemm(a, stream);
+    return e != hipSuccess ? e : launch_gemm(b, stream);
+  }
+  if (a.nx <= 0 || a.ny <= 0) return hipSuccess;
+  if (a.K <= 0) return hipErrorInvalidValue;
+  GemmParams p = make_params(a);
+  p.x2 = static_cast<const __bf16*>(b.x.p);
+  p.y2 = static_cast<const __bf16*>(b.y.p);
+  p.c2 = b.c;
+  return launch_params(a, p, 2, stream);
 }
 
 }  // namespace ulysses

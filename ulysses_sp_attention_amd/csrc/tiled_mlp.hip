@@ -146,9 +146,9 @@ MlpWork carve(void* ws, int64_t S, int64_t d, int64_t I) {
 
 // C (+)= X Y^T on the matrix-core GEMM; each operand given as (pointer,
 // leading dimension, k-major?).
-hipError_t gemm(const void* x, int64_t ldx, bool xk, const void* y, int64_t ldy, bool yk,
-                int64_t nx, int64_t ny, int64_t K, void* c, int64_t ldc, bool c_bf16,
-                bool accumulate, hipStream_t stream) {
+GemmOp gemm_op(const void* x, int64_t ldx, bool xk, const void* y, int64_t ldy, bool yk,
+               int64_t nx, int64_t ny, int64_t K, void* c, int64_t ldc, bool c_bf16,
+               bool accumulate) {
   GemmOp op{};
   op.x = GemmOperand{x, ldx, xk};
   op.y = GemmOperand{y, ldy, yk};
@@ -159,16 +159,23 @@ hipError_t gemm(const void* x, int64_t ldx, bool xk, const void* y, int64_t ldy,
   op.ldc = ldc;
   op.c_bf16 = c_bf16;
   op.accumulate = accumulate;
-  return launch_gemm(op, stream);
+  return op;
+}
+
+hipError_t gemm(const void* x, int64_t ldx, bool xk, const void* y, int64_t ldy, bool yk,
+                int64_t nx, int64_t ny, int64_t K, void* c, int64_t ldc, bool c_bf16,
+                bool accumulate, hipStream_t stream) {
+  return launch_gemm(gemm_op(x, ldx, xk, y, ldy, yk, nx, ny, K, c, ldc, c_bf16, accumulate), stream);
 }
 
 // g and u of rows [r0, r0 + rows): g[s][i] = sum_k x[s][k] Wg[i][k].
 hipError_t gate_up(const TiledMlpArgs& a, const MlpWork& w, int64_t r0, int64_t rows,
                    hipStream_t stream) {
   const __bf16* xs = static_cast<const __bf16*>(a.x) + r0 * a.d;
-  hipError_t e = gemm(xs, a.d, true, a.wg, a.d, true, rows, a.I, a.d, w.g, a.I, false, false, stream);
-  if (e != hipSuccess) return e;
-  return gemm(xs, a.d, true, a.wu, a.d, true, rows, a.I, a.d, w.u, a.I, false, false, stream);
+  // both products in one launch: their tiles fill one grid
+  return launch_gemm_pair(gemm_op(xs, a.d, true, a.wg, a.d, true, rows, a.I, a.d, w.g, a.I, false, false),
+                          gemm_op(xs, a.d, true, a.wu, a.d, true, rows, a.I, a.d, w.u, a.I, false, false),
+                          stream);
 }
 
 }  // namespace
@@ -217,11 +224,10 @@ hipError_t launch_tiled_mlp(const TiledMlpArgs& a, hipStream_t stream) {
     if ((e = gemm(dys, d, false, w.a, I, false, d, I, rows, a.dwd, I, false, acc, stream)) !=
         hipSuccess)
       return e;
-    // dWg[i][j] (+)= sum_s dg[s][i] x[s][j]; dWu likewise with du
-    if ((e = gemm(w.dg, I, false, xs, d, false, I, d, rows, a.dwg, d, false, acc, stream)) !=
-            hipSuccess ||
-        (e = gemm(w.du, I, false, xs, d, false, I, d, rows, a.dwu, d, false, acc, stream)) !=
-            hipSuccess)
+    // dWg[i][j] (+)= sum_s dg[s][i] x[s][j]; dWu likewise with du (one launch)
+    if ((e = launch_gemm_pair(gemm_op(w.dg, I, false, xs, d, false, I, d, rows, a.dwg, d, false, acc),
+                              gemm_op(w.du, I, false, xs, d, false, I, d, rows, a.dwu, d, false, acc),
+                              stream)) != hipSuccess)
       return e;
     // dx[s][j] = sum_i dg[s][i] Wg[i][j] + sum_i du[s][i] Wu[i][j]
     if ((e = gemm(w.dg, I, true, a.wg, d, false, rows, d, I, w.dx, d, false, false, stream)) !=
