@@ -53,6 +53,10 @@ def gpu_bwd(q, k, v, o, lse, do, scale, causal=True, cu=None):
     return dq, dk, dv
 
 
+def _cu(lengths):
+    return [0] + np.cumsum(lengths).tolist()
+
+
 SMALL = [
     # N, bs, hq, hkv, hd, dtype, causal, cu
     (1, 1, 4, 1, 128, "bf16", True, None),
@@ -69,6 +73,15 @@ SMALL = [
     (256, 1, 2, 2, 64, "f32", True, None),
     (97, 2, 4, 2, 32, "f32", True, None),
     (150, 1, 4, 1, 128, "f32", True, [0, 50, 51, 150]),
+    # Packed documents launch their blocks in order of work (computed on the
+    # device from cu_seqlens): ragged lengths with 1-token documents and
+    # lengths around the 64-query and 128-key block sizes; block-aligned
+    # documents over two key/value heads; more documents than that order
+    # handles (the launch keeps the positional order).
+    (3000, 1, 4, 1, 128, "bf16", True, _cu([1, 63, 64, 65, 127, 128, 129, 700, 1, 1, 2, 1000, 300, 7,
+                                             8, 9, 395])),
+    (4096, 1, 8, 2, 128, "bf16", True, _cu([512, 1024, 256, 2304])),
+    (2600, 1, 4, 1, 64, "bf16", True, _cu([7] * 300 + [500])),
 ]
 
 

@@ -144,9 +144,18 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_kernel(BwdParams p) {
   const int group = wave >> 2;   // waves w and w+4 share a SIMD
 
   const int64_t N = wave_uniform(p.N);
-  const int64_t pb = p.num_blocks - 1 - (int64_t)blockIdx.x;   // heaviest first
+  // Dispatch order as in the forward: slices fastest, blocks heaviest first
+  // (by position, or by work within documents).
+  const uint64_t lin = (uint64_t)blockIdx.y * gridDim.x + blockIdx.x;
+  const int64_t t = lin / gridDim.y;
+  int64_t pb = p.num_blocks - 1 - t;
+  if (p.cu != nullptr && p.causal) {
+    const int64_t s = doc_sorted_block<false>(t, p.num_blocks, C::kBP, p.cu, p.n_docs, N);
+    if (s >= 0) pb = s;
+  }
+  pb = wave_uniform(pb);
   const int ngroups = p.g / GPACK;
-  int y = blockIdx.y;
+  int y = (int)(lin % gridDim.y);
   const int hg = y % ngroups;
   y /= ngroups;
   const int kh = y % p.hkv;
@@ -550,13 +559,22 @@ __global__ __launch_bounds__(512) void attn_bwd_dkv_kernel(BwdParams p) {
   const int r32 = lane & 31;
 
   const int64_t N = wave_uniform(p.N);
-  const int kh = blockIdx.y % p.hkv;
-  const int b = blockIdx.y / p.hkv;
-  // Workgroup x = key block * split + part: heaviest (smallest keys) first,
-  // the parts of a block next to each other.
+  // Dispatch rank u over (key block, part, slice), slices fastest: key blocks
+  // heaviest first (smallest keys, or by work within documents), the parts
+  // of a block next to each other.
+  const uint64_t lin = (uint64_t)blockIdx.y * gridDim.x + blockIdx.x;
+  const uint64_t u = lin / gridDim.y;
+  const int ys = (int)(lin % gridDim.y);
+  const int kh = ys % p.hkv;
+  const int b = ys / p.hkv;
   const int split = p.split;
-  const int part = (int)(blockIdx.x % (uint32_t)split);
-  const int64_t k0 = (int64_t)(blockIdx.x / (uint32_t)split) * C::kBK;
+  const int part = (int)(u % (uint32_t)split);
+  int64_t kb = (int64_t)(u / (uint32_t)split);
+  if (p.cu != nullptr && p.causal) {
+    const int64_t s = doc_sorted_block<true>(kb, gridDim.x / (uint32_t)split, C::kBK, p.cu, p.n_docs, N);
+    if (s >= 0) kb = s;
+  }
+  const int64_t k0 = wave_uniform(kb) * C::kBK;
   const int64_t kw = k0 + 32 * pair;                // first key of the block
   const int64_t kj = kw + r32;                      // this lane's key
 

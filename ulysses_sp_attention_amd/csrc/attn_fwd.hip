@@ -49,7 +49,8 @@
 //  * LDS rows are swizzled in 16-byte chunks (swz in device_common.h) so both
 //    the row reads of K and the transposing reads of V avoid bank conflicts;
 //    fragments are read several products ahead of the MFMA that uses them.
-//  * Blocks are launched heaviest (largest positions) first.
+//  * Blocks are launched heaviest first: by position for one document, by
+//    their work within documents for packed documents (doc_sorted_block).
 #include <math.h>
 
 #include <type_traits>
@@ -117,9 +118,19 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdParams p) {
   const int group = wave >> 2;     // waves w and w+4 share a SIMD
 
   const int64_t N = wave_uniform(p.N);
-  const int64_t pb = p.num_pos_blocks - 1 - (int64_t)blockIdx.x;   // heaviest first
+  // Dispatch rank t of this workgroup over (block, slice) pairs, slices
+  // fastest, so every slice's heavy blocks go first; blocks by position,
+  // heaviest (largest positions) first, or by work within documents.
+  const uint64_t lin = (uint64_t)blockIdx.y * gridDim.x + blockIdx.x;
+  const int64_t t = lin / gridDim.y;
+  int64_t pb = p.num_pos_blocks - 1 - t;
+  if (p.cu != nullptr && p.causal) {
+    const int64_t s = doc_sorted_block<false>(t, p.num_pos_blocks, C::kBP, p.cu, p.n_docs, N);
+    if (s >= 0) pb = s;
+  }
+  pb = wave_uniform(pb);
   const int ngroups = p.g / GPACK;
-  int y = blockIdx.y;
+  int y = (int)(lin % gridDim.y);
   const int hg = y % ngroups;
   y /= ngroups;
   const int kh = y % p.hkv;

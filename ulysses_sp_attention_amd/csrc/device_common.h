@@ -255,6 +255,101 @@ __device__ __forceinline__ int64_t doc_end_of(const int32_t* cu, int n_docs, int
   return e;
 }
 
+// Dispatch order of the position blocks of a packed-document share, heaviest
+// first.  Under the causal mask within documents, the work of a block of B
+// query positions grows with its index inside its document, and that of a
+// block of B keys with its distance to the document's end, so launching by
+// position (right for one document) interleaves heavy and light blocks and
+// leaves a long tail.  A block of query positions [kb B, kb B + B) belongs
+// to the document holding its first position and its sort key is its index
+// from the block holding the document's start (kKeyBlocks false); a block of
+// keys belongs to the document holding its last key (whose end bounds the
+// queries it sees) and its key is its distance to that document's last
+// block (kKeyBlocks true).  Rank t of the order
+// (largest key first, documents in order within a key) is found by a binary
+// search over the key j of C(j), the number of blocks whose key is at least
+// j, then a ballot over the documents with a block of that key.  The whole
+// wave computes it, 64 documents per pass; the result is wave-uniform.  It
+// returns -1, and the caller keeps its default order, without cu, with more
+// than kOrderDocs documents, or when cu's contents (clamped to [0, N]) do not
+// cover rank t.
+constexpr int kOrderDocs = 256;
+
+template <bool kKeyBlocks>
+__device__ __forceinline__ int64_t doc_sorted_block(int64_t t, int64_t nblocks, int B,
+                                                      const int32_t* cu, int n_docs,
+                                                      int64_t N) {
+  constexpr int kPer = kOrderDocs / 64;
+  if (cu == nullptr || n_docs < 1 || n_docs > kOrderDocs) return -1;
+  const int lane = threadIdx.x & 63;
+  // Owned blocks [f, l] and start block a of this lane's documents.
+  int f[kPer], l[kPer], a[kPer];
+  int jmax = -1;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int d = lane + 64 * i;
+    f[i] = 1;
+    l[i] = 0;
+    a[i] = 0;
+    if (d < n_docs) {
+      int64_t s = cu[d], e = cu[d + 1];
+      s = s < 0 ? 0 : (s > N ? N : s);
+      e = e < s ? s : (e > N ? N : e);
+      if (kKeyBlocks) {   // blocks whose last key lies in [s, e)
+        f[i] = (int)(s / B);
+        l[i] = e <= s ? f[i] - 1 : (e >= N ? (int)(nblocks - 1) : (int)(e / B) - 1);
+      } else {            // blocks whose first position lies in [s, e)
+        f[i] = (int)((s + B - 1) / B);
+        l[i] = (int)((e + B - 1) / B) - 1;
+        a[i] = (int)(s / B);
+      }
+      if (l[i] > nblocks - 1) l[i] = (int)(nblocks - 1);
+      if (l[i] >= f[i]) {
+        const int top = kKeyBlocks ? l[i] - f[i] : l[i] - a[i];
+        jmax = top > jmax ? top : jmax;
+      }
+    }
+  }
+  for (int off = 32; off > 0; off >>= 1) {
+    const int o = __shfl_xor(jmax, off, 64);
+    jmax = o > jmax ? o : jmax;
+  }
+  // C(j), summed over the wave.
+  auto count_ge = [&](int j) __attribute__((always_inline)) {
+    int c = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int lo = kKeyBlocks ? f[i] : (f[i] > a[i] + j ? f[i] : a[i] + j);
+      const int hi = kKeyBlocks ? l[i] - j : l[i];
+      c += hi >= lo ? hi - lo + 1 : 0;
+    }
+    for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off, 64);
+    return c;
+  };
+  if (jmax < 0 || count_ge(0) <= t) return -1;
+  int lo = 0, hi = jmax;   // the largest j with C(j) > t lies in [lo, hi]
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (count_ge(mid) > t) lo = mid; else hi = mid - 1;
+  }
+  int r = (int)t - count_ge(lo + 1);   // rank among the blocks of key lo
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int kb = kKeyBlocks ? l[i] - lo : a[i] + lo;
+    const bool member = l[i] >= f[i] && kb >= f[i] && kb <= l[i];
+    const uint64_t m = __ballot(member);
+    const int cnt = __popcll(m);
+    if (r < cnt) {
+      const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+      const uint64_t sel = __ballot(member && below == r);
+      return wave_uniform(__shfl(kb, __ffsll((unsigned long long)sel) - 1, 64));
+    }
+    r -= cnt;
+  }
+  return -1;
+}
+
 template <typename Tuple, size_t... I>
 inline void fill_argv(Tuple& t, void** argv, std::index_sequence<I...>) {
   ((argv[I] = static_cast<void*>(&std::get<I>(t))), ...);
