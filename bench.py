@@ -80,8 +80,8 @@ def parse_args():
     ap.add_argument("--no-logits-loss", action="store_true",
                     help="skip the language-model loss and tiled MLP records (outside the "
                          "attention step)")
-    ap.add_argument("--cpu-rows", type=int, default=768,
-                    help="query rows of the oracle's timed sample")
+    ap.add_argument("--cpu-rows", type=int, default=2560,
+                    help="query rows of the oracle's timed sample (about 10-15 s on 16 cores)")
     ap.add_argument("--pack-sets", type=int, default=4,
                     help="distinct buffer sets the rotated exchange measurement cycles through")
     ap.add_argument("--pack-reps", type=int, default=24,
