@@ -528,7 +528,7 @@ hipError_t launch_gemm_pair(const GemmOp& a, const GemmOp& b, hipStream_t stream
   const bool same = a.nx == b.nx && a.ny == b.ny && a.K == b.K && a.x.ld == b.x.ld &&
                     a.y.ld == b.y.ld && a.x.kmajor == b.x.kmajor && a.y.kmajor == b.y.kmajor &&
                     a.ldc == b.ldc && a.c_bf16 == b.c_bf16 && a.accumulate == b.accumulate &&
-                    a.stats == nullptr && b.stats == nullptr;
+                    a.stats == nullptr && b.stats == nullptr && a.c != b.c;
   if (!same) {
     const hipError_t e = launch_gemm(a, stream);
     return e != hipSuccess ? e : launch_gemm(b, stream);

@@ -183,8 +183,10 @@ struct GemmOp {
 int gemm_tiles_y(int64_t ny);
 hipError_t launch_gemm(const GemmOp& op, hipStream_t stream);
 // Two products in one launch when they share every size, layout and output
-// mode (and neither has stats), so their tiles fill one grid; two launches
-// otherwise.
+// mode (and neither has stats), so their tiles fill one grid; two launches,
+// a then b, otherwise or when both write the same output.  In one launch the
+// products run concurrently: neither output may overlap the other product's
+// operands.
 hipError_t launch_gemm_pair(const GemmOp& a, const GemmOp& b, hipStream_t stream);
 
 // Sequence-tiled SwiGLU MLP over T rows, shard_rows at a time.  x [T, d],
