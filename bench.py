@@ -121,7 +121,7 @@ def main():
     args = parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share of the path; --gpus {args.gpus} is not supported "
-              "(this build runs on a single GPU, with no collectives between GPUs)", file=sys.stderr)
+              "(libulysses runs on a single GPU, with no collectives between GPUs)", file=sys.stderr)
         return 2
     if args.oracle_plan:
         print(json.dumps(oracle_plan()))

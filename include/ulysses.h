@@ -83,7 +83,7 @@ enum {
   ULYSSES_ERR_DIVISIBILITY = 3,   /* head counts do not divide as the method requires */
   ULYSSES_ERR_DTYPE = 4,          /* unknown element type */
   ULYSSES_ERR_ALIGNMENT = 5,      /* pointer or row not 16-byte aligned */
-  ULYSSES_ERR_UNSUPPORTED = 6,    /* valid request this build does not implement */
+  ULYSSES_ERR_UNSUPPORTED = 6,    /* valid request the library does not implement */
   ULYSSES_ERR_WORKSPACE = 7,      /* workspace NULL or smaller than required */
   ULYSSES_ERR_HIP = 8             /* kernel launch failed */
 };

@@ -22,7 +22,7 @@
  *    sequence Transformer models" (DeepSpeed blog, Chinese), the design
  *    section (per-head attention after the first all-to-all).
  *
- * Readings where the pages are silent (also listed in the design doc):
+ * Readings where the pages are silent:
  *  - attention is standard scaled dot-product softmax attention per head
  *    (the formula on the DeepSpeed blog is an image that did not survive);
  *  - query head h uses key/value head floor(h / (hq / hkv));

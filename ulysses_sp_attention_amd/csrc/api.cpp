@@ -179,7 +179,7 @@ const char* ulysses_status_string(ulysses_status_t status) {
     case ULYSSES_ERR_DIVISIBILITY: return "head counts not divisible as required";
     case ULYSSES_ERR_DTYPE: return "unknown element type";
     case ULYSSES_ERR_ALIGNMENT: return "pointer or row not 16-byte aligned";
-    case ULYSSES_ERR_UNSUPPORTED: return "request not supported by this build";
+    case ULYSSES_ERR_UNSUPPORTED: return "request not supported by the library";
     case ULYSSES_ERR_WORKSPACE: return "workspace missing or too small";
     case ULYSSES_ERR_HIP: return "HIP kernel launch failed";
   }
