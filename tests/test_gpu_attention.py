@@ -82,6 +82,9 @@ SMALL = [
                                              8, 9, 395])),
     (4096, 1, 8, 2, 128, "bf16", True, _cu([512, 1024, 256, 2304])),
     (2600, 1, 4, 1, 64, "bf16", True, _cu([7] * 300 + [500])),
+    # exactly as many documents as the ordered launch handles, the longest last
+    (sum(1 + (7 * i) % 29 for i in range(255)) + 2000, 1, 4, 1, 128, "bf16", True,
+     _cu([1 + (7 * i) % 29 for i in range(255)] + [2000])),
 ]
 
 
